@@ -1,0 +1,309 @@
+/*
+ * The oracle: a plain, slow, obviously correct CPU implementation of one Mixture-of-Experts
+ * expert-FFN layer. TEST INFRASTRUCTURE ONLY: it is compiled and called by the tests, by the
+ * smoke check and by the CPU-baseline leg of the benchmark, never by the library. It shares no
+ * source with the HIP library.
+ *
+ * Arithmetic is fp64 throughout. Stored weights are decoded element by element with this
+ * file's own decoders, from the same bytes the GPU reads, in the logical row-major layout:
+ *   W_gate, W_up : [H][I]   W_down : [I][H]   (one matrix per expert, experts back to back)
+ *   f32   float[K][N]
+ *   bf16  uint16[K][N]                                   (bit patterns)
+ *   fp8   uint8[K][N] OCP E4M3FN + float[K/128][N/128]   (w = e4m3(code) * s)
+ *   mxfp4 uint8[K][N/2] e2m1, even n in the low nibble + uint8[K/32][N] e8m0
+ *                                                        (w = e2m1(code) * 2^(E-127))
+ *
+ * What it computes, step by step (sources: "AI infra book, ch. 6 Supernodes" (bojieli.github.io
+ * ai-infra-book ch. 6) = [ch6]; "DeepSeek-V4-Pro on NVIDIA H200" report = [V4]):
+ *   1. router scores l[t][e] = sum_h x[t][h] Wr[h][e] (+ b[e])       [ch6 §6.2.6; V4 step D4]
+ *   2. the k largest scores per token, ties to the lower expert index, listed in ascending
+ *      expert index                                                  [V4 step D4 "top-6"]
+ *   3. weights: softmax over all E scores, renormalised over the k selected
+ *      (a1, a6 of the token-A example)                               [ch6 §6.2.6]
+ *   4. permutation: rows regrouped by expert, stable in token order  [ch6 §6.2.6, receiver side]
+ *   5. each expert: Y = [SiLU(X Wg) (.) (X Wu)] Wd                    [ch6 §6.2.2, SwiGLU display]
+ *   6. the shared expert: the same FFN on every token, weight 1      [V4 §0.1.2, §3.2]
+ *   7. combine: y[t] = sum_j w[t][j] y_perm[pair_slot[t k + j]] + y_sh[t]
+ *                                                                    [ch6 §6.2.6, §6.4.1]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3 };
+
+/* ---------------------------------------------------------------------------------------- */
+/* decoders                                                                                  */
+/* ---------------------------------------------------------------------------------------- */
+
+double oracle_decode_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities; S.1111.111 = NaN. */
+double oracle_decode_e4m3fn(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9); /* subnormal: m/8 * 2^-6 */
+  else
+    v = ldexp(8.0 + m, e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+/* OCP e2m1: 1 sign, 2 exponent (bias 1), 1 mantissa bit. */
+double oracle_decode_e2m1(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = (e == 0) ? 0.5 * m : ldexp(2.0 + m, e - 2); /* (1 + m/2) * 2^(e-1) */
+  return s ? -v : v;
+}
+
+/* OCP e8m0: 2^(E-127); E = 255 is NaN. */
+double oracle_decode_e8m0(uint8_t E) {
+  if (E == 255) return NAN;
+  return ldexp(1.0, (int)E - 127);
+}
+
+static double act_at(const void* p, int act, size_t i) {
+  return act == OR_F32 ? (double)((const float*)p)[i] : oracle_decode_bf16(((const uint16_t*)p)[i]);
+}
+
+/* Element W[k][n] of a stored K x N matrix. */
+static double w_at(const void* w, const void* scale, int fmt, int K, int N, int k, int n) {
+  size_t i = (size_t)k * N + n;
+  switch (fmt) {
+    case OR_F32: return (double)((const float*)w)[i];
+    case OR_BF16: return oracle_decode_bf16(((const uint16_t*)w)[i]);
+    case OR_FP8: {
+      double s = (double)((const float*)scale)[(size_t)(k / 128) * (N / 128) + n / 128];
+      return oracle_decode_e4m3fn(((const uint8_t*)w)[i]) * s;
+    }
+    case OR_MXFP4: {
+      uint8_t byte = ((const uint8_t*)w)[(size_t)k * (N / 2) + n / 2];
+      uint8_t code = (n & 1) ? (byte >> 4) : (byte & 15);
+      uint8_t E = ((const uint8_t*)scale)[(size_t)(k / 32) * N + n];
+      return oracle_decode_e2m1(code) * oracle_decode_e8m0(E);
+    }
+  }
+  return NAN;
+}
+
+/* Bytes of one stored K x N matrix and of its scales. */
+static size_t w_bytes(int fmt, int K, int N) {
+  switch (fmt) {
+    case OR_F32: return (size_t)K * N * 4;
+    case OR_BF16: return (size_t)K * N * 2;
+    case OR_FP8: return (size_t)K * N;
+    case OR_MXFP4: return (size_t)K * N / 2;
+  }
+  return 0;
+}
+static size_t s_bytes(int fmt, int K, int N) {
+  switch (fmt) {
+    case OR_FP8: return (size_t)(K / 128) * (N / 128) * 4;
+    case OR_MXFP4: return (size_t)(K / 32) * N;
+  }
+  return 0;
+}
+
+/* Decode a whole stored matrix to fp64 (for tests of the decoders and the generator). */
+int oracle_decode_matrix(int fmt, int K, int N, const void* w, const void* scale, double* out) {
+  for (int k = 0; k < K; ++k)
+    for (int n = 0; n < N; ++n) out[(size_t)k * N + n] = w_at(w, scale, fmt, K, N, k, n);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* the row-vector times matrix product every step is made of: out[n] = sum_k u[k] W[k][n]    */
+/* ---------------------------------------------------------------------------------------- */
+
+int oracle_row_matmul(int K, int N, int fmt, const void* w, const void* scale, const double* u,
+                      double* out) {
+  for (int n = 0; n < N; ++n) out[n] = 0.0;
+  for (int k = 0; k < K; ++k) {
+    double uk = u[k];
+    for (int n = 0; n < N; ++n) out[n] += uk * w_at(w, scale, fmt, K, N, k, n);
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* steps 1-3: router                                                                         */
+/* ---------------------------------------------------------------------------------------- */
+
+int oracle_route(int T, int H, int E, int k, int act, const void* x, const void* Wr,
+                 const float* bias, int32_t* topk_idx, double* topk_w, double* logits_out) {
+  if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return 1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int t = 0; t < T; ++t) {
+    double* l = (double*)malloc(sizeof(double) * E);
+    char* chosen = (char*)calloc(E, 1);
+    double* u = (double*)malloc(sizeof(double) * H);
+    if (!l || !chosen || !u) {
+      bad = 1;
+    } else {
+      for (int h = 0; h < H; ++h) u[h] = act_at(x, act, (size_t)t * H + h);
+      oracle_row_matmul(H, E, act == OR_F32 ? OR_F32 : OR_BF16, Wr, NULL, u, l);
+      if (bias)
+        for (int e = 0; e < E; ++e) l[e] += (double)bias[e];
+      if (logits_out) memcpy(logits_out + (size_t)t * E, l, sizeof(double) * E);
+      /* k rounds of "largest not yet chosen"; scanning upward with '>' keeps the lower index
+         on an exact tie */
+      for (int r = 0; r < k; ++r) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+          if (!chosen[e] && (best < 0 || l[e] > l[best])) best = e;
+        chosen[best] = 1;
+      }
+      /* softmax over all E, then renormalise over the chosen k */
+      double m = l[0];
+      for (int e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+      double z_all = 0.0, z_sel = 0.0;
+      for (int e = 0; e < E; ++e) z_all += exp(l[e] - m);
+      for (int e = 0; e < E; ++e)
+        if (chosen[e]) z_sel += exp(l[e] - m) / z_all;
+      int j = 0;
+      for (int e = 0; e < E; ++e)
+        if (chosen[e]) {
+          topk_idx[(size_t)t * k + j] = e;
+          topk_w[(size_t)t * k + j] = (exp(l[e] - m) / z_all) / z_sel;
+          ++j;
+        }
+    }
+    free(l);
+    free(chosen);
+    free(u);
+  }
+  return bad ? 2 : 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* step 4: permutation (a stable counting sort of the pairs q = t*k + j by expert)           */
+/* ---------------------------------------------------------------------------------------- */
+
+int oracle_permute(int T, int k, int E, const int32_t* topk_idx, int32_t* expert_offsets,
+                   int32_t* slot_token, int32_t* pair_slot) {
+  int P = T * k;
+  int32_t* fill = (int32_t*)calloc((size_t)E + 1, sizeof(int32_t));
+  if (!fill) return 2;
+  for (int e = 0; e <= E; ++e) expert_offsets[e] = 0;
+  for (int q = 0; q < P; ++q) {
+    int e = topk_idx[q];
+    if (e < 0 || e >= E) {
+      free(fill);
+      return 1;
+    }
+    expert_offsets[e + 1] += 1;
+  }
+  for (int e = 0; e < E; ++e) expert_offsets[e + 1] += expert_offsets[e];
+  for (int e = 0; e < E; ++e) fill[e] = expert_offsets[e];
+  for (int q = 0; q < P; ++q) {
+    int slot = fill[topk_idx[q]]++;
+    slot_token[slot] = q / k;
+    pair_slot[q] = slot;
+  }
+  free(fill);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* step 5/6: one expert's SwiGLU FFN on M rows                                               */
+/* ---------------------------------------------------------------------------------------- */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+int oracle_expert_ffn(int H, int I, int M, int fmt, const void* wg, const void* sg,
+                      const void* wu, const void* su, const void* wd, const void* sd,
+                      const double* u, double* y) {
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int m = 0; m < M; ++m) {
+    double* g = (double*)malloc(sizeof(double) * I);
+    double* v = (double*)malloc(sizeof(double) * I);
+    if (!g || !v) {
+      bad = 1;
+    } else {
+      oracle_row_matmul(H, I, fmt, wg, sg, u + (size_t)m * H, g);
+      oracle_row_matmul(H, I, fmt, wu, su, u + (size_t)m * H, v);
+      for (int i = 0; i < I; ++i) g[i] = silu(g[i]) * v[i];
+      oracle_row_matmul(I, H, fmt, wd, sd, g, y + (size_t)m * H);
+    }
+    free(g);
+    free(v);
+  }
+  return bad ? 2 : 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* step 7: combine one token                                                                  */
+/* ---------------------------------------------------------------------------------------- */
+
+int oracle_combine_token(int H, int k, const double* w, const double* yk, const double* ysh,
+                         double* y) {
+  for (int n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int j = 0; j < k; ++j) acc += w[j] * yk[(size_t)j * H + n];
+    y[n] = acc + (ysh ? ysh[n] : 0.0);
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* the whole layer, steps 1-7                                                                */
+/* ---------------------------------------------------------------------------------------- */
+
+int oracle_layer(int T, int H, int E, int k, int I, int act, const void* x, const void* Wr,
+                 const float* bias, int fmt_r, const void* rg, const void* rsg, const void* ru,
+                 const void* rsu, const void* rd, const void* rsd, int has_shared, int fmt_s,
+                 const void* sg, const void* ssg, const void* su, const void* ssu,
+                 const void* sd, const void* ssd, int32_t* topk_idx, double* topk_w,
+                 int32_t* expert_offsets, int32_t* slot_token, int32_t* pair_slot, double* y) {
+  int P = T * k, rc;
+  rc = oracle_route(T, H, E, k, act, x, Wr, bias, topk_idx, topk_w, NULL);
+  if (rc) return rc;
+  rc = oracle_permute(T, k, E, topk_idx, expert_offsets, slot_token, pair_slot);
+  if (rc) return rc;
+  size_t gw = w_bytes(fmt_r, H, I), gs = s_bytes(fmt_r, H, I);
+  size_t dw = w_bytes(fmt_r, I, H), ds = s_bytes(fmt_r, I, H);
+  double* xin = (double*)malloc(sizeof(double) * (size_t)(P > T ? P : T) * H);
+  double* yperm = (double*)malloc(sizeof(double) * (size_t)P * H);
+  double* ysh = has_shared ? (double*)malloc(sizeof(double) * (size_t)T * H) : NULL;
+  if (!xin || !yperm || (has_shared && !ysh)) return 2;
+  /* rows of each expert's group, gathered in slot order */
+  for (int r = 0; r < P; ++r)
+    for (int h = 0; h < H; ++h) xin[(size_t)r * H + h] = act_at(x, act, (size_t)slot_token[r] * H + h);
+  for (int e = 0; e < E && !rc; ++e) {
+    int r0 = expert_offsets[e], M = expert_offsets[e + 1] - r0;
+    if (M == 0) continue;
+    rc = oracle_expert_ffn(H, I, M, fmt_r, (const char*)rg + e * gw, rsg ? (const char*)rsg + e * gs : NULL,
+                           (const char*)ru + e * gw, rsu ? (const char*)rsu + e * gs : NULL,
+                           (const char*)rd + e * dw, rsd ? (const char*)rsd + e * ds : NULL,
+                           xin + (size_t)r0 * H, yperm + (size_t)r0 * H);
+  }
+  if (has_shared && !rc) {
+    for (int t = 0; t < T; ++t)
+      for (int h = 0; h < H; ++h) xin[(size_t)t * H + h] = act_at(x, act, (size_t)t * H + h);
+    rc = oracle_expert_ffn(H, I, T, fmt_s, sg, ssg, su, ssu, sd, ssd, xin, ysh);
+  }
+  if (!rc) {
+    double* yk = (double*)malloc(sizeof(double) * (size_t)k * H);
+    if (!yk) rc = 2;
+    for (int t = 0; t < T && !rc; ++t) {
+      for (int j = 0; j < k; ++j)
+        memcpy(yk + (size_t)j * H, yperm + (size_t)pair_slot[(size_t)t * k + j] * H, sizeof(double) * H);
+      oracle_combine_token(H, k, topk_w + (size_t)t * k, yk, ysh ? ysh + (size_t)t * H : NULL,
+                           y + (size_t)t * H);
+    }
+    free(yk);
+  }
+  free(xin);
+  free(yperm);
+  free(ysh);
+  return rc;
+}

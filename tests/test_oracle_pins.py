@@ -1,0 +1,355 @@
+"""Pins of the CPU oracle to facts outside itself: format specifications, library routines,
+closed forms, invariants, special cases and brute force on tiny inputs.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a wrong sign or
+index, a transposed operand, a wrong tie rule) fails it. Pages are cited by title and section.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from inputgen import layers as L
+from inputgen import philox as px
+from oracle import oracle as O
+
+
+# ------------------------------------------------------------------ decoders (exhaustive)
+
+def test_e4m3fn_all_codes_match_torch():
+    """All 256 OCP E4M3FN codes against torch's float8_e4m3fn -> float32 conversion."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = np.array([O.decode_scalar("e4m3fn", c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.sum(np.isnan(got)) == 2  # S.1111.111 only
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def test_e2m1_all_codes_match_ocp_table():
+    """OCP Microscaling v1.0 FP4 (E2M1) value table."""
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    ref = table + [-v for v in table]
+    got = [O.decode_scalar("e2m1", c) for c in range(16)]
+    assert got == ref
+
+
+def test_e8m0_all_codes():
+    for E in range(255):
+        assert O.decode_scalar("e8m0", E) == math.ldexp(1.0, E - 127)
+    assert math.isnan(O.decode_scalar("e8m0", 255))
+
+
+def test_bf16_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 2 ** 16, 4096).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]  # finite values only
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).float().numpy()
+    got = np.array([O.decode_scalar("bf16", int(b)) for b in bits])
+    assert np.array_equal(got, ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4"])
+def test_decode_matrix_layout(fmt):
+    """The matrix decoder against an independent numpy/torch decode of the stored layout."""
+    K, N = 256, 256
+    w = px.normal_f32(7, 99, 0, 0, K * N, 0.05).reshape(K, N)
+    st = L.store_matrix(w, fmt)
+    got = O.decode_matrix(fmt, K, N, st["w"], st["scale"])
+    if fmt == "f32":
+        ref = w.astype(np.float64)
+    elif fmt == "bf16":
+        ref = px.bf16_bits_to_f32(st["w"]).astype(np.float64)
+    elif fmt == "fp8":
+        v = torch.from_numpy(st["w"]).view(torch.float8_e4m3fn).double().numpy()
+        ref = v * np.kron(st["scale"].astype(np.float64), np.ones((128, 128)))
+    else:
+        lo, hi = st["w"] & 15, st["w"] >> 4
+        codes = np.empty((K, N), np.uint8)
+        codes[:, 0::2], codes[:, 1::2] = lo, hi
+        table = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+        scale = np.ldexp(1.0, st["scale"].astype(np.int64) - 127)
+        ref = table[codes] * np.repeat(scale, 32, axis=0)
+    assert np.array_equal(got, ref)
+    # the stored value is the nearest representable one: relative error bound of the format
+    rel = {"f32": 0, "bf16": 2 ** -8, "fp8": 2 ** -3, "mxfp4": 0.5}[fmt]
+    if fmt != "mxfp4":
+        assert np.all(np.abs(got - w) <= rel * np.abs(w) + 2 ** -9 * 1e-1)
+
+
+# ------------------------------------------------------------------ the product everything uses
+
+def test_row_matmul_printed_example():
+    """x = [2, 3], W = [[1, 4], [2, 5]] gives xW = [8, 23]; splitting W by rows gives the
+    partial sums [2, 8] and [6, 15] (Chapter 6 'Supernodes', section 6.2.2, Figs. 6-7/6-8)."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_closed_forms.json")))
+    ex = g["tp_split_example"]
+    W = np.array(ex["W"], np.float32)
+    assert list(O.row_matmul(np.array(ex["x"], float), W)) == ex["xW"]
+    p0 = O.row_matmul(np.array([ex["x"][0]], float), W[:1])
+    p1 = O.row_matmul(np.array([ex["x"][1]], float), W[1:])
+    assert [list(p0), list(p1)] == ex["row_split_partials"]
+    # columns: each card computes one output element
+    assert O.row_matmul(np.array(ex["x"], float), W[:, :1].copy())[0] == ex["xW"][0]
+
+
+def test_row_matmul_vs_numpy_not_transposed():
+    rng = np.random.default_rng(1)
+    W = rng.standard_normal((7, 5)).astype(np.float32)
+    u = rng.standard_normal(7)
+    assert np.allclose(O.row_matmul(u, W), u @ W.astype(np.float64), rtol=1e-14, atol=1e-14)
+
+
+# ------------------------------------------------------------------ router
+
+def _tiny(T=24, H=128, E=16, k=4, act="bf16", seed=11, **kw):
+    return L.LayerSpec("tiny", T=T, H=H, E=E, k=k, I=128, act=act, w_routed="bf16", seed=seed, **kw)
+
+
+def test_route_brute_force_selection():
+    """Selection against sorting every score (a different algorithm from the oracle's k rounds
+    of arg-max); logits against a numpy float64 matmul of the decoded inputs."""
+    for act in ("f32", "bf16"):
+        s = _tiny(act=act)
+        r = L.router_inputs(s)
+        idx, w, logits = O.route(r["x"], r["Wr"], r["bias"], s.k, s.act)
+        ref_logits = L.act_to_f64(r["x"], act) @ L.act_to_f64(r["Wr"], act)
+        assert np.allclose(logits, ref_logits, rtol=1e-12, atol=1e-12)
+        for t in range(s.T):
+            order = sorted(range(s.E), key=lambda e: (-logits[t, e], e))
+            assert list(idx[t]) == sorted(order[:s.k])
+
+
+def test_route_weights_identity_and_sum():
+    """Renormalised softmax over the selection equals the softmax of the selected scores alone,
+    and the weights of a token sum to 1 (the combine a1 y1 + a6 y6 of Chapter 6, section 6.2.6
+    averages expert outputs)."""
+    s = _tiny(E=32, k=6, router="zipf", zipf_alpha=1.0, calib_tokens=256)
+    r = L.router_inputs(s)
+    idx, w, logits = O.route(r["x"], r["Wr"], r["bias"], s.k, s.act)
+    # bias enters the score
+    ref = L.act_to_f64(r["x"], s.act) @ L.act_to_f64(r["Wr"], s.act) + r["bias"].astype(np.float64)
+    assert np.allclose(logits, ref, rtol=1e-12, atol=1e-12)
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    alt = np.exp(sel - sel.max(1, keepdims=True))
+    alt /= alt.sum(1, keepdims=True)
+    assert np.allclose(w, alt, rtol=1e-12, atol=1e-14)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-12)
+    # the larger score gets the larger weight
+    for t in range(s.T):
+        o = np.argsort(sel[t])
+        assert np.all(np.diff(w[t][o]) >= -1e-15)
+
+
+def test_route_all_ties_go_to_lower_index():
+    """Wr = 0, no bias: every score ties, so the selection is experts 0..k-1 with weight 1/k."""
+    T, H, E, k = 5, 64, 12, 3
+    x = L.store_act(px.normal_f32(1, 1, 0, 0, T * H).reshape(T, H), "bf16")
+    Wr = np.zeros((H, E), np.uint16)
+    idx, w, _ = O.route(x, Wr, None, k, "bf16")
+    assert (idx == np.arange(k)).all()
+    assert np.allclose(w, 1.0 / k, atol=1e-15)
+
+
+def test_route_partial_tie_at_the_boundary():
+    """Scores [5, 1, 3, 3, 3] with k = 3: 0 and the two lowest-index of the tied 3s."""
+    x = np.ones((1, 1), np.float32)
+    Wr = np.array([[5, 1, 3, 3, 3]], np.float32)
+    idx, w, _ = O.route(x, Wr, None, 3, "f32")
+    assert list(idx[0]) == [0, 2, 3]
+    e = np.exp([0.0, -2.0, -2.0])
+    assert np.allclose(w[0], e / e.sum(), rtol=1e-14)
+
+
+def test_route_k_equals_E_and_k_one():
+    x = np.ones((2, 1), np.float32)
+    Wr = np.array([[0.5, -1.0, 2.0]], np.float32)
+    idx, w, _ = O.route(x, Wr, None, 3, "f32")
+    assert (idx == [0, 1, 2]).all()
+    p = np.exp(np.array([0.5, -1.0, 2.0]) - 2.0)
+    assert np.allclose(w[0], p / p.sum(), rtol=1e-14)
+    idx, w, _ = O.route(x, Wr, None, 1, "f32")
+    assert (idx[:, 0] == 2).all() and np.all(w == 1.0)
+
+
+def test_expected_active_experts_eq_6_8():
+    """Uniform router: the mean number of experts a batch selects matches
+    E (1 - (1 - k/E)^m) (Chapter 6 'Supernodes', eq. (6-8)) within 3 standard errors."""
+    from expert_ffn_layer_amd.perfmodel import expected_active
+    E, k, m = 128, 8, 8
+    counts = []
+    for seed in range(40):
+        s = L.LayerSpec("u", T=m, H=128, E=E, k=k, I=128, seed=100 + seed)
+        r = L.router_inputs(s)
+        idx, _, _ = O.route(r["x"], r["Wr"], None, k, "bf16")
+        counts.append(len(np.unique(idx)))
+    mu = expected_active(E, k, m)
+    assert abs(mu - 52) < 0.5  # the page's "about 52"
+    se = np.std(counts, ddof=1) / np.sqrt(len(counts))
+    assert abs(np.mean(counts) - mu) < 3 * se + 0.3
+
+
+# ------------------------------------------------------------------ permutation
+
+def _perm_check(idx, E):
+    off, st, ps = O.permute(idx, E)
+    T, k = idx.shape
+    P = T * k
+    flat = idx.reshape(-1)
+    q_sorted = sorted(range(P), key=lambda q: (flat[q], q))
+    assert off[0] == 0 and off[-1] == P
+    assert list(np.diff(off)) == [int((flat == e).sum()) for e in range(E)]
+    assert [q // k for q in q_sorted] == list(st)
+    # bijection: pair -> slot -> token
+    assert sorted(ps) == list(range(P))
+    for q in range(P):
+        assert st[ps[q]] == q // k
+        e = flat[q]
+        assert off[e] <= ps[q] < off[e + 1]
+    return off, st, ps
+
+
+def test_permute_brute_force_random():
+    rng = np.random.default_rng(3)
+    for T, E, k in ((1, 4, 1), (7, 5, 3), (33, 16, 4), (64, 128, 8)):
+        idx = np.sort(np.stack([rng.choice(E, k, replace=False) for _ in range(T)]), axis=1)
+        _perm_check(idx.astype(np.int32), E)
+
+
+def test_permute_512_dispatches_uniform_and_concentrated():
+    """64 tokens x 8 experts = 512 dispatches; spread evenly over 128 experts each gets 4 rows,
+    all on the same 8 experts each gets 64 (Chapter 6, section 6.3.2, Fig. 6-19)."""
+    T, k, E = 64, 8, 128
+    uni = np.array([[(t * 8 + j) % E for j in range(k)] for t in range(T)])
+    uni = np.sort(uni, axis=1).astype(np.int32)
+    assert all(len(set(r)) == k for r in uni)
+    off, _, _ = _perm_check(uni, E)
+    assert off[-1] == 512 and set(np.diff(off)) == {4}
+    conc = np.tile(np.arange(8, dtype=np.int32), (T, 1))
+    off, _, _ = _perm_check(conc, E)
+    assert list(np.diff(off)[:8]) == [64] * 8 and off[-1] == 512
+
+
+def test_permute_rejects_bad_index():
+    with pytest.raises(RuntimeError):
+        O.permute(np.array([[0, 5]], np.int32), 4)
+
+
+# ------------------------------------------------------------------ expert FFN
+
+def _dense_ref(u, wts, fmt, H, I):
+    g = O.decode_matrix(fmt, H, I, wts["gate"], wts["gate_scale"])
+    v = O.decode_matrix(fmt, H, I, wts["up"], wts["up_scale"])
+    d = O.decode_matrix(fmt, I, H, wts["down"], wts["down_scale"])
+    a = torch.from_numpy(u @ g)
+    return (torch.nn.functional.silu(a).numpy() * (u @ v)) @ d
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4"])
+def test_expert_ffn_is_swiglu(fmt):
+    """Y = [SiLU(X Wg) (.) (X Wu)] Wd (Chapter 6 'Supernodes', section 6.2.2) against numpy
+    float64 matmuls and torch's SiLU on the decoded weights."""
+    H, I, M = 256, 128, 5
+    s = L.LayerSpec("f", T=M, H=H, E=1, k=1, I=I, w_routed=fmt)
+    wts = L.expert_weights(s, "routed", 0)
+    u = px.normal_f32(3, 5, 0, 0, M * H).reshape(M, H).astype(np.float64)
+    y = O.expert_ffn(u, wts, fmt)
+    ref = _dense_ref(u, wts, fmt, H, I)
+    assert np.allclose(y, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_expert_ffn_split_identity_eq_6_3():
+    """Y = Z0 Wd0 + Z1 Wd1 when the intermediate width is split in halves (eq. (6-3))."""
+    H, I, M = 128, 256, 3
+    s = L.LayerSpec("f", T=M, H=H, E=1, k=1, I=I, w_routed="f32", act="f32")
+    w = L.expert_weights(s, "routed", 0)
+    u = px.normal_f32(4, 5, 0, 0, M * H).reshape(M, H).astype(np.float64)
+    y = O.expert_ffn(u, w, "f32")
+    halves = []
+    for sl in (slice(0, I // 2), slice(I // 2, I)):
+        wh = {"gate": w["gate"][:, sl].copy(), "up": w["up"][:, sl].copy(),
+              "down": w["down"][sl, :].copy(), "gate_scale": None, "up_scale": None,
+              "down_scale": None}
+        halves.append(O.expert_ffn(u, wh, "f32"))
+    assert np.allclose(y, halves[0] + halves[1], rtol=1e-12, atol=1e-13)
+
+
+def test_silu_sign_and_zero():
+    """SiLU(0) = 0 and SiLU(z) -> z for large z, SiLU(z) -> 0 for very negative z: an FFN with
+    identity-like weights exposes the activation directly."""
+    H = I = 128
+    eye = np.eye(H, dtype=np.float32)
+    w = {"gate": eye * 30, "up": eye, "down": eye, "gate_scale": None, "up_scale": None,
+         "down_scale": None}
+    u = np.zeros((3, H))
+    u[0, 0], u[1, 0], u[2, 0] = 1.0, -1.0, 0.0
+    y = O.expert_ffn(u, w, "f32")
+    # h = SiLU(30 u) * u
+    assert abs(y[0, 0] - 30 / (1 + math.exp(-30))) < 1e-12
+    assert abs(y[1, 0] - (-30 / (1 + math.exp(30))) * -1.0) < 1e-12
+    assert y[2, 0] == 0.0
+
+
+# ------------------------------------------------------------------ combine and the whole layer
+
+def test_combine_token_example():
+    """a1 y1 + a6 y6 for token A (Chapter 6, section 6.2.6), plus a shared expert term."""
+    y1, y6, sh = np.array([1.0, 2.0]), np.array([-3.0, 0.5]), np.array([0.25, 0.0])
+    y = O.combine_token([0.75, 0.25], np.stack([y1, y6]), sh)
+    assert np.allclose(y, 0.75 * y1 + 0.25 * y6 + sh, rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_layer_identical_experts_equals_dense_ffn(shared):
+    """With every routed expert the same, the weights summing to 1 make the layer equal one
+    FFN of the token, whatever the routing (plus the shared expert when present)."""
+    s = L.LayerSpec("id", T=12, H=128, E=8, k=3, I=128, shared=shared, act="bf16",
+                    w_routed="bf16", w_shared="bf16", router="zipf", zipf_alpha=1.0,
+                    calib_tokens=256, seed=21)
+    r = L.router_inputs(s)
+    e0 = L.expert_weights(s, "routed", 0)
+    routed = {kk: (None if v is None else np.stack([v] * s.E)) for kk, v in e0.items()}
+    sh = L.expert_weights(s, "shared", 0) if shared else None
+    out = O.layer(s, r["x"], r["Wr"], r["bias"], routed, sh)
+    u = L.act_to_f64(r["x"], "bf16")
+    ref = _dense_ref(u, e0, "bf16", s.H, s.I)
+    if shared:
+        ref = ref + _dense_ref(u, sh, "bf16", s.H, s.I)
+    assert np.allclose(out["y"], ref, rtol=1e-10, atol=1e-12)
+    assert len(np.unique(out["topk_idx"])) > s.k  # the routing really varied
+
+
+def test_layer_single_choice_routes_each_token_to_its_expert():
+    """k = 1: y[t] = FFN_{e(t)}(x[t]) exactly, with the expert forced by a dominant bias."""
+    s = L.LayerSpec("k1", T=6, H=128, E=3, k=1, I=128, act="f32", w_routed="f32", seed=5)
+    x = L.store_act(px.normal_f32(5, 1, 0, 0, s.T * s.H).reshape(s.T, s.H), "f32")
+    Wr = np.zeros((s.H, s.E), np.float32)
+    Wr[0] = [0.0, 100.0, -100.0]  # token sign of x[:,0] decides
+    routed = L.stack_experts(s)
+    out = O.layer(s, x, Wr, None, routed, None)
+    for t in range(s.T):
+        e = 1 if x[t, 0] > 0 else 2
+        assert out["topk_idx"][t, 0] == e
+        one = {kk: (None if v is None else v[e]) for kk, v in routed.items()}
+        ref = _dense_ref(x[t:t + 1].astype(np.float64), one, "f32", s.H, s.I)[0]
+        assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_layer_matches_its_own_steps():
+    """The fused layer function equals route -> permute -> per-expert FFN -> combine."""
+    s = L.CONFIGS["c1"]
+    r = L.router_inputs(s)
+    routed = L.stack_experts(s)
+    out = O.layer(s, r["x"], r["Wr"], r["bias"], routed, None)
+    idx, w, _ = O.route(r["x"], r["Wr"], None, s.k, s.act)
+    off, st, ps = O.permute(idx, s.E)
+    assert np.array_equal(idx, out["topk_idx"]) and np.array_equal(ps, out["pair_slot"])
+    u = L.act_to_f64(r["x"], s.act)
+    for t in range(s.T):
+        yk = np.stack([O.expert_ffn(u[t:t + 1], {kk: (None if v is None else v[e])
+                                                 for kk, v in routed.items()}, "f32")[0]
+                       for e in idx[t]])
+        assert np.allclose(O.combine_token(w[t], yk), out["y"][t], rtol=1e-13, atol=1e-15)
