@@ -1,0 +1,363 @@
+// The C ABI (include/moe.h): argument validation, workspace layout and kernel orchestration.
+// Host code only; every step of the layer runs in the kernels it enqueues.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
+int act_bytes(moe_dtype a) { return a == MOE_F32 ? 4 : 2; }
+int pad64(int n) { return (n + 63) / 64 * 64; }
+constexpr int ROW_BLOCK = 64;
+
+bool valid_fmt(int f) { return f >= MOE_F32 && f <= MOE_MXFP4_B32; }
+
+// Bytes of `count` packed K x N matrices and of their packed scales.
+moe_status packed_sizes(moe_dtype fmt, int count, int K, int N, size_t* bytes, size_t* sbytes) {
+  if (!valid_fmt(fmt)) return fail(MOE_ERR_INVALID_ARG, "unknown weight format %d", (int)fmt);
+  if (count < 0 || K < 1 || N < 1) return fail(MOE_ERR_INVALID_ARG, "bad matrix size count=%d K=%d N=%d", count, K, N);
+  const int KP = kp_of(fmt);
+  if (K % KP) return fail(MOE_ERR_INVALID_ARG, "K=%d is not a multiple of %d for format %d", K, KP, (int)fmt);
+  if (fmt == MOE_FP8_E4M3_B128 && (K % 128 || N % 128))
+    return fail(MOE_ERR_INVALID_ARG, "fp8 block-128 scales need K, N multiples of 128 (K=%d N=%d)", K, N);
+  if (fmt == MOE_MXFP4_B32 && N % 2) return fail(MOE_ERR_INVALID_ARG, "MXFP4 packs N=%d in pairs", N);
+  const size_t NT = pad64(N) / 16, KT = K / KP;
+  *bytes = (size_t)count * NT * KT * PACKET_BYTES;
+  if (fmt == MOE_FP8_E4M3_B128)
+    *sbytes = (size_t)count * (K / 128) * (N / 128) * 4;
+  else if (fmt == MOE_MXFP4_B32)
+    *sbytes = (size_t)count * NT * KT * 64;
+  else
+    *sbytes = 0;
+  return MOE_OK;
+}
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", s->T);
+  if (s->H < 128 || s->H % 128) return fail(MOE_ERR_INVALID_ARG, "H=%d must be a positive multiple of 128", s->H);
+  if (s->I < 128 || s->I % 128) return fail(MOE_ERR_INVALID_ARG, "I=%d must be a positive multiple of 128", s->I);
+  if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", s->E);
+  if (s->k < 1 || s->k > s->E || s->k > 16) return fail(MOE_ERR_INVALID_ARG, "k=%d outside [1, min(E, 16)]", s->k);
+  if ((long long)s->T * s->k + s->T > 0x7fffffffLL / 2) return fail(MOE_ERR_INVALID_ARG, "T*k too large");
+  if (s->I_shared != 0 && s->I_shared != s->I)
+    return fail(MOE_ERR_UNSUPPORTED, "I_shared=%d: only 0 or I (=%d) is supported", s->I_shared, s->I);
+  if (s->act != MOE_F32 && s->act != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "act must be F32 or BF16");
+  if (!valid_fmt(s->w_routed) || (s->I_shared && !valid_fmt(s->w_shared)))
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight format");
+  if (s->path < MOE_PATH_AUTO || s->path > MOE_PATH_PREFILL) return fail(MOE_ERR_INVALID_ARG, "bad path %d", (int)s->path);
+  const bool f32 = s->act == MOE_F32;
+  auto ok = [&](moe_dtype w) { return f32 ? w == MOE_F32 : w != MOE_F32; };
+  if (!ok(s->w_routed) || (s->I_shared && !ok(s->w_shared)))
+    return fail(MOE_ERR_UNSUPPORTED, "weights must be F32 with F32 activations and BF16/FP8/MXFP4 with BF16 ones");
+  return MOE_OK;
+}
+
+struct Ws {
+  size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, h, y_perm,
+      y_shared, total;
+};
+
+Ws ws_layout(const moe_shape& s) {
+  const size_t P = (size_t)s.T * s.k, S = s.I_shared ? 1 : 0, R = P + S * s.T;
+  const size_t ab = act_bytes(s.act);
+  Ws w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += up(bytes ? bytes : 1);
+    return at;
+  };
+  w.logits = take((size_t)s.T * pad64(s.E) * 4);
+  w.idx = take(P * 4);
+  w.w = take(P * 4);
+  w.offsets = take(((size_t)s.E + 1) * 4);
+  w.slot_token = take(P * 4);
+  w.pair_slot = take(P * 4);
+  w.rank = take(P * 4);
+  w.hist = take((size_t)permute_blocks((int)P) * s.E * 4);
+  w.group_range = take(((size_t)s.E + 1) * 8);
+  w.cum_blocks = take(((size_t)s.E + 2) * 4);
+  w.h = take(R * s.I * ab);
+  w.y_perm = take(P * s.H * ab);
+  w.y_shared = take(S * s.T * s.H * ab);
+  w.total = o;
+  return w;
+}
+
+moe_status check_ws(const moe_shape& s, void* ws, size_t ws_bytes, Ws* out) {
+  *out = ws_layout(s);
+  if (!ws && out->total) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < out->total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, out->total);
+  if ((uintptr_t)ws % ALIGN) return fail(MOE_ERR_INVALID_ARG, "workspace must be %zu-byte aligned", ALIGN);
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+moe_status check_weights(const moe_weights* w, moe_dtype fmt, const char* what) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "%s weights are NULL", what);
+  if (!w->gate || !w->up || !w->down) return fail(MOE_ERR_INVALID_ARG, "%s weight pointer is NULL", what);
+  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP4_B32) && (!w->gate_scale || !w->up_scale || !w->down_scale))
+    return fail(MOE_ERR_INVALID_ARG, "%s scales are NULL", what);
+  return MOE_OK;
+}
+
+// moe_route without the argument checks.
+moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const float* bias, int32_t* idx,
+                    float* w, void* ws, const Ws& L, hipStream_t st) {
+  if (s.T == 0) return MOE_OK;
+  const int Ep = pad64(s.E);
+  GroupedArgs a{};
+  a.group_range = nullptr;
+  a.cum_blocks = nullptr;
+  a.G = 1;
+  a.shared_group = -1;
+  a.P = s.T;
+  a.M = s.T;
+  a.gather = nullptr;
+  a.act = x;
+  a.lda = s.H;
+  a.act_rows = s.T;
+  a.wa_r = (const uint8_t*)Wr;
+  a.mat_bytes = 0;
+  a.K = s.H;
+  a.N = Ep;
+  a.out = at<float>(ws, L.logits);
+  a.ldo = Ep;
+  hipError_t e = launch_grouped_decode(s.act, EPI_F32, s.act, s.act, a, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
+  if (e != hipSuccess) return hip_status(e, "router scores");
+  e = launch_topk(s.act == MOE_F32, at<float>(ws, L.logits), Ep, bias, s.T, s.E, s.k, idx, w, st);
+  return hip_status(e, "router top-k");
+}
+
+moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int32_t* st_, int32_t* ps, void* ws,
+                      const Ws& L, hipStream_t st) {
+  if (s.T == 0) return hip_status(launch_fill_i32(off, 0, s.E + 1, st), "permute (empty)");
+  hipError_t e = launch_permute(idx, s.T, s.k, s.E, off, st_, ps, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.hist), st);
+  return hip_status(e, "permute");
+}
+
+moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const int32_t* slot_token,
+                  const moe_weights& r, const moe_weights* sh, void* y_perm, void* y_shared, void* ws, const Ws& L,
+                  hipStream_t st) {
+  if (s.T == 0) return MOE_OK;
+  const int P = s.T * s.k, S = s.I_shared ? 1 : 0, G = s.E + S;
+  size_t mb1, sb1, mb2, sb2;
+  moe_status ps = packed_sizes(s.w_routed, 1, s.H, s.I, &mb1, &sb1);
+  if (ps != MOE_OK) return ps;
+  ps = packed_sizes(s.w_routed, 1, s.I, s.H, &mb2, &sb2);
+  if (ps != MOE_OK) return ps;
+  int32_t* gr = at<int32_t>(ws, L.group_range);
+  int32_t* cb = at<int32_t>(ws, L.cum_blocks);
+  hipError_t e = launch_plan(off, s.E, P, s.T, S, ROW_BLOCK, gr, cb, st);
+  if (e != hipSuccess) return hip_status(e, "plan");
+  const int max_rb = std::min(s.E, P) + (P + ROW_BLOCK - 1) / ROW_BLOCK + S * ((s.T + ROW_BLOCK - 1) / ROW_BLOCK);
+
+  GroupedArgs a{};
+  a.group_range = gr;
+  a.cum_blocks = cb;
+  a.G = G;
+  a.shared_group = S ? s.E : -1;
+  a.P = P;
+  a.M = P + S * s.T;
+  // gate/up with the SwiGLU epilogue: h = SiLU(x Wg) * (x Wu)
+  a.gather = slot_token;
+  a.act = x;
+  a.lda = s.H;
+  a.act_rows = s.T;
+  a.wa_r = (const uint8_t*)r.gate;
+  a.wb_r = (const uint8_t*)r.up;
+  a.sa_r = (const uint8_t*)r.gate_scale;
+  a.sb_r = (const uint8_t*)r.up_scale;
+  if (S) {
+    a.wa_s = (const uint8_t*)sh->gate;
+    a.wb_s = (const uint8_t*)sh->up;
+    a.sa_s = (const uint8_t*)sh->gate_scale;
+    a.sb_s = (const uint8_t*)sh->up_scale;
+  }
+  a.mat_bytes = (long long)mb1;
+  a.scale_bytes = (long long)sb1;
+  a.K = s.H;
+  a.N = s.I;
+  a.out = at<void>(ws, L.h);
+  a.ldo = s.I;
+  a.out_s = nullptr;
+  const int cs = S ? s.w_shared : s.w_routed;
+  e = launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
+  if (e != hipSuccess) return hip_status(e, "gate/up grouped GEMM");
+  // down: y = h Wd
+  a.gather = nullptr;
+  a.act = at<void>(ws, L.h);
+  a.lda = s.I;
+  a.act_rows = P + S * s.T;
+  a.wa_r = (const uint8_t*)r.down;
+  a.wb_r = nullptr;
+  a.sa_r = (const uint8_t*)r.down_scale;
+  a.sb_r = nullptr;
+  if (S) {
+    a.wa_s = (const uint8_t*)sh->down;
+    a.wb_s = nullptr;
+    a.sa_s = (const uint8_t*)sh->down_scale;
+    a.sb_s = nullptr;
+  }
+  a.mat_bytes = (long long)mb2;
+  a.scale_bytes = (long long)sb2;
+  a.K = s.I;
+  a.N = s.H;
+  a.out = y_perm;
+  a.ldo = s.H;
+  a.out_s = S ? y_shared : nullptr;
+  a.ldo_s = s.H;
+  e = launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);
+  return hip_status(e, "down grouped GEMM");
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("hidden"))) hipError_t moe_launch_pack(int fmt, int count, int K, int N, const void* w, const void* scale, void* packed,
+                           void* packed_scale, hipStream_t stream);
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_pack_size(moe_dtype fmt, int32_t count, int32_t K, int32_t N, size_t* packed_bytes,
+                         size_t* packed_scale_bytes) {
+  if (!packed_bytes || !packed_scale_bytes) return fail(MOE_ERR_INVALID_ARG, "NULL size pointer");
+  return packed_sizes(fmt, count, K, N, packed_bytes, packed_scale_bytes);
+}
+
+moe_status moe_pack(moe_dtype fmt, int32_t count, int32_t K, int32_t N, const void* w, const void* scale,
+                    void* packed, void* packed_scale, moe_stream_t stream) {
+  size_t b, sb;
+  moe_status s = packed_sizes(fmt, count, K, N, &b, &sb);
+  if (s != MOE_OK) return s;
+  if (count == 0) return MOE_OK;
+  if (!w || !packed) return fail(MOE_ERR_INVALID_ARG, "NULL matrix pointer");
+  if (sb && (!scale || !packed_scale)) return fail(MOE_ERR_INVALID_ARG, "NULL scale pointer");
+  return hip_status(moe_launch_pack(fmt, count, K, N, w, scale, packed, packed_scale, (hipStream_t)stream), "pack");
+}
+
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(*shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (shape->T && (!x || !Wr_packed || !topk_idx || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  Ws L;
+  if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
+  return do_route(*shape, x, Wr_packed, bias, topk_idx, topk_w, ws, L, (hipStream_t)stream);
+}
+
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* expert_offsets,
+                       int32_t* slot_token, int32_t* pair_slot, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (!expert_offsets || (shape->T && (!topk_idx || !slot_token || !pair_slot)))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  Ws L;
+  if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
+  return do_permute(*shape, topk_idx, expert_offsets, slot_token, pair_slot, ws, L, (hipStream_t)stream);
+}
+
+moe_status moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
+                           const int32_t* slot_token, const moe_weights* routed, const moe_weights* shared,
+                           void* y_perm, void* y_shared, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(routed, shape->w_routed, "routed")) != MOE_OK) return s;
+  if (shape->I_shared && (s = check_weights(shared, shape->w_shared, "shared")) != MOE_OK) return s;
+  if (shape->T && (!x || !expert_offsets || !slot_token || !y_perm || (shape->I_shared && !y_shared)))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  Ws L;
+  if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
+  return do_ffn(*shape, x, expert_offsets, slot_token, *routed, shared, y_perm, y_shared, ws, L, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* pair_slot, const float* topk_w,
+                       const void* y_shared, void* y, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (shape->T && (!y_perm || !pair_slot || !topk_w || !y)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  return hip_status(launch_combine(shape->act, y_perm, pair_slot, topk_w, y_shared, y, shape->T, shape->H, shape->k,
+                                   (hipStream_t)stream),
+                    "combine");
+}
+
+moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
+                             const moe_weights* routed, const moe_weights* shared, void* y, int32_t* topk_idx_out,
+                             float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(routed, shape->w_routed, "routed")) != MOE_OK) return s;
+  if (shape->I_shared && (s = check_weights(shared, shape->w_shared, "shared")) != MOE_OK) return s;
+  if (shape->T && (!x || !Wr_packed || !y)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  Ws L;
+  if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
+  if (shape->T == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* off = at<int32_t>(ws, L.offsets);
+  int32_t* slot_token = at<int32_t>(ws, L.slot_token);
+  int32_t* pair_slot = at<int32_t>(ws, L.pair_slot);
+  void* y_perm = at<void>(ws, L.y_perm);
+  void* y_sh = shape->I_shared ? at<void>(ws, L.y_shared) : nullptr;
+  if ((s = do_route(*shape, x, Wr_packed, bias, idx, w, ws, L, st)) != MOE_OK) return s;
+  if ((s = do_permute(*shape, idx, off, slot_token, pair_slot, ws, L, st)) != MOE_OK) return s;
+  if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, st)) != MOE_OK) return s;
+  return hip_status(launch_combine(shape->act, y_perm, pair_slot, w, y_sh, y, shape->T, shape->H, shape->k, st),
+                    "combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,310 @@
+// Decode-regime grouped GEMM: few rows per expert, bound by streaming the expert weights.
+//
+// Work item = (group, block of up to 64 rows of that group, tile of 16*NF output features).
+// The weights are the MFMA A operand (16 features x KP reduction elements per 1 KiB packet, one
+// 128-bit load per lane), the gathered activations the B operand (16 rows), so one
+// v_mfma_f32_16x16x32_bf16 (or 16x16x4_f32) consumes a packet with no data shuffles. The four
+// waves of a workgroup split the rows into 16-row slices and, when there are fewer than 64
+// rows, split the reduction into 2 or 4 contiguous parts whose fp32 partial sums are added in
+// LDS in a fixed order. Each selected expert's weights are therefore streamed once per block
+// of 64 rows (the within-batch reuse of Chapter 6 'Supernodes', section 6.3.2).
+//
+// Epilogues: SwiGLU (gate and up tiles of the same features, h = SiLU(g) * u,
+// Chapter 6 section 6.2.2), plain store in the activation type, or plain fp32 store (router
+// scores).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int RB = 64;  // rows per work item
+
+template <int C>
+struct Codec;
+
+template <>
+struct Codec<MOE_F32> {
+  static constexpr int KP = 16, ACT16 = 1;  // activation 16-byte chunks per packet per lane
+  __device__ static void mma(const u32x4& w, const u32x4* x, float, f32x4& acc) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w[s]), __uint_as_float(x[0][s]), acc, 0, 0, 0);
+  }
+};
+
+template <>
+struct Codec<MOE_BF16> {
+  static constexpr int KP = 32, ACT16 = 1;
+  __device__ static void mma(const u32x4& w, const u32x4* x, float, f32x4& acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                  __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
+  }
+};
+
+// e4m3fn codes -> fp32 (exact, v_cvt_pk_f32_fp8 reads OCP E4M3FN on gfx950) -> * block scale
+// -> bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1, float s) {
+  typedef __attribute__((ext_vector_type(2))) float f2;
+  f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+  f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+  f2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  u32x4 r;
+  r[0] = pack_bf16x2(a.x * s, a.y * s);
+  r[1] = pack_bf16x2(b.x * s, b.y * s);
+  r[2] = pack_bf16x2(c.x * s, c.y * s);
+  r[3] = pack_bf16x2(d.x * s, d.y * s);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <>
+struct Codec<MOE_FP8_E4M3_B128> {
+  static constexpr int KP = 64, ACT16 = 2;
+  __device__ static void mma(const u32x4& w, const u32x4* x, float s, f32x4& acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[0], w[1], s),
+                                                  __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[2], w[3], s),
+                                                  __builtin_bit_cast(bf16x8, x[1]), acc, 0, 0, 0);
+  }
+};
+
+// 8 e2m1 codes (one dword, element 2b in the low nibble of byte b) -> 8 bf16, times 2^(E-127).
+// v_cvt_scalef32_pk_bf16_fp4 is exact here and applies the exponent of `scale`.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <>
+struct Codec<MOE_MXFP4_B32> {
+  static constexpr int KP = 128, ACT16 = 4;
+  __device__ static void mma(const u32x4& w, const u32x4* x, float s, f32x4& acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16(w[i], s),
+                                                    __builtin_bit_cast(bf16x8, x[i]), acc, 0, 0, 0);
+  }
+};
+
+// Scale of the lane's packet (nt, kt).
+template <int C>
+__device__ __forceinline__ float packet_scale(const uint8_t* sc, int N, int KT, int nt, int kt, int lane) {
+  if (C == MOE_FP8_E4M3_B128) {
+    const int kb = (kt * 64 + (lane >> 4) * 16) >> 7;
+    return ((const float*)sc)[kb * (N >> 7) + (nt >> 3)];
+  } else if (C == MOE_MXFP4_B32) {
+    const uint32_t E = sc[((size_t)nt * KT + kt) * 64 + lane];
+    return __uint_as_float(E << 23);
+  }
+  return 1.0f;
+}
+
+template <int EPI>
+struct EpiTraits {
+  static constexpr int NMAT = EPI == EPI_SWIGLU ? 2 : 1;
+};
+
+// One wave: 16 rows x (16*NF) features of NMAT matrices over packets [kt0, kt1).
+template <int C, int ACT, int NMAT, int NF>
+__device__ __forceinline__ void wave_mma(const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
+                                         const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,
+                                         const uint8_t* __restrict__ xrow, int N, int KT, int nt0,
+                                         int kt0, int kt1, int lane, f32x4 (&acc)[NMAT][NF]) {
+  using Cd = Codec<C>;
+  constexpr int AB = ACT == MOE_F32 ? 4 : 2;  // bytes per activation element
+  const size_t lane_off = (size_t)lane * 16;
+#pragma unroll 2
+  for (int kt = kt0; kt < kt1; ++kt) {
+    u32x4 x[Cd::ACT16];
+#pragma unroll
+    for (int i = 0; i < Cd::ACT16; ++i) x[i] = *(const u32x4*)(xrow + (size_t)kt * Cd::KP * AB + i * 16);
+    u32x4 wv[NMAT][NF];
+    float sv[NMAT][NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const size_t off = ((size_t)(nt0 + f) * KT + kt) * PACKET_BYTES + lane_off;
+      wv[0][f] = ld_nt((const u32x4*)(w0 + off));
+      sv[0][f] = packet_scale<C>(s0, N, KT, nt0 + f, kt, lane);
+      if (NMAT == 2) {
+        wv[NMAT - 1][f] = ld_nt((const u32x4*)(w1 + off));
+        sv[NMAT - 1][f] = packet_scale<C>(s1, N, KT, nt0 + f, kt, lane);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) Cd::mma(wv[m][f], x, sv[m][f], acc[m][f]);
+    }
+  }
+}
+
+template <int C, int ACT, int EPI, int NF>
+__device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_shared, int blk, int ntw,
+                                         float* red) {
+  constexpr int NMAT = EpiTraits<EPI>::NMAT;
+  constexpr int KP = Codec<C>::KP;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rbeg = a.group_range ? a.group_range[2 * g] : 0;
+  const int rend = a.group_range ? a.group_range[2 * g + 1] : a.M;
+  const int row0 = rbeg + RB * blk;
+  const int nr = min(RB, rend - row0);
+  const int mtp = nr <= 16 ? 1 : (nr <= 32 ? 2 : 4);
+  const int ks = 4 / mtp;
+  const int msub = wave % mtp, kpart = wave / mtp;
+  const int wr0 = row0 + 16 * msub;
+  const int wnr = nr - 16 * msub;
+  const int KT = a.K / KP;
+  const int kt0 = kpart * KT / ks, kt1 = (kpart + 1) * KT / ks;
+  const int nt0 = ntw * NF;
+
+  // operand pointers
+  const uint8_t* w0 = is_shared ? a.wa_s : a.wa_r + (size_t)g * a.mat_bytes;
+  const uint8_t* w1 = is_shared ? a.wb_s : (a.wb_r ? a.wb_r + (size_t)g * a.mat_bytes : nullptr);
+  const uint8_t* s0 = is_shared ? a.sa_s : (a.sa_r ? a.sa_r + (size_t)g * a.scale_bytes : nullptr);
+  const uint8_t* s1 = is_shared ? a.sb_s : (a.sb_r ? a.sb_r + (size_t)g * a.scale_bytes : nullptr);
+
+  const int rl = lane & 15;
+  const int r = (wnr > 0) ? wr0 + (rl < wnr ? rl : 0) : row0;
+  int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
+  if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
+  constexpr int AB = ACT == MOE_F32 ? 4 : 2;
+  const uint8_t* xrow = (const uint8_t*)a.act + ((size_t)src * a.lda + (lane >> 4) * (KP / 4)) * AB;
+
+  f32x4 acc[NMAT][NF];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (wnr > 0) wave_mma<C, ACT, NMAT, NF>(w0, w1, s0, s1, xrow, a.N, KT, nt0, kt0, kt1, lane, acc);
+
+  if (ks > 1) {  // fixed-order reduction of the reduction-dimension parts
+    constexpr int NREG = NMAT * NF * 4;
+    if (kpart > 0) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[((wave - 1) * NREG + (m * NF + f) * 4 + i) * 64 + lane] = acc[m][f][i];
+    }
+    __syncthreads();
+    if (kpart > 0) return;
+    for (int p = 1; p < ks; ++p) {
+      const int wsrc = msub + mtp * p;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][f][i] += red[((wsrc - 1) * NREG + (m * NF + f) * 4 + i) * 64 + lane];
+    }
+  }
+  if (wnr <= 0 || rl >= wnr) return;
+
+  // epilogue: lane holds features n = (nt0+f)*16 + 4*(lane/16) + i of row wr0 + rl
+  const int orow = wr0 + rl;
+  uint8_t* out;
+  int ldo;
+  size_t row;
+  if (a.out_s && orow >= a.P) {
+    out = (uint8_t*)a.out_s;
+    ldo = a.ldo_s;
+    row = (size_t)(orow - a.P);
+  } else {
+    out = (uint8_t*)a.out;
+    ldo = a.ldo;
+    row = (size_t)orow;
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int n = (nt0 + f) * 16 + 4 * (lane >> 4);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (EPI == EPI_SWIGLU) ? silu(acc[0][f][i]) * acc[NMAT - 1][f][i] : acc[0][f][i];
+    if (EPI == EPI_F32 || ACT == MOE_F32) {
+      *(f32x4*)(out + (row * ldo + n) * 4) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      *(u32x2*)(out + (row * ldo + n) * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+  }
+}
+
+template <int CR, int CS, int ACT, int EPI, int NF>
+__global__ void __launch_bounds__(256) grouped_decode_kernel(GroupedArgs a) {
+  constexpr int NMAT = EpiTraits<EPI>::NMAT;
+  __shared__ float red[3 * NMAT * NF * 4 * 64];
+  const int rbi = blockIdx.x / a.NTW, ntw = blockIdx.x % a.NTW;
+  int g = 0, blk = rbi;
+  if (a.cum_blocks) {
+    if (rbi >= a.cum_blocks[a.G]) return;
+    int lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cum_blocks[mid] <= rbi) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    blk = rbi - a.cum_blocks[g];
+  } else if (rbi * RB >= a.M) {
+    return;
+  }
+  const bool is_shared = g == a.shared_group;
+  if (CR == CS || !is_shared)
+    run_item<CR, ACT, EPI, NF>(a, g, is_shared, blk, ntw, red);
+  else
+    run_item<CS, ACT, EPI, NF>(a, g, is_shared, blk, ntw, red);
+}
+
+// ------------------------------------------------------------------------------------------
+// host side
+// ------------------------------------------------------------------------------------------
+
+template <int CR, int CS, int ACT, int EPI, int NF>
+static hipError_t launch_t(const GroupedArgs& a, int max_row_blocks, hipStream_t st) {
+  GroupedArgs b = a;
+  b.NTW = (a.N / 16) / NF;
+  dim3 grid((unsigned)(max_row_blocks * b.NTW)), block(256);
+  if (grid.x == 0) return hipSuccess;
+  grouped_decode_kernel<CR, CS, ACT, EPI, NF><<<grid, block, 0, st>>>(b);
+  return hipGetLastError();
+}
+
+template <int ACT, int EPI, int NF>
+static hipError_t launch_codecs(int cr, int cs, const GroupedArgs& a, int mrb, hipStream_t st) {
+#define MOE_CASE(R, S) \
+  if (cr == R && cs == S) return launch_t<R, S, ACT, EPI, NF>(a, mrb, st);
+  if (ACT == MOE_F32) {
+    MOE_CASE(MOE_F32, MOE_F32)
+  } else {
+    MOE_CASE(MOE_BF16, MOE_BF16)
+    MOE_CASE(MOE_BF16, MOE_FP8_E4M3_B128)
+    MOE_CASE(MOE_BF16, MOE_MXFP4_B32)
+    MOE_CASE(MOE_FP8_E4M3_B128, MOE_BF16)
+    MOE_CASE(MOE_FP8_E4M3_B128, MOE_FP8_E4M3_B128)
+    MOE_CASE(MOE_FP8_E4M3_B128, MOE_MXFP4_B32)
+    MOE_CASE(MOE_MXFP4_B32, MOE_BF16)
+    MOE_CASE(MOE_MXFP4_B32, MOE_FP8_E4M3_B128)
+    MOE_CASE(MOE_MXFP4_B32, MOE_MXFP4_B32)
+  }
+#undef MOE_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped_decode(int act, int epi, int cr, int cs, const GroupedArgs& a,
+                                 int max_row_blocks, hipStream_t st) {
+  if (a.N % 64 != 0) return hipErrorInvalidValue;
+  if (act == MOE_F32) {
+    if (epi == EPI_SWIGLU) return launch_codecs<MOE_F32, EPI_SWIGLU, 4>(cr, cs, a, max_row_blocks, st);
+    if (epi == EPI_PLAIN) return launch_codecs<MOE_F32, EPI_PLAIN, 4>(cr, cs, a, max_row_blocks, st);
+    return launch_codecs<MOE_F32, EPI_F32, 4>(cr, cs, a, max_row_blocks, st);
+  }
+  if (epi == EPI_SWIGLU) return launch_codecs<MOE_BF16, EPI_SWIGLU, 4>(cr, cs, a, max_row_blocks, st);
+  if (epi == EPI_PLAIN) return launch_codecs<MOE_BF16, EPI_PLAIN, 4>(cr, cs, a, max_row_blocks, st);
+  return launch_codecs<MOE_BF16, EPI_F32, 4>(cr, cs, a, max_row_blocks, st);
+}
+
+}  // namespace moe

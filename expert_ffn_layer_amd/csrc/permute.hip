@@ -1,0 +1,190 @@
+// Permutation of the (token, expert) pairs into expert-contiguous rows, and the row-block plan
+// of the grouped GEMMs.
+//
+// Chapter 6 'Supernodes' section 6.2.6: the receiver regroups its input rows by expert, runs
+// the matrix products, and restores token order by token number. Here that is a stable
+// counting sort of the pairs q = t*k + j by expert (ties in ascending q, i.e. token order):
+//   1. rank:    per block of PB pairs, each pair's rank among earlier pairs of the block with
+//               the same expert (wave ballots, no atomics) and the block's expert histogram;
+//   2. scan:    per expert, exclusive prefix over blocks, then over experts -> offsets;
+//   3. scatter: slot = offsets[e] + prefix over earlier blocks + rank; pair_slot[q] = slot,
+//               slot_token[slot] = q / k.
+// Every result is a pure function of topk_idx: the map is the same on every run.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int PB = 2048;   // pairs per block
+constexpr int PTHR = 256;  // threads per block
+
+int permute_blocks(int P) { return (P + PB - 1) / PB; }
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return lane ? (~0ull >> (64 - lane)) : 0ull; }
+
+__global__ void __launch_bounds__(PTHR) perm_rank_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                         int32_t* __restrict__ rank,
+                                                         int32_t* __restrict__ hist) {
+  extern __shared__ int32_t sm[];  // run[E], wcnt[4][E]
+  int32_t* run = sm;
+  int32_t* wcnt = sm + E;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < 5 * E; e += PTHR) sm[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * PB;
+  for (int c = 0; c < PB; c += PTHR) {
+    const int q = base + c + tid;
+    int e = -1;
+    if (q < P) {
+      e = idx[q];
+      if (e < 0 || e >= E) e = -1;
+    }
+    // rank within the wave among lanes with the same expert, and the wave's counts
+    uint64_t pending = __ballot(e >= 0);
+    int r_in_wave = 0;
+    while (pending) {
+      const int leader = __ffsll((long long)pending) - 1;
+      const int ek = __shfl(e, leader, 64);
+      const uint64_t same = __ballot(e == ek) & pending;
+      if (e == ek) r_in_wave = __popcll(same & lanemask_lt(lane));
+      if (lane == leader) wcnt[wave * E + ek] = __popcll(same);
+      pending &= ~same;
+    }
+    __syncthreads();
+    if (e >= 0) {
+      int r = run[e] + r_in_wave;
+      for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
+      rank[q] = r;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += PTHR) {
+      run[ee] += wcnt[ee] + wcnt[E + ee] + wcnt[2 * E + ee] + wcnt[3 * E + ee];
+      wcnt[ee] = wcnt[E + ee] = wcnt[2 * E + ee] = wcnt[3 * E + ee] = 0;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < E; e += PTHR) hist[(size_t)blockIdx.x * E + e] = run[e];
+}
+
+// Exclusive scan of n <= 2 * blockDim.x ints held in lds[0..n) (in place); returns the total.
+__device__ int block_exclusive_scan(int32_t* lds, int32_t* tmp, int n) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  // Hillis-Steele inclusive scan over 2 elements per thread, ping-ponging lds <-> tmp
+  int32_t* src = lds;
+  int32_t* dst = tmp;
+  for (int off = 1; off < n; off <<= 1) {
+    for (int i = tid; i < n; i += nt) dst[i] = src[i] + (i >= off ? src[i - off] : 0);
+    __syncthreads();
+    int32_t* t = src;
+    src = dst;
+    dst = t;
+  }
+  const int total = n ? src[n - 1] : 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += nt) dst[i] = i ? src[i - 1] : 0;
+  __syncthreads();
+  if (dst != lds)
+    for (int i = tid; i < n; i += nt) lds[i] = dst[i];
+  __syncthreads();
+  return total;
+}
+
+__global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ hist, int NB, int E,
+                                                          int32_t* __restrict__ offsets) {
+  __shared__ int32_t cnt[1024], tmp[1024];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int running = 0;
+    for (int b = 0; b < NB; ++b) {
+      const int c = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = running;
+      running += c;
+    }
+    cnt[e] = running;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(cnt, tmp, E);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    offsets[e] = cnt[e];
+    for (int b = 0; b < NB; ++b) hist[(size_t)b * E + e] += cnt[e];
+  }
+  if (threadIdx.x == 0) offsets[E] = total;
+}
+
+__global__ void __launch_bounds__(PTHR) perm_scatter_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                            int k, const int32_t* __restrict__ rank,
+                                                            const int32_t* __restrict__ base,
+                                                            int32_t* __restrict__ slot_token,
+                                                            int32_t* __restrict__ pair_slot) {
+  const int q = blockIdx.x * PTHR + threadIdx.x;
+  if (q >= P) return;
+  const int e = idx[q];
+  if (e < 0 || e >= E) {
+    pair_slot[q] = -1;
+    return;
+  }
+  const int slot = base[(size_t)(q / PB) * E + e] + rank[q];
+  pair_slot[q] = slot;
+  slot_token[slot] = q / k;
+}
+
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* slot_token,
+                          int32_t* pair_slot, int32_t* ws_rank, int32_t* ws_hist, hipStream_t st) {
+  const int P = T * k;
+  const int NB = permute_blocks(P);
+  if (E > 1024) return hipErrorInvalidValue;
+  perm_rank_kernel<<<NB, PTHR, 5 * E * sizeof(int32_t), st>>>(idx, P, E, ws_rank, ws_hist);
+  perm_scan_kernel<<<1, 1024, 0, st>>>(ws_hist, NB, E, offsets);
+  perm_scatter_kernel<<<(P + PTHR - 1) / PTHR, PTHR, 0, st>>>(idx, P, E, k, ws_rank, ws_hist, slot_token,
+                                                              pair_slot);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Grouped-GEMM plan: the row range [begin, end) of each group (routed expert g from
+// expert_offsets, then the shared expert as group E with rows [P, P+T)), and the prefix count
+// of row blocks of rb rows per group. Offsets are clamped into [0, P] so malformed input
+// cannot produce rows outside the buffers.
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ off, int E, int P, int T,
+                                                     int shared, int rb, int32_t* __restrict__ group_range,
+                                                     int32_t* __restrict__ cum_blocks) {
+  __shared__ int32_t blk[2048], tmp[2048];
+  const int G = E + (shared ? 1 : 0);
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    int b0, b1;
+    if (g < E) {
+      b0 = min(max(off[g], 0), P);
+      b1 = min(max(off[g + 1], b0), P);
+    } else {
+      b0 = P;
+      b1 = P + T;
+    }
+    group_range[2 * g] = b0;
+    group_range[2 * g + 1] = b1;
+    blk[g] = (b1 - b0 + rb - 1) / rb;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(blk, tmp, G);
+  for (int g = threadIdx.x; g < G; g += blockDim.x) cum_blocks[g] = blk[g];
+  if (threadIdx.x == 0) cum_blocks[G] = total;
+}
+
+hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
+                       int32_t* group_range, int32_t* cum_blocks, hipStream_t st) {
+  if (E + 1 > 2048) return hipErrorInvalidValue;
+  plan_kernel<<<1, 1024, 0, st>>>(expert_offsets, E, P, T, shared, rb, group_range, cum_blocks);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  fill_i32_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,184 @@
+/*
+ * moe.h — C ABI of a single-GPU Mixture-of-Experts expert-FFN layer for AMD MI355X (gfx950).
+ *
+ * The layer (sources: "Chapter 6 Supernodes" of the AI-infra book = [ch6];
+ * "DeepSeek-V4-Pro on NVIDIA H200" report = [V4]):
+ *   route    scores l[t][e] = x[t] . Wr[:, e] (+ b[e]); the k largest per token; weights =
+ *            softmax over all E renormalised over the k chosen            [ch6 §6.2.6; V4 D4]
+ *   permute  regroup the (token, expert) pairs by expert, stable in token order, and keep the
+ *            map back to token order                             [ch6 §6.2.6, receiver side]
+ *   FFN      each expert e on its rows X_e: Y_e = [SiLU(X_e Wg_e) (.) (X_e Wu_e)] Wd_e
+ *                                                                 [ch6 §6.2.2, SwiGLU; V4 D6]
+ *   shared   an always-active expert of the same form, weight 1           [V4 §0.1.2, §3.2]
+ *   combine  y[t] = sum_j w[t][j] Y[pair_slot[t k + j]] + Y_shared[t]    [ch6 §6.2.6, §6.4.1]
+ *
+ * Conventions (all functions):
+ *   - Every pointer argument is device memory owned by the caller, except the moe_shape /
+ *     moe_weights structs, which are host memory read during the call only.
+ *   - Functions validate their arguments on the host, then only enqueue kernels on `stream`
+ *     and return. MOE_OK means "enqueued"; results are valid in stream order (the same
+ *     contract the chapter describes for collective calls, [ch6 §6.4.3]). No function
+ *     synchronises, allocates or frees memory, or copies data-dependent sizes to the host.
+ *   - Scratch memory comes from the caller's workspace `ws` (moe_workspace_size); the library
+ *     keeps no mutable global state, so calls on different streams with different
+ *     workspaces may run concurrently.
+ *   - Errors are returned as codes, never thrown; on an error nothing has been enqueued,
+ *     except MOE_ERR_HIP (a launch failed; moe_last_error() has the runtime's message).
+ *   - Row-major everywhere. Activations x, y are [T][H] in the `act` type.
+ *
+ * Weights are read in the packed layout written by moe_pack (once, at weight-load time): see
+ * moe_pack for the layout and for which logical matrix each argument is.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* a hipStream_t; NULL = the null stream */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,       /* null required pointer, bad size, bad dtype */
+  MOE_ERR_UNSUPPORTED = 2,       /* a valid but unimplemented combination */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                /* a kernel launch failed */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,            /* float32 */
+  MOE_BF16 = 1,           /* bfloat16 */
+  MOE_FP8_E4M3_B128 = 2,  /* OCP E4M3FN codes + one fp32 scale per 128 x 128 block */
+  MOE_MXFP4_B32 = 3       /* OCP e2m1 codes + one e8m0 exponent per 32 reduction elements */
+} moe_dtype;
+
+typedef enum {
+  MOE_PATH_AUTO = 0,      /* pick by the average rows per expert */
+  MOE_PATH_DECODE = 1,    /* weight-streaming grouped GEMM (few rows per expert) */
+  MOE_PATH_PREFILL = 2    /* LDS-tiled MFMA grouped GEMM (many rows per expert) */
+} moe_path;
+
+typedef struct {
+  int32_t T;          /* tokens, >= 1 */
+  int32_t H;          /* hidden size, multiple of 128 */
+  int32_t E;          /* routed experts, 1..1024 */
+  int32_t k;          /* experts per token, 1..min(E, 16) */
+  int32_t I;          /* expert intermediate size, multiple of 128 */
+  int32_t I_shared;   /* shared expert intermediate size: 0 = no shared expert, else == I */
+  moe_dtype act;      /* MOE_F32 or MOE_BF16: x, Wr, y and the intermediates */
+  moe_dtype w_routed; /* MOE_F32 (with act MOE_F32) or BF16 / FP8 / MXFP4 (with act BF16) */
+  moe_dtype w_shared; /* same rule */
+  moe_path path;
+} moe_shape;
+
+/* Packed weights of one kind (routed: E experts back to back; shared: one expert). */
+typedef struct {
+  const void* gate;        /* packed W_gate (logical [H][I] per expert) */
+  const void* up;          /* packed W_up   (logical [H][I]) */
+  const void* down;        /* packed W_down (logical [I][H]) */
+  const void* gate_scale;  /* packed scales, NULL for F32 / BF16 */
+  const void* up_scale;
+  const void* down_scale;
+} moe_weights;
+
+/* Readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* Detail text of the last error returned on this thread (static storage, thread-local). */
+const char* moe_last_error(void);
+
+/*
+ * moe_pack_size / moe_pack — convert `count` logical K x N matrices (back to back) from the
+ * row-major layout in which the chapter writes them (W[k][n]: k indexes the reduction, n the
+ * output feature; [ch6 §6.2.2]) to the packed layout the kernels stream.
+ *
+ * Logical (source) formats, per matrix:
+ *   MOE_F32   float[K][N]                MOE_BF16  uint16[K][N] (bf16 bits)
+ *   MOE_FP8_E4M3_B128  uint8[K][N] codes + float[K/128][N/128] scales (w = e4m3(c) * s)
+ *   MOE_MXFP4_B32      uint8[K][N/2] codes, even n in the low nibble + uint8[K/32][N] e8m0
+ *                      exponents (w = e2m1(c) * 2^(E-127))
+ * Packed layout: 1 KiB packets of 16 features x KP reduction elements (KP = 16, 32, 64, 128 for
+ * F32, BF16, FP8, MXFP4), packet (nt, kt) at byte (nt*(K/KP) + kt)*1024, lane l of a packet
+ * holding feature nt*16 + l%16 and reduction run kt*KP + (l/16)*KP/4 + [0, KP/4). FP8 scales
+ * are copied unchanged; MXFP4 scales are regrouped one byte per lane per packet.
+ * N is padded up to a multiple of 64 with zero features (only the router, N = E, needs it).
+ * Requirements: K a multiple of KP (and of 128 for FP8), N a multiple of 16 (128 for FP8, 2
+ * for MXFP4) before padding. `packed_scale` may be NULL for F32 / BF16.
+ * Router: pack Wr[H][E] as one K = H, N = E matrix in the `act` format.
+ */
+moe_status moe_pack_size(moe_dtype fmt, int32_t count, int32_t K, int32_t N,
+                         size_t* packed_bytes, size_t* packed_scale_bytes);
+moe_status moe_pack(moe_dtype fmt, int32_t count, int32_t K, int32_t N, const void* w,
+                    const void* scale, void* packed, void* packed_scale, moe_stream_t stream);
+
+/* Scratch bytes moe_layer_forward / moe_grouped_ffn / moe_permute / moe_route need for
+ * `shape` (the same workspace serves any of them). */
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/*
+ * moe_route — router scores, top-k and weights [ch6 §6.2.6; V4 D4].
+ *   x        [T][H] act          Wr_packed  packed Wr (K = H, N = E, act format)
+ *   bias     float[E] or NULL: added to the scores (selection and weights)
+ *   topk_idx int32[T][k] out: chosen experts in ascending index; an exact tie at the k-th
+ *            place goes to the lower index
+ *   topk_w   float[T][k] out: exp(l - m) / sum over the chosen of exp(l - m), m = max score
+ */
+moe_status moe_route(const moe_shape* shape, const void* x, const void* Wr_packed,
+                     const float* bias, int32_t* topk_idx, float* topk_w, void* ws,
+                     size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_permute — stable counting sort of the pairs q = t*k + j by expert [ch6 §6.2.6].
+ *   topk_idx       int32[T*k] in: values in [0, E) (entries outside are skipped)
+ *   expert_offsets int32[E+1] out: rows of expert e are [off[e], off[e+1]); off[E] = T*k
+ *   slot_token     int32[T*k] out: token of each row (slot)
+ *   pair_slot      int32[T*k] out: row of each pair
+ * Deterministic: no atomics decide an order.
+ */
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx,
+                       int32_t* expert_offsets, int32_t* slot_token, int32_t* pair_slot,
+                       void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_grouped_ffn — every expert's SwiGLU on its rows, plus the shared expert on all tokens
+ * [ch6 §6.2.2; V4 D6].
+ *   x              [T][H] act
+ *   expert_offsets, slot_token: from moe_permute
+ *   routed         packed routed weights (E experts)
+ *   shared         packed shared weights, or NULL when I_shared == 0
+ *   y_perm         [T*k][H] act out: row r = FFN_e(x[slot_token[r]]) for the e owning r
+ *   y_shared       [T][H] act out (NULL when I_shared == 0)
+ * The intermediate SiLU(x Wg) (.) (x Wu) is kept in `ws` in the act type; accumulation fp32.
+ */
+moe_status moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
+                           const int32_t* slot_token, const moe_weights* routed,
+                           const moe_weights* shared, void* y_perm, void* y_shared, void* ws,
+                           size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_combine — y[t] = sum_{j<k} topk_w[t][j] * y_perm[pair_slot[t*k+j]] + y_shared[t], summed
+ * in ascending j in fp32, one gather per output row, no atomics [ch6 §6.2.6, §6.4.1].
+ *   y_shared may be NULL.
+ */
+moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* pair_slot,
+                       const float* topk_w, const void* y_shared, void* y, moe_stream_t stream);
+
+/*
+ * moe_layer_forward — route, permute, grouped FFN and combine in one call (V4 §8.3: router
+ * top-k, grouped expert weight reads, Linear-1/activation/Linear-2, combine).
+ *   y              [T][H] act out
+ *   topk_idx_out   int32[T][k] or NULL; topk_w_out float[T][k] or NULL (copies of the routing)
+ */
+moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* Wr_packed,
+                             const float* bias, const moe_weights* routed,
+                             const moe_weights* shared, void* y, int32_t* topk_idx_out,
+                             float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

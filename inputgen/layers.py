@@ -215,13 +215,17 @@ def topk_gap(logits: np.ndarray, k: int) -> np.ndarray:
     return part[:, k - 1] - part[:, k]
 
 
-def activations(spec: LayerSpec, Wr_stored: np.ndarray, bias, max_attempts: int = 256):
+def activations(spec: LayerSpec, Wr_stored: np.ndarray, bias, max_attempts: int = 256, x0=None):
     """x[T, H] in the act format, with rows redrawn until the router margin holds.
 
+    ``x0`` may hold the attempt-0 draw already (e.g. from the GPU fill, which is bit-identical).
     Returns (x_stored, attempts[T]) where attempts[t] is the stream x[t] finally came from.
     """
     T, H = spec.T, spec.H
-    x = store_act(draw_f32(spec.seed, TID_X, 0, (T, H)), spec.act)
+    if x0 is None:
+        x = store_act(draw_f32(spec.seed, TID_X, 0, (T, H)), spec.act)
+    else:
+        x = np.array(x0, copy=True)
     attempts = np.zeros(T, np.int32)
     W = act_to_f64(Wr_stored, spec.act)
     b = np.zeros(spec.E) if bias is None else np.asarray(bias, np.float64)

@@ -140,7 +140,7 @@ int oracle_route(int T, int H, int E, int k, int act, const void* x, const void*
                  const float* bias, int32_t* topk_idx, double* topk_w, double* logits_out) {
   if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return 1;
   int bad = 0;
-#pragma omp parallel for schedule(dynamic, 4)
+#pragma omp parallel for schedule(dynamic, 4) if (T > 1)
   for (int t = 0; t < T; ++t) {
     double* l = (double*)malloc(sizeof(double) * E);
     char* chosen = (char*)calloc(E, 1);
@@ -222,7 +222,7 @@ int oracle_expert_ffn(int H, int I, int M, int fmt, const void* wg, const void* 
                       const void* wu, const void* su, const void* wd, const void* sd,
                       const double* u, double* y) {
   int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) if (M > 1)
   for (int m = 0; m < M; ++m) {
     double* g = (double*)malloc(sizeof(double) * I);
     double* v = (double*)malloc(sizeof(double) * I);

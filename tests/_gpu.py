@@ -1,0 +1,107 @@
+"""Helpers of the GPU tests: build a synthetic layer on the device, run it through the C ABI,
+and compute the oracle's answer for all or for sampled tokens."""
+from __future__ import annotations
+
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+from expert_ffn_layer_amd import native as N
+from expert_ffn_layer_amd.layer import PackedLayer
+from inputgen import gpu as G
+from inputgen import layers as L
+from oracle import oracle as O
+
+TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 4e-2, "mxfp4": 4e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tol_of(spec):
+    fmts = [spec.w_routed] + ([spec.w_shared] if spec.shared else [])
+    if spec.act == "f32":
+        return TOL["f32"]
+    return max(TOL[f] for f in fmts)
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def act_torch(spec):
+    return torch.float32 if spec.act == "f32" else torch.bfloat16
+
+
+def to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def build(spec, dev, path="auto"):
+    lay = G.layer_on_device(spec, dev)
+    pl = PackedLayer(spec, lay["Wr"], lay["routed"], lay["shared"], path=path)
+    return lay, pl
+
+
+def run(spec, lay, pl):
+    dev = lay["x"].device
+    y = torch.empty((spec.T, spec.H), dtype=act_torch(spec), device=dev)
+    idx = torch.empty((spec.T, spec.k), dtype=torch.int32, device=dev)
+    w = torch.empty((spec.T, spec.k), dtype=torch.float32, device=dev)
+    x = lay["x"] if spec.act == "f32" else lay["x"].view(torch.bfloat16)
+    pl.forward(x, lay["bias"], y, idx, w)
+    torch.cuda.synchronize()
+    return y, idx, w
+
+
+def host_weights(d, experts=None):
+    """Stored weights (device) -> numpy, for all experts or the listed ones."""
+    out = {}
+    for k, v in d.items():
+        if v is None:
+            out[k] = None
+        elif experts is None:
+            out[k] = G.to_numpy_stored(v)
+        else:
+            out[k] = G.to_numpy_stored(v[list(experts)])
+    return out
+
+
+def oracle_full(spec, lay):
+    routed = host_weights(lay["routed"])
+    shared = None
+    if spec.shared:
+        shared = {k: (None if v is None else v[0]) for k, v in host_weights(lay["shared"]).items()}
+    return O.layer(spec, lay["x_host"], lay["Wr_host"], lay["bias_host"], routed, shared)
+
+
+def oracle_tokens(spec, lay, idx, w, tokens, threads=16):
+    """Oracle output rows for the listed tokens, given the oracle's routing (idx, w)."""
+    need = sorted({int(e) for t in tokens for e in idx[t]})
+    routed = host_weights(lay["routed"], need)
+    pos = {e: i for i, e in enumerate(need)}
+    shared = None
+    if spec.shared:
+        shared = {k: (None if v is None else v[0]) for k, v in host_weights(lay["shared"]).items()}
+    u = L.act_to_f64(lay["x_host"], spec.act)
+
+    def ffn(t, e):
+        if e < 0:
+            return O.expert_ffn(u[t:t + 1], shared, spec.w_shared)[0]
+        one = {k: (None if v is None else v[pos[e]]) for k, v in routed.items()}
+        return O.expert_ffn(u[t:t + 1], one, spec.w_routed)[0]
+
+    jobs = [(t, int(e)) for t in tokens for e in idx[t]] + ([(t, -1) for t in tokens] if spec.shared else [])
+    with ThreadPoolExecutor(threads) as ex:
+        res = dict(zip(jobs, ex.map(lambda j: ffn(*j), jobs)))
+    out = []
+    for t in tokens:
+        yk = np.stack([res[(t, int(e))] for e in idx[t]])
+        out.append(O.combine_token(w[t], yk, res[(t, -1)] if spec.shared else None))
+    return np.stack(out)

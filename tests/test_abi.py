@@ -1,0 +1,98 @@
+"""The C ABI library loads, exports every function include/moe.h declares, and rejects bad
+arguments on the host before launching anything (no GPU needed for these)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from expert_ffn_layer_amd import native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "moe.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(N.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = N.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)", out))
+    assert exported == set(_declared())  # nothing undeclared leaks out
+
+
+def test_status_strings():
+    lib = N.load()
+    for code, name in N.STATUS.items():
+        assert lib.moe_status_string(code).decode() == name
+
+
+def _shape(**kw):
+    base = dict(T=4, H=256, E=8, k=2, I=128, I_shared=0, act="bf16", w_routed="bf16", w_shared="bf16")
+    base.update(kw)
+    return N.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), 1), (dict(H=100), 1), (dict(I=64), 1), (dict(E=0), 1), (dict(E=2000), 1),
+    (dict(k=0), 1), (dict(k=9), 1), (dict(E=32, k=17), 1), (dict(I_shared=256), 2),
+    (dict(act="fp8"), 1), (dict(act="f32"), 2), (dict(w_routed="f32"), 2),
+])
+def test_shape_validation(kw, status):
+    with pytest.raises(N.MoeError) as e:
+        N.moe_workspace_size(_shape(**kw))
+    assert e.value.status == status
+
+
+def test_workspace_grows_with_tokens_and_shared_expert():
+    a = N.moe_workspace_size(_shape(T=4))
+    b = N.moe_workspace_size(_shape(T=64))
+    c = N.moe_workspace_size(_shape(T=64, I_shared=128))
+    assert 0 < a < b < c
+    assert N.moe_workspace_size(_shape(T=0)) > 0
+
+
+def test_pack_sizes():
+    assert N.moe_pack_size("bf16", 3, 4096, 1536) == (3 * 4096 * 1536 * 2, 0)
+    assert N.moe_pack_size("f32", 1, 256, 128) == (256 * 128 * 4, 0)
+    assert N.moe_pack_size("fp8", 2, 7168, 2048) == (2 * 7168 * 2048, 2 * 56 * 16 * 4)
+    assert N.moe_pack_size("mxfp4", 1, 7168, 3072) == (7168 * 3072 // 2, 7168 * 3072 // 32)
+    # the router's E is padded to 64 features
+    assert N.moe_pack_size("bf16", 1, 256, 8) == (256 * 64 * 2, 0)
+    for fmt, K, Nn in (("fp8", 7168, 100), ("fp8", 100, 128), ("bf16", 48, 64), ("mxfp4", 128, 3)):
+        with pytest.raises(N.MoeError):
+            N.moe_pack_size(fmt, 1, K, Nn)
+
+
+def test_entry_points_reject_null_and_small_workspace_before_launch():
+    lib = N.load()
+    s = _shape()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first
+    assert lib.moe_route(ctypes.byref(s), None, fake, None, fake, fake, fake, 1 << 30, None) == 1
+    # workspace too small
+    assert lib.moe_route(ctypes.byref(s), fake, fake, None, fake, fake, fake, 16, None) == 3
+    w = N.MoeWeights(0x1000, 0x1000, None, None, None, None)
+    assert lib.moe_grouped_ffn(ctypes.byref(s), fake, fake, fake, ctypes.byref(w), None, fake, None, fake,
+                               1 << 30, None) == 1
+    s8 = _shape(w_routed="fp8")
+    w8 = N.MoeWeights(0x1000, 0x1000, 0x1000, None, None, None)  # fp8 needs scales
+    assert lib.moe_layer_forward(ctypes.byref(s8), fake, fake, None, ctypes.byref(w8), None, fake, None, None,
+                                 fake, 1 << 30, None) == 1
+    assert "scales" in lib.moe_last_error().decode()
+    sh = _shape(I_shared=128)
+    wf = N.MoeWeights(0x1000, 0x1000, 0x1000, None, None, None)
+    assert lib.moe_layer_forward(ctypes.byref(sh), fake, fake, None, ctypes.byref(wf), None, fake, None, None,
+                                 fake, 1 << 30, None) == 1  # shared weights missing
+    # misaligned workspace
+    assert lib.moe_permute(ctypes.byref(s), fake, fake, fake, fake, P(0x1001), 1 << 30, None) == 1

@@ -1,0 +1,229 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by element on the
+same seeded inputs. Routing indices, offsets and the permutation must be identical; outputs
+must meet the relative Frobenius bound of their precision (1e-5 fp32, 1e-2 bf16, 4e-2 fp8 and
+MXFP4); routing weights within 1e-5."""
+import numpy as np
+import pytest
+import torch
+
+from expert_ffn_layer_amd import native as N
+from expert_ffn_layer_amd.layer import PackedLayer, pack
+from inputgen import gpu as G
+from inputgen import layers as L
+from inputgen import philox as px
+from oracle import oracle as O
+
+from _gpu import build, oracle_full, oracle_tokens, rel_fro, run, say, to_f64, tol_of
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    N.load()
+    G.lib()
+    yield
+
+
+# ------------------------------------------------------------------ the input generator
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4"])
+def test_gpu_generator_is_bit_identical_to_numpy(fmt):
+    K, Nn = 256, 384
+    c, s = G.alloc_matrices(fmt, 2, K, Nn, DEV)
+    G.fill_matrices(c, s, fmt, 7, 17, 3, K, Nn, K)
+    for m in range(2):
+        ref = L.store_matrix(L.draw_f32(7, 17, 3 + m, (K, Nn), K), fmt)
+        assert np.array_equal(G.to_numpy_stored(c[m]), ref["w"])
+        if s is not None:
+            assert np.array_equal(G.to_numpy_stored(s[m]), ref["scale"])
+
+
+def test_gpu_activations_bit_identical():
+    spec = L.CONFIGS["c2"].replace(T=40, H=1024)
+    x = G.to_numpy_stored(G.activations_attempt0(spec, DEV))
+    assert np.array_equal(x, L.store_act(L.draw_f32(spec.seed, L.TID_X, 0, (spec.T, spec.H)), "bf16"))
+
+
+# ------------------------------------------------------------------ packing
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4"])
+def test_pack_layout(fmt):
+    """Unpack the packed bytes with numpy following the documented layout."""
+    K, Nn = 256, 384
+    c, s = G.alloc_matrices(fmt, 1, K, Nn, DEV)
+    G.fill_matrices(c, s, fmt, 3, 16, 0, K, Nn, K)
+    packed, pscale = pack(fmt, c, s, K, Nn)
+    torch.cuda.synchronize()
+    KP = {"f32": 16, "bf16": 32, "fp8": 64, "mxfp4": 128}[fmt]
+    ebytes = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}[fmt]
+    NT, KT = Nn // 16, K // KP
+    raw = packed.cpu().numpy().reshape(NT, KT, 64, 16)
+    stored = G.to_numpy_stored(c[0])
+    if fmt == "mxfp4":
+        codes = np.empty((K, Nn), np.uint8)
+        codes[:, 0::2], codes[:, 1::2] = stored & 15, stored >> 4
+        lanes = np.stack([raw & 15, raw >> 4], axis=-1).reshape(NT, KT, 64, 32)
+    elif fmt == "fp8":
+        codes, lanes = stored, raw
+    else:
+        dt = np.float32 if fmt == "f32" else np.uint16
+        codes, lanes = stored, raw.view(dt).reshape(NT, KT, 64, -1)
+    run_len = KP // 4
+    rebuilt = np.empty((K, Nn), codes.dtype)
+    for l in range(64):
+        n = np.arange(NT)[:, None] * 16 + l % 16
+        for kt in range(KT):
+            k0 = kt * KP + (l // 16) * run_len
+            rebuilt[k0:k0 + run_len, n[:, 0]] = lanes[:, kt, l, :run_len].T
+    assert np.array_equal(rebuilt, codes)
+    if fmt == "fp8":
+        assert np.array_equal(pscale.cpu().numpy().view(np.float32).reshape(s[0].shape), s[0].cpu().numpy())
+    if fmt == "mxfp4":
+        ps = pscale.cpu().numpy().reshape(NT, KT, 64)
+        sc = G.to_numpy_stored(s[0])
+        for l in range(64):
+            for kt in range(KT):
+                assert np.array_equal(ps[:, kt, l], sc[(kt * KP + (l // 16) * 32) // 32, np.arange(NT) * 16 + l % 16])
+
+
+# ------------------------------------------------------------------ whole layer, small shapes
+
+SMALL = [
+    # name, spec overrides
+    ("c1", L.CONFIGS["c1"]),
+    ("bf16-shared-zipf", L.LayerSpec("s1", T=37, H=512, E=16, k=4, I=256, shared=True, router="zipf",
+                                     zipf_alpha=1.0, calib_tokens=512, seed=31)),
+    ("bf16-big-groups", L.LayerSpec("s2", T=300, H=256, E=4, k=2, I=128, seed=32)),
+    ("fp8-shared", L.LayerSpec("s3", T=50, H=512, E=8, k=3, I=256, shared=True, w_routed="fp8",
+                               w_shared="fp8", router="zipf", zipf_alpha=1.2, calib_tokens=512, seed=33)),
+    ("mxfp4-bf16-shared", L.LayerSpec("s4", T=20, H=512, E=24, k=6, I=384, shared=True, w_routed="mxfp4",
+                                      w_shared="bf16", seed=34)),
+    ("one-token", L.LayerSpec("s5", T=1, H=256, E=8, k=8, I=128, seed=35)),
+    ("k1-f32", L.LayerSpec("s6", T=70, H=384, E=3, k=1, I=256, act="f32", w_routed="f32", w_shared="f32",
+                           shared=True, seed=36)),
+    ("wide-E", L.LayerSpec("s7", T=9, H=256, E=300, k=7, I=128, seed=37)),
+]
+
+
+@pytest.mark.parametrize("name,spec", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("path", ["auto"])
+def test_layer_small(name, spec, path):
+    say("layer", name, spec)
+    lay, pl = build(spec, DEV, path)
+    y, idx, w = run(spec, lay, pl)
+    ref = oracle_full(spec, lay)
+    assert np.array_equal(idx.cpu().numpy(), ref["topk_idx"])
+    assert np.max(np.abs(w.cpu().numpy() - ref["topk_w"])) <= 1e-5
+    err = rel_fro(to_f64(y), ref["y"])
+    say("  rel. Frobenius error %.3e (bound %.0e)" % (err, tol_of(spec)))
+    assert err <= tol_of(spec)
+    # deterministic: a second call gives the same bits
+    y2, idx2, w2 = run(spec, lay, pl)
+    assert torch.equal(y, y2) and torch.equal(idx, idx2) and torch.equal(w, w2)
+
+
+def test_layer_zero_tokens_is_a_no_op():
+    spec = L.CONFIGS["c1"]
+    lay, pl = build(spec, DEV)
+    pl.set_tokens(0)
+    y = torch.full((1, spec.H), 7.0, device=DEV)
+    pl.forward(lay["x"], None, y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+# ------------------------------------------------------------------ the four stages one by one
+
+def test_stages_match_oracle_stage_by_stage():
+    spec = L.LayerSpec("st", T=45, H=512, E=12, k=3, I=256, shared=True, router="zipf", zipf_alpha=1.0,
+                       calib_tokens=512, seed=41)
+    lay, pl = build(spec, DEV)
+    s = pl.shape
+    T, k, E, H = spec.T, spec.k, spec.E, spec.H
+    x = lay["x"].view(torch.bfloat16)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    N.moe_route(s, x, pl.Wr, lay["bias"], idx, w, pl.ws)
+    ridx, rw, _ = O.route(lay["x_host"], lay["Wr_host"], lay["bias_host"], k, spec.act)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-5
+    # permutation from the oracle's routing
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    st = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    ps = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    N.moe_permute(s, torch.from_numpy(ridx).to(DEV), off, st, ps, pl.ws)
+    roff, rst, rps = O.permute(ridx, E)
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(st.cpu().numpy(), rst) and np.array_equal(ps.cpu().numpy(), rps)
+    # grouped FFN from the oracle's permutation
+    yp = torch.empty((T * k, H), dtype=torch.bfloat16, device=DEV)
+    ysh = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    N.moe_grouped_ffn(s, x, torch.from_numpy(roff).to(DEV), torch.from_numpy(rst).to(DEV), pl.routed, pl.shared,
+                      yp, ysh, pl.ws)
+    torch.cuda.synchronize()
+    from _gpu import host_weights
+    rt = host_weights(lay["routed"])
+    sh = {kk: (None if v is None else v[0]) for kk, v in host_weights(lay["shared"]).items()}
+    u = L.act_to_f64(lay["x_host"], "bf16")
+    ref_perm = np.zeros((T * k, H))
+    for e in range(E):
+        r0, r1 = roff[e], roff[e + 1]
+        if r1 > r0:
+            one = {kk: (None if v is None else v[e]) for kk, v in rt.items()}
+            ref_perm[r0:r1] = O.expert_ffn(u[rst[r0:r1]], one, "bf16")
+    ref_sh = O.expert_ffn(u, sh, "bf16")
+    assert rel_fro(to_f64(yp), ref_perm) <= 1e-2
+    assert rel_fro(to_f64(ysh), ref_sh) <= 1e-2
+    # combine from the oracle's intermediate rows (rounded to bf16, the act type)
+    yp_ref = torch.from_numpy(ref_perm).to(torch.bfloat16).to(DEV)
+    ysh_ref = torch.from_numpy(ref_sh).to(torch.bfloat16).to(DEV)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    N.moe_combine(s, yp_ref, torch.from_numpy(rps).to(DEV), torch.from_numpy(rw.astype(np.float32)).to(DEV),
+                  ysh_ref, y)
+    torch.cuda.synchronize()
+    ypr, yshr = to_f64(yp_ref), to_f64(ysh_ref)
+    ref_y = np.stack([O.combine_token(rw[t], ypr[rps[t * k:(t + 1) * k]], yshr[t]) for t in range(T)])
+    assert rel_fro(to_f64(y), ref_y) <= 4e-3  # only the final bf16 rounding differs
+
+
+# ------------------------------------------------------------------ full-size layers
+
+FULL = ["c2", "c3", "c4", "c5"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", FULL)
+def test_full_size_layer(cfg):
+    """The bench's launch configuration at full size: routing and permutation identical for
+    every token, outputs against the oracle on sampled tokens."""
+    spec = L.CONFIGS[cfg]
+    say("full-size", cfg, spec)
+    lay, pl = build(spec, DEV)
+    y, idx, w = run(spec, lay, pl)
+    say("  ran; oracle routing")
+    ridx, rw, _ = O.route(lay["x_host"], lay["Wr_host"], lay["bias_host"], spec.k, spec.act)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-5
+    # the permutation the layer used
+    roff, rst, rps = O.permute(ridx, spec.E)
+    s = pl.shape
+    off = torch.empty(spec.E + 1, dtype=torch.int32, device=DEV)
+    st = torch.empty(spec.T * spec.k, dtype=torch.int32, device=DEV)
+    ps = torch.empty(spec.T * spec.k, dtype=torch.int32, device=DEV)
+    N.moe_permute(s, idx, off, st, ps, pl.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(st.cpu().numpy(), rst) and np.array_equal(ps.cpu().numpy(), rps)
+    counts = np.diff(roff)
+    hot = int(np.argmax(counts))
+    rng = np.random.default_rng(7)
+    tokens = sorted({0, spec.T - 1, int(rst[roff[hot]]), *rng.choice(spec.T, 5, replace=False).tolist()})
+    say("  active experts %d, max rows %d; oracle on tokens %s" % ((counts > 0).sum(), counts.max(), tokens))
+    ref = oracle_tokens(spec, lay, ridx, rw, tokens)
+    err = rel_fro(to_f64(y)[tokens], ref)
+    say("  rel. Frobenius error on sampled tokens %.3e (bound %.0e)" % (err, tol_of(spec)))
+    assert err <= tol_of(spec)
