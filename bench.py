@@ -1,0 +1,201 @@
+"""Benchmark of one MoE expert-FFN layer forward on one MI355X.
+
+A step is one call of moe_layer_forward (router -> permute -> grouped SwiGLU FFN -> combine)
+over one batch of T synthetic tokens, with every input already resident in HBM. Prints one
+JSON line: whole-step tokens/s, the layer's algorithmic HBM GB/s and TFLOP/s, the dominant
+kernel's roofline fraction (its duration measured with HIP events on the launch stream), and
+the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--config c2] [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+# bounded CPU-oracle samples (tokens): about 10-30 s of oracle work per config
+CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard "
+              "by experts across GPUs; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from expert_ffn_layer_amd import native as N
+    from expert_ffn_layer_amd import perfmodel as pm
+    from expert_ffn_layer_amd.layer import PackedLayer
+    from inputgen import gpu as G
+    from inputgen import layers as L
+
+    N.load()
+    dev = torch.device("cuda:0")
+    spec = L.CONFIGS[args.config]
+    log("bench: generating %s on the device" % spec.name)
+    lay = G.layer_on_device(spec, dev)
+    pl = PackedLayer(spec, lay["Wr"], lay["routed"], lay["shared"], path=args.path)
+    # the stored (unpacked) copies are only needed by the CPU baseline; free HBM otherwise
+    x = lay["x"] if spec.act == "f32" else lay["x"].view(torch.bfloat16)
+    act_dt = torch.float32 if spec.act == "f32" else torch.bfloat16
+    y = torch.empty((spec.T, spec.H), dtype=act_dt, device=dev)
+    idx = torch.empty((spec.T, spec.k), dtype=torch.int32, device=dev)
+    w = torch.empty((spec.T, spec.k), dtype=torch.float32, device=dev)
+    bias = lay["bias"]
+
+    def step():
+        N.moe_layer_forward(pl.shape, x, pl.Wr, bias, pl.routed, pl.shared, y, idx, w, pl.ws)
+
+    log("bench: warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=spec.E)
+    traffic = pm.layer_traffic(spec, counts)
+
+    log("bench: timing %d steps" % args.steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel durations, live, with events recorded between the kernels of each forward
+    log("bench: per-stage timing")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(N.TIMED_EVENTS)]
+    for e in evs:
+        e.record()  # creates the underlying HIP events
+    names = ["route", "permute", "plan", "gate_up", "down", "combine"]
+    acc = np.zeros(len(names))
+    for _ in range(args.steps):
+        N.moe_layer_forward_timed(pl.shape, x, pl.Wr, bias, pl.routed, pl.shared, y, evs, idx, w, pl.ws)
+        torch.cuda.synchronize()
+        acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
+    stage_ms = acc / args.steps
+
+    # roofline of the dominant kernel (the gate/up grouped GEMM)
+    H, I, T, k = spec.H, spec.I, spec.T, spec.k
+    R = T * k + (T if spec.shared else 0)
+    ab = 4 if spec.act == "f32" else 2
+    gu_bytes = (traffic["active_experts"] * 2 * pm.matrix_bytes(H, I, spec.w_routed)
+                + (2 * pm.matrix_bytes(H, I, spec.w_shared) if spec.shared else 0)
+                + T * H * ab + R * I * ab)
+    gu_flops = 4 * H * I * R
+    gu_ms = stage_ms[names.index("gate_up")]
+    prefill = (T * k) / spec.E >= 64
+    if prefill:
+        peak = MFMA_PEAK_TFLOPS["bf16" if spec.act == "bf16" else "f32"]
+        ach = gu_flops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "kernel": "gate/up grouped GEMM",
+                "per_launch": {"flops": gu_flops, "ms": round(gu_ms, 4)}}
+    else:
+        ach = gu_bytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "gate/up grouped GEMM",
+                "per_launch": {"bytes": gu_bytes, "ms": round(gu_ms, 4)}}
+
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.act,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "T": T, "H": H, "E": spec.E, "k": k, "I": I,
+                   "shared_expert": spec.shared, "w_routed": spec.w_routed,
+                   "w_shared": spec.w_shared if spec.shared else None, "router": spec.router,
+                   "zipf_alpha": spec.zipf_alpha or None, "active_experts": traffic["active_experts"],
+                   "max_rows_per_expert": int(counts.max())},
+        "hbm_GBps": round(traffic["bytes"] / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(traffic["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "tflops": round(traffic["flops"] / (ms * 1e-3) / 1e12, 2),
+        "algorithmic": {"bytes": traffic["bytes"], "flops": traffic["flops"]},
+        "stages_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(spec, lay, args.cpu_tokens or CPU_TOKENS[args.config])
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(spec, lay, S):
+    """The oracle, as it stands, on the first S tokens of the same layer (host cores)."""
+    import numpy as np
+
+    from inputgen import gpu as G
+    from oracle import oracle as O
+
+    S = min(S, spec.T)
+    log("bench: CPU oracle on %d tokens" % S)
+    x = lay["x_host"][:S]
+    idx, wts, _ = O.route(x, lay["Wr_host"], lay["bias_host"], spec.k, spec.act)
+    need = sorted(set(idx.reshape(-1).tolist()))
+    routed = {k: None if v is None else G.to_numpy_stored(v[need]) for k, v in lay["routed"].items()}
+    shared = None
+    if spec.shared:
+        shared = {k: None if v is None else G.to_numpy_stored(v[0]) for k, v in lay["shared"].items()}
+    import os as _os
+    cores = int(_os.environ.get("OMP_NUM_THREADS", _os.cpu_count() or 1))
+    t = time.perf_counter()
+    from inputgen.layers import act_to_f64
+    idx, wts, _ = O.route(x, lay["Wr_host"], lay["bias_host"], spec.k, spec.act)
+    off, st, ps = O.permute(idx, spec.E)
+    u = act_to_f64(x, spec.act)
+    yperm = np.zeros((S * spec.k, spec.H))
+    for j, e in enumerate(need):
+        r0, r1 = off[e], off[e + 1]
+        one = {k: None if v is None else v[j] for k, v in routed.items()}
+        yperm[r0:r1] = O.expert_ffn(u[st[r0:r1]], one, spec.w_routed)
+    ysh = O.expert_ffn(u, shared, spec.w_shared) if spec.shared else None
+    for tkn in range(S):
+        O.combine_token(wts[tkn], yperm[ps[tkn * spec.k:(tkn + 1) * spec.k]], None if ysh is None else ysh[tkn])
+    dt = time.perf_counter() - t
+    return {"value": round(S / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d of %d tokens of the same layer (route, permute, %d active experts' SwiGLU%s, "
+                      "combine), fp64 C oracle, %.1f s" % (S, spec.T, len(need),
+                                                           " + shared expert" if spec.shared else "", dt)}
+
+
+if __name__ == "__main__":
+    main()

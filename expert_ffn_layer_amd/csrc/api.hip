@@ -169,9 +169,14 @@ moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int3
   return hip_status(e, "permute");
 }
 
+moe_status record(hipEvent_t ev, hipStream_t st) {
+  return ev ? hip_status(hipEventRecord(ev, st), "event record") : MOE_OK;
+}
+
+// ev (optional, 3 events): recorded after the plan, after gate/up and after down.
 moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const int32_t* slot_token,
                   const moe_weights& r, const moe_weights* sh, void* y_perm, void* y_shared, void* ws, const Ws& L,
-                  hipStream_t st) {
+                  hipStream_t st, hipEvent_t const* ev = nullptr) {
   if (s.T == 0) return MOE_OK;
   const int P = s.T * s.k, S = s.I_shared ? 1 : 0, G = s.E + S;
   size_t mb1, sb1, mb2, sb2;
@@ -183,6 +188,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   int32_t* cb = at<int32_t>(ws, L.cum_blocks);
   hipError_t e = launch_plan(off, s.E, P, s.T, S, ROW_BLOCK, gr, cb, st);
   if (e != hipSuccess) return hip_status(e, "plan");
+  moe_status rs;
+  if (ev && (rs = record(ev[0], st)) != MOE_OK) return rs;
   const int max_rb = std::min(s.E, P) + (P + ROW_BLOCK - 1) / ROW_BLOCK + S * ((s.T + ROW_BLOCK - 1) / ROW_BLOCK);
 
   GroupedArgs a{};
@@ -217,6 +224,7 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   const int cs = S ? s.w_shared : s.w_routed;
   e = launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
   if (e != hipSuccess) return hip_status(e, "gate/up grouped GEMM");
+  if (ev && (rs = record(ev[1], st)) != MOE_OK) return rs;
   // down: y = h Wd
   a.gather = nullptr;
   a.act = at<void>(ws, L.h);
@@ -241,7 +249,40 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.out_s = S ? y_shared : nullptr;
   a.ldo_s = s.H;
   e = launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);
-  return hip_status(e, "down grouped GEMM");
+  if (e != hipSuccess) return hip_status(e, "down grouped GEMM");
+  return ev ? record(ev[2], st) : MOE_OK;
+}
+
+moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
+                    const moe_weights* routed, const moe_weights* shared, void* y, int32_t* topk_idx_out,
+                    float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t const* ev) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(routed, shape->w_routed, "routed")) != MOE_OK) return s;
+  if (shape->I_shared && (s = check_weights(shared, shape->w_shared, "shared")) != MOE_OK) return s;
+  if (shape->T && (!x || !Wr_packed || !y)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  Ws L;
+  if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
+  if (shape->T == 0) return MOE_OK;
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* off = at<int32_t>(ws, L.offsets);
+  int32_t* slot_token = at<int32_t>(ws, L.slot_token);
+  int32_t* pair_slot = at<int32_t>(ws, L.pair_slot);
+  void* y_perm = at<void>(ws, L.y_perm);
+  void* y_sh = shape->I_shared ? at<void>(ws, L.y_shared) : nullptr;
+  if (ev && (s = record(ev[0], st)) != MOE_OK) return s;
+  if ((s = do_route(*shape, x, Wr_packed, bias, idx, w, ws, L, st)) != MOE_OK) return s;
+  if (ev && (s = record(ev[1], st)) != MOE_OK) return s;
+  if ((s = do_permute(*shape, idx, off, slot_token, pair_slot, ws, L, st)) != MOE_OK) return s;
+  if (ev && (s = record(ev[2], st)) != MOE_OK) return s;
+  if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, st, ev ? ev + 3 : nullptr)) !=
+      MOE_OK)
+    return s;
+  s = hip_status(launch_combine(shape->act, y_perm, pair_slot, w, y_sh, y, shape->T, shape->H, shape->k, st),
+                 "combine");
+  if (s == MOE_OK && ev) s = record(ev[6], st);
+  return s;
 }
 
 }  // namespace
@@ -337,27 +378,19 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
 moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
                              const moe_weights* routed, const moe_weights* shared, void* y, int32_t* topk_idx_out,
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
-  moe_status s = check_shape(shape);
-  if (s != MOE_OK) return s;
-  if ((s = check_weights(routed, shape->w_routed, "routed")) != MOE_OK) return s;
-  if (shape->I_shared && (s = check_weights(shared, shape->w_shared, "shared")) != MOE_OK) return s;
-  if (shape->T && (!x || !Wr_packed || !y)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
-  Ws L;
-  if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
-  if (shape->T == 0) return MOE_OK;
-  hipStream_t st = (hipStream_t)stream;
-  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
-  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
-  int32_t* off = at<int32_t>(ws, L.offsets);
-  int32_t* slot_token = at<int32_t>(ws, L.slot_token);
-  int32_t* pair_slot = at<int32_t>(ws, L.pair_slot);
-  void* y_perm = at<void>(ws, L.y_perm);
-  void* y_sh = shape->I_shared ? at<void>(ws, L.y_shared) : nullptr;
-  if ((s = do_route(*shape, x, Wr_packed, bias, idx, w, ws, L, st)) != MOE_OK) return s;
-  if ((s = do_permute(*shape, idx, off, slot_token, pair_slot, ws, L, st)) != MOE_OK) return s;
-  if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, st)) != MOE_OK) return s;
-  return hip_status(launch_combine(shape->act, y_perm, pair_slot, w, y_sh, y, shape->T, shape->H, shape->k, st),
-                    "combine");
+  return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, ws_bytes,
+                  (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_layer_forward_timed(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
+                                   const moe_weights* routed, const moe_weights* shared, void* y,
+                                   int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                                   moe_stream_t stream, moe_event_t* events) {
+  if (!events) return fail(MOE_ERR_INVALID_ARG, "events is NULL");
+  for (int i = 0; i < MOE_TIMED_EVENTS; ++i)
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "event %d is NULL", i);
+  return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, ws_bytes,
+                  (hipStream_t)stream, (hipEvent_t const*)events);
 }
 
 }  // extern "C"

@@ -18,7 +18,9 @@ PATH = {"auto": 0, "decode": 1, "prefill": 2}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_pack_size", "moe_pack", "moe_workspace_size",
-           "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward")
+           "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
+           "moe_layer_forward_timed")
+TIMED_EVENTS = 7
 
 
 class MoeError(RuntimeError):
@@ -64,6 +66,8 @@ def load() -> ctypes.CDLL:
         lib.moe_grouped_ffn.argtypes = [PS, P, P, P, PW, PW, P, P, P, SZ, P]
         lib.moe_combine.argtypes = [PS, P, P, P, P, P, P]
         lib.moe_layer_forward.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P]
+        lib.moe_layer_forward_timed.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P,
+                                                ctypes.POINTER(ctypes.c_void_p)]
         for name in EXPORTS[2:]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -150,3 +154,14 @@ def moe_layer_forward(shape, x, Wr_packed, bias, routed: dict, shared: dict | No
                                     None if s is None else ctypes.byref(s), _p(y), _p(topk_idx), _p(topk_w),
                                     _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def moe_layer_forward_timed(shape, x, Wr_packed, bias, routed: dict, shared: dict | None, y, events,
+                            topk_idx=None, topk_w=None, ws=None, stream=None):
+    """``events``: TIMED_EVENTS torch.cuda.Event(enable_timing=True) objects."""
+    r, s = weights(routed), weights(shared)
+    arr = (ctypes.c_void_p * TIMED_EVENTS)(*[e.cuda_event for e in events])
+    _check(load().moe_layer_forward_timed(ctypes.byref(shape), _p(x), _p(Wr_packed), _p(bias), ctypes.byref(r),
+                                          None if s is None else ctypes.byref(s), _p(y), _p(topk_idx),
+                                          _p(topk_w), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                          _stream(stream), arr))

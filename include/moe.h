@@ -40,6 +40,7 @@ extern "C" {
 #endif
 
 typedef struct ihipStream_t* moe_stream_t; /* a hipStream_t; NULL = the null stream */
+typedef struct ihipEvent_t* moe_event_t;   /* a hipEvent_t */
 
 typedef enum {
   MOE_OK = 0,
@@ -177,6 +178,20 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              const float* bias, const moe_weights* routed,
                              const moe_weights* shared, void* y, int32_t* topk_idx_out,
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_layer_forward_timed — moe_layer_forward that also records `events` (MOE_TIMED_EVENTS
+ * caller-created HIP events) on `stream` around its kernels, for per-stage timing:
+ *   [0] start   [1] after route   [2] after permute   [3] after the grouped-GEMM plan
+ *   [4] after the gate/up grouped GEMM   [5] after the down grouped GEMM   [6] after combine
+ * Same results as moe_layer_forward. With T == 0 nothing is recorded.
+ */
+#define MOE_TIMED_EVENTS 7
+moe_status moe_layer_forward_timed(const moe_shape* shape, const void* x, const void* Wr_packed,
+                                   const float* bias, const moe_weights* routed,
+                                   const moe_weights* shared, void* y, int32_t* topk_idx_out,
+                                   float* topk_w_out, void* ws, size_t ws_bytes,
+                                   moe_stream_t stream, moe_event_t* events);
 
 #ifdef __cplusplus
 }
