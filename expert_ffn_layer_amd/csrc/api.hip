@@ -80,6 +80,18 @@ moe_status check_shape(const moe_shape* s) {
   return MOE_OK;
 }
 
+// Split-K factor of the router scores: enough workgroups (about 512) to stream Wr at full rate
+// when T is small; every part keeps at least 8 packets of the reduction.
+int router_ksplit(const moe_shape& s) {
+  if (s.T <= 0) return 1;
+  const int rbk = (s.T + ROW_BLOCK - 1) / ROW_BLOCK;
+  const int ntw = pad64(s.E) / 16 / decode_nf(s.act, EPI_F32);
+  const int KT = s.H / kp_of(s.act);
+  int ks = (512 + rbk * ntw - 1) / (rbk * ntw);
+  ks = std::min(ks, std::max(1, KT / 8));
+  return std::max(ks, 1);
+}
+
 struct Ws {
   size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, h, y_perm,
       y_shared, total;
@@ -95,7 +107,7 @@ Ws ws_layout(const moe_shape& s) {
     o += up(bytes ? bytes : 1);
     return at;
   };
-  w.logits = take((size_t)s.T * pad64(s.E) * 4);
+  w.logits = take((size_t)router_ksplit(s) * s.T * pad64(s.E) * 4);
   w.idx = take(P * 4);
   w.w = take(P * 4);
   w.offsets = take(((size_t)s.E + 1) * 4);
@@ -156,16 +168,26 @@ moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const flo
   a.N = Ep;
   a.out = at<float>(ws, L.logits);
   a.ldo = Ep;
+  a.ksplit = router_ksplit(s);
   hipError_t e = launch_grouped_decode(s.act, EPI_F32, s.act, s.act, a, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
   if (e != hipSuccess) return hip_status(e, "router scores");
-  e = launch_topk(s.act == MOE_F32, at<float>(ws, L.logits), Ep, bias, s.T, s.E, s.k, idx, w, st);
+  e = launch_topk(at<float>(ws, L.logits), Ep, a.ksplit, bias, s.T, s.E, s.k, idx, w, st);
   return hip_status(e, "router top-k");
 }
 
+// with_plan: also write the grouped-GEMM plan into the workspace (returns whether it did)
 moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int32_t* st_, int32_t* ps, void* ws,
-                      const Ws& L, hipStream_t st) {
+                      const Ws& L, hipStream_t st, bool with_plan = false, bool* planned = nullptr) {
+  if (planned) *planned = false;
   if (s.T == 0) return hip_status(launch_fill_i32(off, 0, s.E + 1, st), "permute (empty)");
-  hipError_t e = launch_permute(idx, s.T, s.k, s.E, off, st_, ps, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.hist), st);
+  hipError_t e;
+  if (permute_small_ok(s.T * s.k, s.E)) {
+    e = launch_permute_small(idx, s.T, s.k, s.E, s.I_shared ? 1 : 0, ROW_BLOCK, off, st_, ps,
+                             with_plan ? at<int32_t>(ws, L.group_range) : nullptr, at<int32_t>(ws, L.cum_blocks), st);
+    if (planned) *planned = with_plan;
+  } else {
+    e = launch_permute(idx, s.T, s.k, s.E, off, st_, ps, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.hist), st);
+  }
   return hip_status(e, "permute");
 }
 
@@ -176,7 +198,7 @@ moe_status record(hipEvent_t ev, hipStream_t st) {
 // ev (optional, 3 events): recorded after the plan, after gate/up and after down.
 moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const int32_t* slot_token,
                   const moe_weights& r, const moe_weights* sh, void* y_perm, void* y_shared, void* ws, const Ws& L,
-                  hipStream_t st, hipEvent_t const* ev = nullptr) {
+                  hipStream_t st, hipEvent_t const* ev = nullptr, bool plan_ready = false) {
   if (s.T == 0) return MOE_OK;
   const int P = s.T * s.k, S = s.I_shared ? 1 : 0, G = s.E + S;
   size_t mb1, sb1, mb2, sb2;
@@ -186,7 +208,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   if (ps != MOE_OK) return ps;
   int32_t* gr = at<int32_t>(ws, L.group_range);
   int32_t* cb = at<int32_t>(ws, L.cum_blocks);
-  hipError_t e = launch_plan(off, s.E, P, s.T, S, ROW_BLOCK, gr, cb, st);
+  hipError_t e = hipSuccess;
+  if (!plan_ready) e = launch_plan(off, s.E, P, s.T, S, ROW_BLOCK, gr, cb, st);
   if (e != hipSuccess) return hip_status(e, "plan");
   moe_status rs;
   if (ev && (rs = record(ev[0], st)) != MOE_OK) return rs;
@@ -274,10 +297,11 @@ moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed
   if (ev && (s = record(ev[0], st)) != MOE_OK) return s;
   if ((s = do_route(*shape, x, Wr_packed, bias, idx, w, ws, L, st)) != MOE_OK) return s;
   if (ev && (s = record(ev[1], st)) != MOE_OK) return s;
-  if ((s = do_permute(*shape, idx, off, slot_token, pair_slot, ws, L, st)) != MOE_OK) return s;
+  bool planned = false;
+  if ((s = do_permute(*shape, idx, off, slot_token, pair_slot, ws, L, st, true, &planned)) != MOE_OK) return s;
   if (ev && (s = record(ev[2], st)) != MOE_OK) return s;
-  if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, st, ev ? ev + 3 : nullptr)) !=
-      MOE_OK)
+  if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, st, ev ? ev + 3 : nullptr,
+                  planned)) != MOE_OK)
     return s;
   s = hip_status(launch_combine(shape->act, y_perm, pair_slot, w, y_sh, y, shape->T, shape->H, shape->k, st),
                  "combine");

@@ -108,38 +108,104 @@ struct EpiTraits {
   static constexpr int NMAT = EPI == EPI_SWIGLU ? 2 : 1;
 };
 
-// One wave: 16 rows x (16*NF) features of NMAT matrices over packets [kt0, kt1).
+// Registers of one pipeline stage: U consecutive packets of each of the NMAT x NF streams,
+// the matching activation chunks and the packets' scales.
+template <int C, int NMAT, int NF, int U>
+struct Stage {
+  u32x4 x[U][Codec<C>::ACT16];
+  u32x4 w[U][NMAT][NF];
+  float s[U][NMAT][NF];
+};
+
+// Issue the loads of packets kt .. kt+U-1 (indices past kt1-1 re-read packet kt1-1 and are
+// not used, so every address stays inside the stream).
+template <int C, int ACT, int NMAT, int NF, int U>
+__device__ __forceinline__ void load_stage(Stage<C, NMAT, NF, U>& st, const uint8_t* __restrict__ w0,
+                                           const uint8_t* __restrict__ w1, const uint8_t* __restrict__ s0,
+                                           const uint8_t* __restrict__ s1, const uint8_t* __restrict__ xrow, int N,
+                                           int KT, int nt0, int kt, int kt1, int lane) {
+  using Cd = Codec<C>;
+  constexpr int AB = ACT == MOE_F32 ? 4 : 2;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = min(kt + u, kt1 - 1);
+#pragma unroll
+    for (int i = 0; i < Cd::ACT16; ++i) st.x[u][i] = *(const u32x4*)(xrow + (size_t)k * Cd::KP * AB + i * 16);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const size_t off = ((size_t)(nt0 + f) * KT + k) * PACKET_BYTES + (size_t)lane * 16;
+      st.w[u][0][f] = ld_nt((const u32x4*)(w0 + off));
+      st.s[u][0][f] = packet_scale<C>(s0, N, KT, nt0 + f, k, lane);
+      if (NMAT == 2) {
+        st.w[u][NMAT - 1][f] = ld_nt((const u32x4*)(w1 + off));
+        st.s[u][NMAT - 1][f] = packet_scale<C>(s1, N, KT, nt0 + f, k, lane);
+      }
+    }
+  }
+}
+
+template <int C, int NMAT, int NF, int U>
+__device__ __forceinline__ void mma_stage(const Stage<C, NMAT, NF, U>& st, f32x4 (&acc)[NMAT][NF]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) Codec<C>::mma(st.w[u][m][f], st.x[u], st.s[u][m][f], acc[m][f]);
+}
+
+// The same with the weight operand of packets kt + u >= kt1 replaced by zero codes (which
+// decode to 0 in every format), so the MFMAs stay unconditional: no branches around them.
+template <int C, int NMAT, int NF, int U>
+__device__ __forceinline__ void mma_stage_masked(const Stage<C, NMAT, NF, U>& st, int kt, int kt1,
+                                                 f32x4 (&acc)[NMAT][NF]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool valid = kt + u < kt1;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+        Codec<C>::mma(valid ? st.w[u][m][f] : zero, st.x[u], st.s[u][m][f], acc[m][f]);
+  }
+}
+
+// Packets per pipeline stage along K, chosen so a stage keeps about 8 weight packets (4 for the
+// formats converted in registers, whose temporaries would otherwise cost occupancy) and at most
+// 8 activation chunks per lane in flight.
+template <int C, int NMAT, int NF>
+constexpr int stage_depth() {
+  constexpr int per_stage = (C == MOE_BF16 || C == MOE_F32) ? 8 : 4;
+  constexpr int a = per_stage / (NF * NMAT), b = 8 / Codec<C>::ACT16;
+  constexpr int u = a < b ? a : b;
+  return u < 1 ? 1 : u;
+}
+
+// One wave: 16 rows x (16*NF) features of NMAT matrices over packets [kt0, kt1), with the
+// loads of the next stage in flight while the current stage feeds the MFMAs.
 template <int C, int ACT, int NMAT, int NF>
 __device__ __forceinline__ void wave_mma(const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
                                          const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,
                                          const uint8_t* __restrict__ xrow, int N, int KT, int nt0,
                                          int kt0, int kt1, int lane, f32x4 (&acc)[NMAT][NF]) {
-  using Cd = Codec<C>;
-  constexpr int AB = ACT == MOE_F32 ? 4 : 2;  // bytes per activation element
-  const size_t lane_off = (size_t)lane * 16;
-#pragma unroll 2
-  for (int kt = kt0; kt < kt1; ++kt) {
-    u32x4 x[Cd::ACT16];
-#pragma unroll
-    for (int i = 0; i < Cd::ACT16; ++i) x[i] = *(const u32x4*)(xrow + (size_t)kt * Cd::KP * AB + i * 16);
-    u32x4 wv[NMAT][NF];
-    float sv[NMAT][NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const size_t off = ((size_t)(nt0 + f) * KT + kt) * PACKET_BYTES + lane_off;
-      wv[0][f] = ld_nt((const u32x4*)(w0 + off));
-      sv[0][f] = packet_scale<C>(s0, N, KT, nt0 + f, kt, lane);
-      if (NMAT == 2) {
-        wv[NMAT - 1][f] = ld_nt((const u32x4*)(w1 + off));
-        sv[NMAT - 1][f] = packet_scale<C>(s1, N, KT, nt0 + f, kt, lane);
-      }
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) Cd::mma(wv[m][f], x, sv[m][f], acc[m][f]);
-    }
+  constexpr int U = stage_depth<C, NMAT, NF>();
+  if (kt0 >= kt1) return;
+  Stage<C, NMAT, NF, U> A, B;
+  load_stage<C, ACT, NMAT, NF, U>(A, w0, w1, s0, s1, xrow, N, KT, nt0, kt0, kt1, lane);
+  int kt = kt0;
+  // steady state: both stages entirely inside the range, so every load and MFMA is
+  // unconditional and the wait counts stay exact (the next stage's loads remain in flight)
+  for (; kt + 2 * U < kt1; kt += 2 * U) {
+    load_stage<C, ACT, NMAT, NF, U>(B, w0, w1, s0, s1, xrow, N, KT, nt0, kt + U, kt1, lane);
+    mma_stage(A, acc);
+    load_stage<C, ACT, NMAT, NF, U>(A, w0, w1, s0, s1, xrow, N, KT, nt0, kt + 2 * U, kt1, lane);
+    mma_stage(B, acc);
   }
+  // remainder (1 .. 2U packets), branch-free: packets past the range are masked to zero
+  load_stage<C, ACT, NMAT, NF, U>(B, w0, w1, s0, s1, xrow, N, KT, nt0, kt + U, kt1, lane);
+  mma_stage_masked(A, kt, kt1, acc);
+  mma_stage_masked(B, kt + U, kt1, acc);
 }
 
 template <int C, int ACT, int EPI, int NF>
@@ -158,7 +224,11 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
   const int wr0 = row0 + 16 * msub;
   const int wnr = nr - 16 * msub;
   const int KT = a.K / KP;
-  const int kt0 = kpart * KT / ks, kt1 = (kpart + 1) * KT / ks;
+  // reduction range of this workgroup (split-K across workgroups for fp32 partial outputs), then
+  // of this wave
+  const int KS = a.ksplit > 1 ? a.ksplit : 1;
+  const int ktA = blockIdx.y * KT / KS, ktB = (blockIdx.y + 1) * KT / KS;
+  const int kt0 = ktA + kpart * (ktB - ktA) / ks, kt1 = ktA + (kpart + 1) * (ktB - ktA) / ks;
   const int nt0 = ntw * NF;
 
   // operand pointers
@@ -218,7 +288,7 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
   } else {
     out = (uint8_t*)a.out;
     ldo = a.ldo;
-    row = (size_t)orow;
+    row = (size_t)orow + (size_t)blockIdx.y * a.M;  // split-K part y of an fp32 output
   }
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
@@ -267,17 +337,17 @@ template <int CR, int CS, int ACT, int EPI, int NF>
 static hipError_t launch_t(const GroupedArgs& a, int max_row_blocks, hipStream_t st) {
   GroupedArgs b = a;
   b.NTW = (a.N / 16) / NF;
-  dim3 grid((unsigned)(max_row_blocks * b.NTW)), block(256);
+  dim3 grid((unsigned)(max_row_blocks * b.NTW), (unsigned)(a.ksplit > 1 ? a.ksplit : 1)), block(256);
   if (grid.x == 0) return hipSuccess;
   grouped_decode_kernel<CR, CS, ACT, EPI, NF><<<grid, block, 0, st>>>(b);
   return hipGetLastError();
 }
 
-template <int ACT, int EPI, int NF>
+template <int ACT, int EPI>
 static hipError_t launch_codecs(int cr, int cs, const GroupedArgs& a, int mrb, hipStream_t st) {
 #define MOE_CASE(R, S) \
-  if (cr == R && cs == S) return launch_t<R, S, ACT, EPI, NF>(a, mrb, st);
-  if (ACT == MOE_F32) {
+  if (cr == R && cs == S) return launch_t<R, S, ACT, EPI, decode_nf(R, EPI)>(a, mrb, st);
+  if constexpr (ACT == MOE_F32) {
     MOE_CASE(MOE_F32, MOE_F32)
   } else {
     MOE_CASE(MOE_BF16, MOE_BF16)
@@ -296,15 +366,15 @@ static hipError_t launch_codecs(int cr, int cs, const GroupedArgs& a, int mrb, h
 
 hipError_t launch_grouped_decode(int act, int epi, int cr, int cs, const GroupedArgs& a,
                                  int max_row_blocks, hipStream_t st) {
-  if (a.N % 64 != 0) return hipErrorInvalidValue;
+  if (a.N % (16 * decode_nf(cr, epi)) != 0) return hipErrorInvalidValue;
   if (act == MOE_F32) {
-    if (epi == EPI_SWIGLU) return launch_codecs<MOE_F32, EPI_SWIGLU, 4>(cr, cs, a, max_row_blocks, st);
-    if (epi == EPI_PLAIN) return launch_codecs<MOE_F32, EPI_PLAIN, 4>(cr, cs, a, max_row_blocks, st);
-    return launch_codecs<MOE_F32, EPI_F32, 4>(cr, cs, a, max_row_blocks, st);
+    if (epi == EPI_SWIGLU) return launch_codecs<MOE_F32, EPI_SWIGLU>(cr, cs, a, max_row_blocks, st);
+    if (epi == EPI_PLAIN) return launch_codecs<MOE_F32, EPI_PLAIN>(cr, cs, a, max_row_blocks, st);
+    return launch_codecs<MOE_F32, EPI_F32>(cr, cs, a, max_row_blocks, st);
   }
-  if (epi == EPI_SWIGLU) return launch_codecs<MOE_BF16, EPI_SWIGLU, 4>(cr, cs, a, max_row_blocks, st);
-  if (epi == EPI_PLAIN) return launch_codecs<MOE_BF16, EPI_PLAIN, 4>(cr, cs, a, max_row_blocks, st);
-  return launch_codecs<MOE_BF16, EPI_F32, 4>(cr, cs, a, max_row_blocks, st);
+  if (epi == EPI_SWIGLU) return launch_codecs<MOE_BF16, EPI_SWIGLU>(cr, cs, a, max_row_blocks, st);
+  if (epi == EPI_PLAIN) return launch_codecs<MOE_BF16, EPI_PLAIN>(cr, cs, a, max_row_blocks, st);
+  return launch_codecs<MOE_BF16, EPI_F32>(cr, cs, a, max_row_blocks, st);
 }
 
 }  // namespace moe

@@ -40,7 +40,14 @@ struct GroupedArgs {
   int ldo;
   void* out_s;
   int ldo_s;
+  int ksplit;  // > 1: fp32 output only; workgroup y sums K part y into out + y * M * ldo
 };
+
+// Output features (in units of 16) per decode work item: a small item (16-32 features) keeps
+// the scheduling granularity far below one CU's share of the weight stream.
+__host__ __device__ constexpr int decode_nf(int codec, int epi) {
+  return epi == EPI_SWIGLU ? (codec == 3 /* MXFP4 */ ? 2 : 1) : (epi == EPI_F32 ? 1 : 2);
+}
 
 hipError_t launch_grouped_decode(int act, int epi, int cr, int cs, const GroupedArgs& a,
                                  int max_row_blocks, hipStream_t st);
@@ -48,12 +55,16 @@ hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const Groupe
                                   hipStream_t st);
 hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
                        int32_t* group_range, int32_t* cum_blocks, hipStream_t st);
-hipError_t launch_topk(int act_is_f32, const float* logits, int ldl, const float* bias, int T, int E,
-                       int k, int32_t* idx, float* w, hipStream_t st);
+hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
+                       int32_t* idx, float* w, hipStream_t st);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* slot_token, int32_t* pair_slot, int32_t* ws_rank,
                           int32_t* ws_hist, hipStream_t st);
 int permute_blocks(int P);
+bool permute_small_ok(int P, int E);
+hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int shared, int rb, int32_t* offsets,
+                                int32_t* slot_token, int32_t* pair_slot, int32_t* group_range, int32_t* cum_blocks,
+                                hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t st);
 hipError_t launch_combine(int act, const void* y_perm, const int32_t* pair_slot, const float* w,
                           const void* y_shared, void* y, int T, int H, int k, hipStream_t st);

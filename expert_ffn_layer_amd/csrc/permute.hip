@@ -176,6 +176,112 @@ hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int s
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------
+// Decode-sized batches (P <= SMALL_P, E <= SMALL_E): the whole permutation, and optionally the
+// grouped-GEMM plan, in one workgroup of 16 waves, so a decode step pays one launch instead of
+// four. Same ranks as the multi-block path: per chunk of 1024 pairs, the rank among earlier
+// pairs of the same expert from wave ballots and per-wave counts, in ascending pair order.
+// ------------------------------------------------------------------------------------------
+constexpr int SMALL_THR = 1024, SMALL_CHUNKS = 8, SMALL_E = 512;
+constexpr int SMALL_P = SMALL_THR * SMALL_CHUNKS;
+
+__global__ void __launch_bounds__(SMALL_THR) permute_small_kernel(
+    const int32_t* __restrict__ idx, int P, int k, int E, int T, int shared, int rb,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot_token, int32_t* __restrict__ pair_slot,
+    int32_t* __restrict__ group_range, int32_t* __restrict__ cum_blocks) {
+  __shared__ int32_t wcnt[16 * SMALL_E];
+  __shared__ int32_t run[2048], tmp[2048];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 16 * E; i += SMALL_THR) wcnt[i] = 0;
+  for (int i = tid; i < E; i += SMALL_THR) run[i] = 0;
+  __syncthreads();
+  int rank[SMALL_CHUNKS], key[SMALL_CHUNKS];
+#pragma unroll
+  for (int c = 0; c < SMALL_CHUNKS; ++c) {
+    rank[c] = 0;
+    key[c] = -1;
+    if (c * SMALL_THR < P) {  // uniform
+      const int q = c * SMALL_THR + tid;
+      int e = -1;
+      if (q < P) {
+        e = idx[q];
+        if (e < 0 || e >= E) e = -1;
+      }
+      uint64_t pending = __ballot(e >= 0);
+      int r_in_wave = 0;
+      while (pending) {
+        const int leader = __ffsll((long long)pending) - 1;
+        const int ek = __shfl(e, leader, 64);
+        const uint64_t same = __ballot(e == ek) & pending;
+        if (e == ek) r_in_wave = __popcll(same & lanemask_lt(lane));
+        if (lane == leader) wcnt[wave * E + ek] = __popcll(same);
+        pending &= ~same;
+      }
+      __syncthreads();
+      if (e >= 0) {
+        int r = run[e] + r_in_wave;
+        for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
+        rank[c] = r;
+      }
+      key[c] = e;
+      __syncthreads();
+      for (int ee = tid; ee < E; ee += SMALL_THR) {
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+          sum += wcnt[w * E + ee];
+          wcnt[w * E + ee] = 0;
+        }
+        run[ee] += sum;
+      }
+      __syncthreads();
+    }
+  }
+  const int total = block_exclusive_scan(run, tmp, E);  // run[e] = offsets[e]
+  for (int e = tid; e < E; e += SMALL_THR) offsets[e] = run[e];
+  if (tid == 0) offsets[E] = total;
+#pragma unroll
+  for (int c = 0; c < SMALL_CHUNKS; ++c) {
+    const int q = c * SMALL_THR + tid;
+    if (q < P) {
+      if (key[c] >= 0) {
+        const int slot = run[key[c]] + rank[c];
+        pair_slot[q] = slot;
+        slot_token[slot] = q / k;
+      } else {
+        pair_slot[q] = -1;
+      }
+    }
+  }
+  if (!group_range) return;
+  // plan: row range and row-block count of each group (routed experts, then the shared one)
+  const int G = E + (shared ? 1 : 0);
+  __syncthreads();
+  for (int g = tid; g < G; g += SMALL_THR) {
+    const int b0 = g < E ? run[g] : P;
+    const int b1 = g < E ? (g + 1 < E ? run[g + 1] : total) : P + T;
+    group_range[2 * g] = b0;
+    group_range[2 * g + 1] = b1;
+    tmp[g] = (b1 - b0 + rb - 1) / rb;
+  }
+  __syncthreads();
+  const int nblk = block_exclusive_scan(tmp, run, G);
+  for (int g = tid; g < G; g += SMALL_THR) cum_blocks[g] = tmp[g];
+  if (tid == 0) cum_blocks[G] = nblk;
+}
+
+bool permute_small_ok(int P, int E) { return P <= SMALL_P && E <= SMALL_E; }
+
+hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int shared, int rb, int32_t* offsets,
+                                int32_t* slot_token, int32_t* pair_slot, int32_t* group_range, int32_t* cum_blocks,
+                                hipStream_t st) {
+  const int P = T * k;
+  if (!permute_small_ok(P, E)) return hipErrorInvalidValue;
+  permute_small_kernel<<<1, SMALL_THR, 0, st>>>(idx, P, k, E, T, shared, rb, offsets, slot_token, pair_slot,
+                                                group_range, cum_blocks);
+  return hipGetLastError();
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
