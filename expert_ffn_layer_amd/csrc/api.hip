@@ -77,6 +77,11 @@ moe_status check_shape(const moe_shape* s) {
   auto ok = [&](moe_dtype w) { return f32 ? w == MOE_F32 : w != MOE_F32; };
   if (!ok(s->w_routed) || (s->I_shared && !ok(s->w_shared)))
     return fail(MOE_ERR_UNSUPPORTED, "weights must be F32 with F32 activations and BF16/FP8/MXFP4 with BF16 ones");
+  if (s->path == MOE_PATH_PREFILL &&
+      !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, std::min(s->H, s->I), s->I,
+                         s->H))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the prefill path needs BF16 activations and one BF16 or FP8 format for all experts");
   return MOE_OK;
 }
 
@@ -85,7 +90,7 @@ moe_status check_shape(const moe_shape* s) {
 int router_ksplit(const moe_shape& s) {
   if (s.T <= 0) return 1;
   const int rbk = (s.T + ROW_BLOCK - 1) / ROW_BLOCK;
-  const int ntw = pad64(s.E) / 16 / decode_nf(s.act, EPI_F32);
+  const int ntw = pad64(s.E) / 16 / decode_nf(s.act, EPI_F32, s.H, pad64(s.E));
   const int KT = s.H / kp_of(s.act);
   int ks = (512 + rbk * ntw - 1) / (rbk * ntw);
   ks = std::min(ks, std::max(1, KT / 8));
@@ -175,6 +180,16 @@ moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const flo
   return hip_status(e, "router top-k");
 }
 
+// The LDS-tiled MFMA kernel when the experts average at least 64 rows (or when asked for and
+// supported: bf16 activations, one weight format for routed and shared experts, bf16 or fp8).
+bool use_prefill(const moe_shape& s) {
+  const int cs = s.I_shared ? s.w_shared : s.w_routed;
+  if (!prefill_supported(s.act, s.w_routed, cs, std::min(s.H, s.I), s.I, s.H)) return false;
+  if (s.path == MOE_PATH_PREFILL) return true;
+  if (s.path == MOE_PATH_DECODE) return false;
+  return (long long)s.T * s.k >= 64LL * s.E;
+}
+
 // with_plan: also write the grouped-GEMM plan into the workspace (returns whether it did)
 moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int32_t* st_, int32_t* ps, void* ws,
                       const Ws& L, hipStream_t st, bool with_plan = false, bool* planned = nullptr) {
@@ -208,12 +223,14 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   if (ps != MOE_OK) return ps;
   int32_t* gr = at<int32_t>(ws, L.group_range);
   int32_t* cb = at<int32_t>(ws, L.cum_blocks);
+  const bool prefill = use_prefill(s);
+  const int rb = prefill ? prefill_row_tile() : ROW_BLOCK;
   hipError_t e = hipSuccess;
-  if (!plan_ready) e = launch_plan(off, s.E, P, s.T, S, ROW_BLOCK, gr, cb, st);
+  if (!plan_ready || prefill) e = launch_plan(off, s.E, P, s.T, S, rb, gr, cb, st);
   if (e != hipSuccess) return hip_status(e, "plan");
   moe_status rs;
   if (ev && (rs = record(ev[0], st)) != MOE_OK) return rs;
-  const int max_rb = std::min(s.E, P) + (P + ROW_BLOCK - 1) / ROW_BLOCK + S * ((s.T + ROW_BLOCK - 1) / ROW_BLOCK);
+  const int max_rb = std::min(s.E, P) + (P + rb - 1) / rb + S * ((s.T + rb - 1) / rb);
 
   GroupedArgs a{};
   a.group_range = gr;
@@ -245,7 +262,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.ldo = s.I;
   a.out_s = nullptr;
   const int cs = S ? s.w_shared : s.w_routed;
-  e = launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
+  e = prefill ? launch_grouped_prefill(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st)
+              : launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
   if (e != hipSuccess) return hip_status(e, "gate/up grouped GEMM");
   if (ev && (rs = record(ev[1], st)) != MOE_OK) return rs;
   // down: y = h Wd
@@ -271,7 +289,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.ldo = s.H;
   a.out_s = S ? y_shared : nullptr;
   a.ldo_s = s.H;
-  e = launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);
+  e = prefill ? launch_grouped_prefill(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st)
+              : launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);
   if (e != hipSuccess) return hip_status(e, "down grouped GEMM");
   return ev ? record(ev[2], st) : MOE_OK;
 }

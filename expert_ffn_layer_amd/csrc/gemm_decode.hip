@@ -343,12 +343,28 @@ static hipError_t launch_t(const GroupedArgs& a, int max_row_blocks, hipStream_t
   return hipGetLastError();
 }
 
+template <int CR, int CS, int ACT, int EPI>
+static hipError_t launch_nf(int nf, const GroupedArgs& a, int mrb, hipStream_t st) {
+  if constexpr (EPI == EPI_F32) {
+    return launch_t<CR, CS, ACT, EPI, 1>(a, mrb, st);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (nf == 1) return launch_t<CR, CS, ACT, EPI, 1>(a, mrb, st);
+    return launch_t<CR, CS, ACT, EPI, 2>(a, mrb, st);
+  } else {
+    if (nf == 2) return launch_t<CR, CS, ACT, EPI, 2>(a, mrb, st);
+    if (nf == 4) return launch_t<CR, CS, ACT, EPI, 4>(a, mrb, st);
+    return launch_t<CR, CS, ACT, EPI, 8>(a, mrb, st);
+  }
+}
+
 template <int ACT, int EPI>
-static hipError_t launch_codecs(int cr, int cs, const GroupedArgs& a, int mrb, hipStream_t st) {
+static hipError_t launch_codecs(int cr, int cs, int nf, const GroupedArgs& a, int mrb, hipStream_t st) {
 #define MOE_CASE(R, S) \
-  if (cr == R && cs == S) return launch_t<R, S, ACT, EPI, decode_nf(R, EPI)>(a, mrb, st);
+  if (cr == R && cs == S) return launch_nf<R, S, ACT, EPI>(nf, a, mrb, st);
   if constexpr (ACT == MOE_F32) {
     MOE_CASE(MOE_F32, MOE_F32)
+  } else if constexpr (EPI == EPI_F32) {
+    MOE_CASE(MOE_BF16, MOE_BF16)
   } else {
     MOE_CASE(MOE_BF16, MOE_BF16)
     MOE_CASE(MOE_BF16, MOE_FP8_E4M3_B128)
@@ -366,15 +382,16 @@ static hipError_t launch_codecs(int cr, int cs, const GroupedArgs& a, int mrb, h
 
 hipError_t launch_grouped_decode(int act, int epi, int cr, int cs, const GroupedArgs& a,
                                  int max_row_blocks, hipStream_t st) {
-  if (a.N % (16 * decode_nf(cr, epi)) != 0) return hipErrorInvalidValue;
+  const int nf = decode_nf(cr, epi, a.K, a.N);
+  if (a.N % (16 * nf) != 0) return hipErrorInvalidValue;
   if (act == MOE_F32) {
-    if (epi == EPI_SWIGLU) return launch_codecs<MOE_F32, EPI_SWIGLU>(cr, cs, a, max_row_blocks, st);
-    if (epi == EPI_PLAIN) return launch_codecs<MOE_F32, EPI_PLAIN>(cr, cs, a, max_row_blocks, st);
-    return launch_codecs<MOE_F32, EPI_F32>(cr, cs, a, max_row_blocks, st);
+    if (epi == EPI_SWIGLU) return launch_codecs<MOE_F32, EPI_SWIGLU>(cr, cs, nf, a, max_row_blocks, st);
+    if (epi == EPI_PLAIN) return launch_codecs<MOE_F32, EPI_PLAIN>(cr, cs, nf, a, max_row_blocks, st);
+    return launch_codecs<MOE_F32, EPI_F32>(cr, cs, nf, a, max_row_blocks, st);
   }
-  if (epi == EPI_SWIGLU) return launch_codecs<MOE_BF16, EPI_SWIGLU>(cr, cs, a, max_row_blocks, st);
-  if (epi == EPI_PLAIN) return launch_codecs<MOE_BF16, EPI_PLAIN>(cr, cs, a, max_row_blocks, st);
-  return launch_codecs<MOE_BF16, EPI_F32>(cr, cs, a, max_row_blocks, st);
+  if (epi == EPI_SWIGLU) return launch_codecs<MOE_BF16, EPI_SWIGLU>(cr, cs, nf, a, max_row_blocks, st);
+  if (epi == EPI_PLAIN) return launch_codecs<MOE_BF16, EPI_PLAIN>(cr, cs, nf, a, max_row_blocks, st);
+  return launch_codecs<MOE_BF16, EPI_F32>(cr, cs, nf, a, max_row_blocks, st);
 }
 
 }  // namespace moe

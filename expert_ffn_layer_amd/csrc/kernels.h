@@ -43,16 +43,25 @@ struct GroupedArgs {
   int ksplit;  // > 1: fp32 output only; workgroup y sums K part y into out + y * M * ldo
 };
 
-// Output features (in units of 16) per decode work item: a small item (16-32 features) keeps
-// the scheduling granularity far below one CU's share of the weight stream.
-__host__ __device__ constexpr int decode_nf(int codec, int epi) {
-  return epi == EPI_SWIGLU ? (codec == 3 /* MXFP4 */ ? 2 : 1) : (epi == EPI_F32 ? 1 : 2);
+// Output features (in units of 16) per decode work item, chosen from the instantiated set so an
+// item streams at least about 128 KiB of weights (or the most the set allows): small enough that
+// the scheduling granularity stays far below one CU's share of the stream, large enough that the
+// per-item setup and reduction stay negligible.
+inline int decode_nf(int codec, int epi, int K, int N) {
+  if (epi == EPI_F32) return 1;
+  const double bpw = codec == 0 ? 4.0 : codec == 1 ? 2.0 : codec == 2 ? 1.0 : 0.53125;
+  const int nmat = epi == EPI_SWIGLU ? 2 : 1;
+  const int lo = epi == EPI_SWIGLU ? 1 : 2, hi = epi == EPI_SWIGLU ? 2 : 8;
+  int nf = lo;
+  while (nf < hi && 16.0 * nf * K * bpw * nmat < 128.0 * 1024 && N % (32 * nf) == 0) nf *= 2;
+  return nf;
 }
-
 hipError_t launch_grouped_decode(int act, int epi, int cr, int cs, const GroupedArgs& a,
                                  int max_row_blocks, hipStream_t st);
-hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const GroupedArgs& a,
+hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const GroupedArgs& a, int max_tiles,
                                   hipStream_t st);
+int prefill_row_tile();
+bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down);
 hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
                        int32_t* group_range, int32_t* cum_blocks, hipStream_t st);
 hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,

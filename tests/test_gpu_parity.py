@@ -107,10 +107,17 @@ SMALL = [
 ]
 
 
+def _prefill_ok(spec):
+    return (spec.act == "bf16" and spec.w_routed in ("bf16", "fp8")
+            and (not spec.shared or spec.w_shared == spec.w_routed) and spec.I % 128 == 0 and spec.H % 256 == 0)
+
+
 @pytest.mark.parametrize("name,spec", SMALL, ids=[s[0] for s in SMALL])
-@pytest.mark.parametrize("path", ["auto"])
+@pytest.mark.parametrize("path", ["auto", "decode", "prefill"])
 def test_layer_small(name, spec, path):
-    say("layer", name, spec)
+    if path == "prefill" and not _prefill_ok(spec):
+        pytest.skip("the prefill kernel takes bf16 activations and one bf16/fp8 weight format")
+    say("layer", name, path, spec)
     lay, pl = build(spec, DEV, path)
     y, idx, w = run(spec, lay, pl)
     ref = oracle_full(spec, lay)
