@@ -78,8 +78,8 @@ moe_status check_shape(const moe_shape* s) {
   if (!ok(s->w_routed) || (s->I_shared && !ok(s->w_shared)))
     return fail(MOE_ERR_UNSUPPORTED, "weights must be F32 with F32 activations and BF16/FP8/MXFP4 with BF16 ones");
   if (s->path == MOE_PATH_PREFILL &&
-      !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, std::min(s->H, s->I), s->I,
-                         s->H))
+      (!prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
+       !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->I, s->I, s->H)))
     return fail(MOE_ERR_UNSUPPORTED,
                 "the prefill path needs BF16 activations and one BF16 or FP8 format for all experts");
   return MOE_OK;
@@ -184,7 +184,8 @@ moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const flo
 // supported: bf16 activations, one weight format for routed and shared experts, bf16 or fp8).
 bool use_prefill(const moe_shape& s) {
   const int cs = s.I_shared ? s.w_shared : s.w_routed;
-  if (!prefill_supported(s.act, s.w_routed, cs, std::min(s.H, s.I), s.I, s.H)) return false;
+  if (!prefill_supported(s.act, s.w_routed, cs, s.H, s.I, s.H) || !prefill_supported(s.act, s.w_routed, cs, s.I, s.I, s.H))
+    return false;
   if (s.path == MOE_PATH_PREFILL) return true;
   if (s.path == MOE_PATH_DECODE) return false;
   return (long long)s.T * s.k >= 64LL * s.E;

@@ -2,13 +2,14 @@
 //
 // Work item = (group, tile of BM = 128 rows, tile of output features). The four waves of a
 // workgroup split the features (64 each: 32 gate + 32 up columns for the SwiGLU GEMM, 64 for the
-// plain one) and share the 128-row activation tile, which is staged in LDS (double-buffered
-// over reduction steps of 64, rows padded to 144 bytes so the 16x16 fragment reads are free of
-// bank conflicts). The weights stream from global memory straight into each wave's registers in
-// the packet layout (one 128-bit load per lane per packet), so every weight byte is converted
-// to bf16 exactly once per workgroup, and feed v_mfma_f32_16x16x32_bf16 as the A operand; the
-// activations are the B operand. fp8 packets are converted in registers (e4m3 -> fp32 exact,
-// times the 128 x 128 block scale, -> bf16).
+// plain one) and share the 128-row activation tile. Both operands reach LDS by direct
+// global -> LDS DMA (global_load_lds_dwordx4) through a 3- or 4-stage ring of 64-wide reduction
+// steps, so the loads of the next stages are in flight for several steps of MFMA work and cost
+// no registers. Each 1 KiB DMA lands in MFMA fragment order (a weight packet as stored; an
+// activation fragment gathered from 16 rows), so every LDS read is a conflict-free 16-byte read
+// at lane * 16. Weights are the A operand of v_mfma_f32_16x16x32_bf16, activations the B
+// operand; fp8 packets are converted once per workgroup in registers (e4m3 -> fp32 exact, times
+// the 128 x 128 block scale, -> bf16).
 //
 // Items are ordered so that a run of consecutive items covers up to 8 feature tiles x all row
 // tiles of one group, and the workgroup -> item map gives each XCD a contiguous run of items:
@@ -19,10 +20,9 @@
 
 namespace moe {
 
-constexpr int PBM = 128;           // rows per item
-constexpr int PBK = 64;            // reduction elements per step
-constexpr int PWN = 64;            // output features per wave (4 tiles of 16)
-constexpr int LDS_ROW = PBK + 8;   // bf16 elements per LDS row (144 bytes)
+constexpr int PBM = 128;  // rows per item
+constexpr int PBK = 64;   // reduction elements per pipeline stage
+constexpr int PWN = 64;   // output features per wave (4 tiles of 16)
 constexpr int NXCD = 8;
 
 template <int C>
@@ -30,9 +30,10 @@ struct PCodec;
 
 template <>
 struct PCodec<MOE_BF16> {
-  static constexpr int PK = 2;  // packets per feature tile per step
-  // byte offset in an LDS row of the B fragment of half h for lane group g
-  __device__ static int boff(int g, int h) { return 16 * g + 64 * h; }
+  static constexpr int PK = 2;      // packets per feature tile per stage
+  static constexpr int STAGES = 3;  // 48 KiB per stage
+  // element offset (within a stage's 64) of the B fragment of half h for lane group g
+  __device__ static int boff(int g, int h) { return 8 * g + 32 * h; }
   __device__ static void frags(const u32x4 (&w)[2], float, bf16x8 (&a)[2]) {
     a[0] = __builtin_bit_cast(bf16x8, w[0]);
     a[1] = __builtin_bit_cast(bf16x8, w[1]);
@@ -57,7 +58,8 @@ __device__ __forceinline__ bf16x8 p_fp8x8(uint32_t w0, uint32_t w1, float s) {
 template <>
 struct PCodec<MOE_FP8_E4M3_B128> {
   static constexpr int PK = 1;
-  __device__ static int boff(int g, int h) { return 32 * g + 16 * h; }
+  static constexpr int STAGES = 4;  // 32 KiB per stage
+  __device__ static int boff(int g, int h) { return 16 * g + 8 * h; }
   __device__ static void frags(const u32x4 (&w)[1], float s, bf16x8 (&a)[2]) {
     a[0] = p_fp8x8(w[0][0], w[0][1], s);
     a[1] = p_fp8x8(w[0][2], w[0][3], s);
@@ -81,6 +83,11 @@ __device__ __forceinline__ void item_tiles(int i, int mt, int ntn, int& m, int& 
   n = nb * 8 + rem % width;
 }
 
+// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt not waited on)
+#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int C, int EPI>
 __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) {
   using Cd = PCodec<C>;
@@ -89,16 +96,23 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
   constexpr int NT = NMAT * WF;  // 16-feature tiles per wave (4)
   constexpr int PK = Cd::PK;
   constexpr int KP = PBK / PK;   // reduction elements per packet
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][PBM * LDS_ROW];
+  constexpr int D = Cd::STAGES;
+  constexpr int ACT_B = 16 * 1024;            // activation fragments per stage (16 x 1 KiB)
+  constexpr int WTS_B = 4 * NT * PK * 1024;   // weight packets per stage (all waves)
+  constexpr int STAGE_B = ACT_B + WTS_B;
+  constexpr int L = 4 + NT * PK;              // DMA loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[D * STAGE_B];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ntn = a.NTW;  // feature tiles of the workgroup width
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (SGPR) so the per-wave scale reads become scalar loads, which do not count
+  // against vmcnt and so do not drain the DMA pipeline
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntn = a.NTW;
   // XCD-aware workgroup -> item map: each XCD takes a contiguous run of the item list
   const int per_xcd = gridDim.x / NXCD;
   const int item = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
   const int total = a.cum_blocks[a.G] * ntn;
   if (item >= total) return;
-  // group of the item: largest g with cum_blocks[g] * ntn <= item
   int lo = 0, hi = a.G - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -116,32 +130,59 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
   const uint8_t* w1 = is_shared ? a.wb_s : (a.wb_r ? a.wb_r + (size_t)g * a.mat_bytes : nullptr);
   const float* s0 = (const float*)(is_shared ? a.sa_s : (a.sa_r ? a.sa_r + (size_t)g * a.scale_bytes : nullptr));
   const float* s1 = (const float*)(is_shared ? a.sb_s : (a.sb_r ? a.sb_r + (size_t)g * a.scale_bytes : nullptr));
-  const int KT = a.K / KP;  // packets along K
+  const int KT = a.K / KP;
   const int nsteps = a.K / PBK;
+  const int j16 = lane & 15, g4 = lane >> 4;
 
-  // this wave's 16-feature tiles: matrix m, tile index (in units of 16 features)
+  // this wave's 16-feature tiles (matrix t / WF) and their packet streams
   int ftile[NT];
   const uint8_t* fbase[NT];
-  const float* fscale[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int m = t / WF, f = t % WF;
-    ftile[t] = (ntile * 4 + wave) * WF + f;
-    fbase[t] = (m == 0 ? w0 : w1) + (size_t)ftile[t] * KT * PACKET_BYTES + (size_t)lane * 16;
-    fscale[t] = m == 0 ? s0 : s1;
+    ftile[t] = (ntile * 4 + wave) * WF + t % WF;
+    fbase[t] = (t / WF == 0 ? w0 : w1) + (size_t)ftile[t] * KT * PACKET_BYTES + (size_t)lane * 16;
+  }
+  // fp8 block scales of this wave: its features of each matrix lie in one 128-wide block, so
+  // the scale depends only on the 128-deep reduction block; lane i holds block i (K <= 8192),
+  // and the loop picks the current one with a lane read (no memory access in the pipeline)
+  const int nblk = ftile[0] >> 3;
+  float scv[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    const float* sp = m == 0 ? s0 : s1;
+    scv[m] = (C == MOE_FP8_E4M3_B128 && lane < (a.K >> 7)) ? sp[lane * (a.N >> 7) + nblk] : 1.0f;
   }
 
-  // activation rows this thread stages: rows r = tid/8 + 32 i, 16-byte chunk c = tid % 8
-  const int c8 = tid & 7;
-  const uint8_t* arow[4];
+  // activation fragments this wave loads per stage: f = 4 * wave + i -> row tile f / 2, half f % 2;
+  // lane l fetches row tile*16 + l%16 at the fragment's reduction offset
+  const uint8_t* arow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = (tid >> 3) + 32 * i;
+  for (int i = 0; i < 2; ++i) {
+    const int rr = (2 * wave + i) * 16 + j16;
     const int r = row0 + (rr < nr ? rr : 0);
     int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
     if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
-    arow[i] = (const uint8_t*)a.act + ((size_t)src * a.lda + c8 * 8) * 2;
+    arow[i] = (const uint8_t*)a.act + (size_t)src * a.lda * 2;
   }
+
+  // issue the DMA of stage `step` (clamped into range) into its LDS slot
+  auto dma = [&](int step) {
+    const int st = min(step, nsteps - 1);
+    uint8_t* base = lds + (step % D) * STAGE_B;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = 4 * wave + i;
+      const uint8_t* src = arow[i >> 1] + (size_t)(st * PBK + Cd::boff(g4, i & 1)) * 2;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(base + f * 1024), 16, 0, 0);
+    }
+    uint8_t* wb = base + ACT_B + wave * (NT * PK * 1024);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int p = 0; p < PK; ++p)
+        __builtin_amdgcn_global_load_lds((const void*)(fbase[t] + (size_t)(st * PK + p) * PACKET_BYTES),
+                                         (lds_void*)(wb + (t * PK + p) * 1024), 16, 0, 0);
+  };
 
   f32x4 acc[NT][8];
 #pragma unroll
@@ -149,76 +190,43 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 xa[4];  // staged activation chunks of the next step
-  // weight packets and scales of two consecutive steps (slot 0: even steps, slot 1: odd steps;
-  // static indices keep them in registers and the wait counts exact)
-  u32x4 wv0[NT][PK], wv1[NT][PK];
-  float sv0[NT], sv1[NT];
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s) dma(s);
 
-  auto load_x = [&](int step) {
+  for (int step = 0; step < nsteps; ++step) {
+    // this wave's loads of `step` have landed; after the barrier, every wave's have, and no
+    // wave still reads the slot the next DMA overwrites (that of step - 1)
+    MOE_WAIT_VMCNT((D - 2) * L);
+    __builtin_amdgcn_s_barrier();
+    dma(step + D - 1);
+    const uint8_t* base = lds + (step % D) * STAGE_B;
+    const uint8_t* wb = base + ACT_B + wave * (NT * PK * 1024) + lane * 16;
+    float sc[NMAT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = *(const u32x4*)(arow[i] + (size_t)step * PBK * 2);
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = (tid >> 3) + 32 * i;
-      *(u32x4*)((uint8_t*)lds[buf] + rr * (LDS_ROW * 2) + c8 * 16) = xa[i];
-    }
-  };
-  auto load_w = [&](int step, u32x4 (&wv)[NT][PK], float (&sv)[NT]) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int p = 0; p < PK; ++p)
-        wv[t][p] = ld_nt((const u32x4*)(fbase[t] + (size_t)(step * PK + p) * PACKET_BYTES));
-      if (C == MOE_FP8_E4M3_B128) {
-        const int kb = (step * PBK + (lane >> 4) * 16) >> 7;
-        sv[t] = fscale[t][kb * (a.N >> 7) + (ftile[t] >> 3)];
-      } else {
-        sv[t] = 1.0f;
-      }
-    }
-  };
-  const int j16 = lane & 15, g4 = lane >> 4;
-  // one reduction step on LDS buffer `buf` with weights (wv, sv), prefetching the next step
-  auto step_body = [&](int step, int buf, u32x4 (&wv)[NT][PK], float (&sv)[NT], u32x4 (&wn)[NT][PK],
-                       float (&sn)[NT]) {
-    // unconditional prefetch (the last step re-reads itself) keeps the wait counts exact
-    const int nxt = min(step + 1, nsteps - 1);
-    load_x(nxt);
-    load_w(nxt, wn, sn);
-    // keep the prefetch at the top of the step: the scheduler would otherwise sink it behind
-    // the MFMAs, and the next step would stall on it
-    __builtin_amdgcn_sched_barrier(0);
+    for (int m = 0; m < NMAT; ++m)
+      sc[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), (step * PBK) >> 7));
     bf16x8 af[NT][2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) Cd::frags(wv[t], sv[t], af[t]);
-    const uint8_t* lb = (const uint8_t*)lds[buf];
+    for (int t = 0; t < NT; ++t) {
+      u32x4 pk[PK];
+#pragma unroll
+      for (int p = 0; p < PK; ++p) pk[p] = *(const u32x4*)(wb + (t * PK + p) * 1024);
+      Cd::frags(pk, sc[t / WF], af[t]);
+    }
+    const uint8_t* ab = base + lane * 16;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint8_t* rowp = lb + (j * 16 + j16) * (LDS_ROW * 2);
-      const bf16x8 b0 = *(const bf16x8*)(rowp + Cd::boff(g4, 0));
-      const bf16x8 b1 = *(const bf16x8*)(rowp + Cd::boff(g4, 1));
+      const bf16x8 b0 = *(const bf16x8*)(ab + (2 * j) * 1024);
+      const bf16x8 b1 = *(const bf16x8*)(ab + (2 * j + 1) * 1024);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+      for (int t = 0; t < NT; ++t)
         acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][0], b0, acc[t][j], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
         acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][1], b1, acc[t][j], 0, 0, 0);
-      }
     }
-    store_x(buf ^ 1);
-    __syncthreads();
-  };
-
-  // prologue
-  load_x(0);
-  load_w(0, wv0, sv0);
-  store_x(0);
-  __syncthreads();
-  for (int step = 0; step < nsteps; step += 2) {
-    step_body(step, 0, wv0, sv0, wv1, sv1);
-    if (step + 1 < nsteps) step_body(step + 1, 1, wv1, sv1, wv0, sv0);
   }
+  MOE_WAIT_VMCNT(0);  // the clamped tail DMAs must land before the workgroup's LDS is released
 
   // epilogue: lane holds features 4*(lane/16) + i of each 16-feature tile, row j*16 + lane%16
   uint8_t* out;
@@ -265,7 +273,8 @@ int prefill_row_tile() { return PBM; }
 
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down) {
   auto ok = [](int c) { return c == MOE_BF16 || c == MOE_FP8_E4M3_B128; };
-  return act == MOE_BF16 && ok(cr) && cr == cs && K % PBK == 0 && N_gateup % PEpi<EPI_SWIGLU>::WGF == 0 &&
+  return act == MOE_BF16 && ok(cr) && cr == cs && K % PBK == 0 && K <= 64 * 128 &&
+         N_gateup % PEpi<EPI_SWIGLU>::WGF == 0 &&
          N_down % PEpi<EPI_PLAIN>::WGF == 0;
 }
 
