@@ -22,6 +22,32 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads for the plain copy
+# kernel of known size that --calib-copy appends. Keyed by workload; an entry holds only while
+# the kernel sources it was measured on are unchanged (sha256 of those files).
+TRAFFIC = {}
+CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
+KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
+                  "prefill": ("gemm_prefill.hip", "common.h", "kernels.h")}
+
+
+def kernel_sha(path: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[path]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: str, path: str):
+    t = TRAFFIC.get(config)
+    if t is None or t["sha"] != kernel_sha(path):
+        return None
+    return t["bytes"]
+
+
 # bounded CPU-oracle samples (tokens): about 10-30 s of oracle work per config
 CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4}
 
@@ -39,6 +65,8 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
+                    help="end with one plain copy kernel of this size (byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard "
@@ -91,18 +119,32 @@ def main():
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / args.steps
 
-    # per-kernel durations, live, with events recorded between the kernels of each forward
-    log("bench: per-stage timing")
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(N.TIMED_EVENTS)]
-    for e in evs:
-        e.record()  # creates the underlying HIP events
+    # Per-kernel durations, live: the same K steps again through the timed entry point, which
+    # records HIP events on the launch stream between the kernels of each forward (one event
+    # set per step, no synchronisation inside the region).
+    log("bench: per-stage timing over %d steps" % args.steps)
     names = ["route", "permute", "plan", "gate_up", "down", "combine"]
-    acc = np.zeros(len(names))
-    for _ in range(args.steps):
+    evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(N.TIMED_EVENTS)] for _ in range(args.steps)]
+    for evs in evsets:
+        for e in evs:
+            e.record()  # creates the underlying HIP events before the region
+    torch.cuda.synchronize()
+    for evs in evsets:
         N.moe_layer_forward_timed(pl.shape, x, pl.Wr, bias, pl.routed, pl.shared, y, evs, idx, w, pl.ws)
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    acc = np.zeros(len(names))
+    for evs in evsets:
         acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
     stage_ms = acc / args.steps
+    timed_ms = sum(evs[0].elapsed_time(evs[-1]) for evs in evsets) / args.steps
+
+    if args.calib_copy:
+        # one plain copy of known size, the reference that scales the byte counters of a --pmc run
+        nb = args.calib_copy << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        G.copy(src, torch.empty_like(src))
+        torch.cuda.synchronize()
+        log("bench: calibration copy of %d bytes" % nb)
 
     # roofline of the dominant kernel (the gate/up grouped GEMM)
     H, I, T, k = spec.H, spec.I, spec.T, spec.k
@@ -114,16 +156,17 @@ def main():
     gu_flops = 4 * H * I * R
     gu_ms = stage_ms[names.index("gate_up")]
     prefill = (T * k) / spec.E >= 64
+    traffic_b = measured_traffic(args.config, "prefill" if prefill else "decode")
     if prefill:
         peak = MFMA_PEAK_TFLOPS["bf16" if spec.act == "bf16" else "f32"]
         ach = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None, "kernel": "gate/up grouped GEMM",
+                "frac": round(ach / peak, 4), "traffic": traffic_b, "kernel": "gate/up grouped GEMM",
                 "per_launch": {"flops": gu_flops, "ms": round(gu_ms, 4)}}
     else:
         ach = gu_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "gate/up grouped GEMM",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic_b, "kernel": "gate/up grouped GEMM",
                 "per_launch": {"bytes": gu_bytes, "ms": round(gu_ms, 4)}}
 
     out = {
@@ -149,6 +192,7 @@ def main():
         "tflops": round(traffic["flops"] / (ms * 1e-3) / 1e12, 2),
         "algorithmic": {"bytes": traffic["bytes"], "flops": traffic["flops"]},
         "stages_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
+        "timed_entry_ms_per_step": round(timed_ms, 4),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "cpu_baseline": None,

@@ -1,28 +1,38 @@
 // Prefill-regime grouped GEMM: many rows per expert, bound by the matrix cores.
 //
-// Work item = (group, tile of BM = 128 rows, tile of output features). The four waves of a
-// workgroup split the features (64 each: 32 gate + 32 up columns for the SwiGLU GEMM, 64 for the
-// plain one) and share the 128-row activation tile. Both operands reach LDS by direct
-// global -> LDS DMA (global_load_lds_dwordx4) through a 3- or 4-stage ring of 64-wide reduction
-// steps, so the loads of the next stages are in flight for several steps of MFMA work and cost
-// no registers. Each 1 KiB DMA lands in MFMA fragment order (a weight packet as stored; an
-// activation fragment gathered from 16 rows), so every LDS read is a conflict-free 16-byte read
-// at lane * 16. Weights are the A operand of v_mfma_f32_16x16x32_bf16, activations the B
-// operand; fp8 packets are converted once per workgroup in registers (e4m3 -> fp32 exact, times
-// the 128 x 128 block scale, -> bf16).
+// A workgroup of 8 waves (two per SIMD, so one wave's LDS reads, conversions and barrier wait
+// overlap the other's MFMAs) computes one work item:
+//   full item: 256 rows x 256 matrix columns; waves (wr, wc) = (wave / 4, wave % 4) take rows
+//              wr * 128 .. + 128 and columns wc * 64 .. + 64;
+//   half item: the last <= 128 rows of a group x 512 matrix columns; wave w takes columns
+//              w * 64 .. + 64 of all rows.
+// Every wave therefore owns a 128-row x 64-column accumulator tile (for the SwiGLU GEMM, 32 gate
+// and the matching 32 up columns, so SiLU(gate) * up is formed in registers). A group of n rows
+// is n / 256 full items plus one full or half item for the rest, which wastes no more rows than
+// 128-row tiles would.
 //
-// Items are ordered so that a run of consecutive items covers up to 8 feature tiles x all row
-// tiles of one group, and the workgroup -> item map gives each XCD a contiguous run of items:
-// workgroups resident at the same time on one XCD then share weight and activation slices in
-// that XCD's L2 (Chapter 6 'Supernodes' section 6.3.2: one weight read serves many rows).
+// Both operands reach LDS by direct global -> LDS DMA (global_load_lds_dwordx4) through a
+// 3-stage ring of reduction steps, so the loads of the next stages are in flight behind two
+// steps of MFMA work and hold no registers. Each 1 KiB DMA lands in MFMA fragment order (a
+// weight packet as stored; an activation fragment gathered from 16 rows), so every LDS read is a
+// conflict-free 16-byte read at lane * 16. Weights are the A operand of
+// v_mfma_f32_16x16x32_bf16, activations the B operand; fp8 packets are converted by the wave
+// that uses them (e4m3 -> fp32 exact, times the 128 x 128 block scale, -> bf16).
+//
+// Items are ordered so that a run of consecutive items covers up to 8 column tiles x all full
+// row tiles of one group, and the workgroup -> item map gives each XCD a contiguous run of the
+// items that exist: workgroups resident at the same time on one XCD then share weight and
+// activation slices in that XCD's L2 (Chapter 6 'Supernodes' section 6.3.2: one weight read
+// serves many rows).
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int PBM = 128;  // rows per item
-constexpr int PBK = 64;   // reduction elements per pipeline stage
-constexpr int PWN = 64;   // output features per wave (4 tiles of 16)
+constexpr int PTHREADS = 512;
+constexpr int PBM = 256;   // rows per full item
+constexpr int PRB = 128;   // rows per half item, and the plan's row block
+constexpr int PWC = 64;    // matrix columns per wave
 constexpr int NXCD = 8;
 
 template <int C>
@@ -30,13 +40,14 @@ struct PCodec;
 
 template <>
 struct PCodec<MOE_BF16> {
-  static constexpr int PK = 2;      // packets per feature tile per stage
-  static constexpr int STAGES = 3;  // 48 KiB per stage
-  // element offset (within a stage's 64) of the B fragment of half h for lane group g
-  __device__ static int boff(int g, int h) { return 8 * g + 32 * h; }
-  __device__ static void frags(const u32x4 (&w)[2], float, bf16x8 (&a)[2]) {
+  static constexpr int KP = 32;      // reduction elements per packet
+  static constexpr int PBK = 32;     // reduction elements per pipeline step
+  static constexpr int H = 1;        // 32-deep MFMA steps per pipeline step
+  static constexpr int PK = 1;       // packets per 16-column tile per pipeline step
+  // element offset (within a step) of the B fragment of half h for lane group g
+  __device__ static int boff(int g, int) { return 8 * g; }
+  __device__ static void frags(const u32x4 (&w)[PK], float, bf16x8 (&a)[H]) {
     a[0] = __builtin_bit_cast(bf16x8, w[0]);
-    a[1] = __builtin_bit_cast(bf16x8, w[1]);
   }
 };
 
@@ -57,10 +68,14 @@ __device__ __forceinline__ bf16x8 p_fp8x8(uint32_t w0, uint32_t w1, float s) {
 
 template <>
 struct PCodec<MOE_FP8_E4M3_B128> {
+  static constexpr int KP = 64;
+  static constexpr int PBK = 64;
+  static constexpr int H = 2;
   static constexpr int PK = 1;
-  static constexpr int STAGES = 4;  // 32 KiB per stage
+  // lane group g of a packet holds reduction elements 16g .. 16g + 15; MFMA half h takes the
+  // h-th run of 8 of them, so the activation fragment must carry the same elements
   __device__ static int boff(int g, int h) { return 16 * g + 8 * h; }
-  __device__ static void frags(const u32x4 (&w)[1], float s, bf16x8 (&a)[2]) {
+  __device__ static void frags(const u32x4 (&w)[PK], float s, bf16x8 (&a)[H]) {
     a[0] = p_fp8x8(w[0][0], w[0][1], s);
     a[1] = p_fp8x8(w[0][2], w[0][3], s);
   }
@@ -69,12 +84,29 @@ struct PCodec<MOE_FP8_E4M3_B128> {
 template <int EPI>
 struct PEpi {
   static constexpr int NMAT = EPI == EPI_SWIGLU ? 2 : 1;
-  static constexpr int WF = PWN / 16 / NMAT;  // feature tiles per matrix per wave
-  static constexpr int WGF = 4 * WF * 16;     // output features per workgroup
+  static constexpr int WF = PWC / 16 / NMAT;   // 16-feature tiles per matrix per wave
+  static constexpr int FULL_F = 4 * WF * 16;   // output features of a full item
 };
 
-// (group-local item) -> (row tile, feature tile): runs of up to 8 feature tiles over all row
-// tiles of the group.
+template <int C>
+struct PLayout {
+  using Cd = PCodec<C>;
+  static constexpr int H = Cd::H, PK = Cd::PK;
+  // per stage: activation fragments (16 row tiles x H for a full item, 8 x H for a half item)
+  // followed by weight packets (16 column tiles x PK, or 32 x PK), in KiB
+  static constexpr int FULL_ACT = 16 * H, HALF_ACT = 8 * H;
+  static constexpr int FULL_W = 16 * PK, HALF_W = 32 * PK;
+  static constexpr int STAGE_KIB = (FULL_ACT + FULL_W) > (HALF_ACT + HALF_W) ? (FULL_ACT + FULL_W)
+                                                                             : (HALF_ACT + HALF_W);
+  static constexpr int STAGES = 3;
+  // DMA instructions per wave per stage; the shorter kind is padded with repeats of its last
+  // load so both kinds issue the same count (the wait counts are compile-time)
+  static constexpr int LF = 2 * H + 2 * PK, LH = H + 4 * PK;
+  static constexpr int L = LF > LH ? LF : LH;
+};
+
+// (group-local full item) -> (row tile, column tile): runs of up to 8 column tiles over all
+// full row tiles of the group.
 __device__ __forceinline__ void item_tiles(int i, int mt, int ntn, int& m, int& n) {
   const int nb = i / (mt * 8);
   const int rem = i - nb * mt * 8;
@@ -89,42 +121,50 @@ __device__ __forceinline__ void item_tiles(int i, int mt, int ntn, int& m, int& 
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int C, int EPI>
-__global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) {
+__global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArgs a) {
   using Cd = PCodec<C>;
+  using Ly = PLayout<C>;
   constexpr int NMAT = PEpi<EPI>::NMAT;
   constexpr int WF = PEpi<EPI>::WF;
-  constexpr int NT = NMAT * WF;  // 16-feature tiles per wave (4)
-  constexpr int PK = Cd::PK;
-  constexpr int KP = PBK / PK;   // reduction elements per packet
-  constexpr int D = Cd::STAGES;
-  constexpr int ACT_B = 16 * 1024;            // activation fragments per stage (16 x 1 KiB)
-  constexpr int WTS_B = 4 * NT * PK * 1024;   // weight packets per stage (all waves)
-  constexpr int STAGE_B = ACT_B + WTS_B;
-  constexpr int L = 4 + NT * PK;              // DMA loads per wave per stage
+  constexpr int NT = NMAT * WF;  // 16-column tiles per wave (4)
+  constexpr int H = Cd::H, PK = Cd::PK, PBK = Cd::PBK;
+  constexpr int KP = Cd::KP;
+  constexpr int D = Ly::STAGES;
+  constexpr int STAGE_B = Ly::STAGE_KIB * 1024;
+  constexpr int L = Ly::L;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[D * STAGE_B];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave-uniform (SGPR) so the per-wave scale reads become scalar loads, which do not count
-  // against vmcnt and so do not drain the DMA pipeline
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ntn = a.NTW;
-  // XCD-aware workgroup -> item map: each XCD takes a contiguous run of the item list
-  const int per_xcd = gridDim.x / NXCD;
+  const int ntn = a.NTW;  // full-item column tiles (even)
+  const int units = a.cum_blocks[a.G];  // 128-row blocks over all groups
+  const int total = units * (ntn >> 1);
+  // XCD-aware workgroup -> item map over the items that exist: XCD x (= blockIdx % 8) takes
+  // items [x * per_xcd, (x + 1) * per_xcd)
+  const int per_xcd = (total + NXCD - 1) / NXCD;
+  if ((int)(blockIdx.x / NXCD) >= per_xcd) return;
   const int item = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
-  const int total = a.cum_blocks[a.G] * ntn;
   if (item >= total) return;
   int lo = 0, hi = a.G - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (a.cum_blocks[mid] * ntn <= item) lo = mid; else hi = mid - 1;
+    if (a.cum_blocks[mid] * (ntn >> 1) <= item) lo = mid; else hi = mid - 1;
   }
   const int g = lo;
-  const int mt = a.cum_blocks[g + 1] - a.cum_blocks[g];
+  const int mt = a.cum_blocks[g + 1] - a.cum_blocks[g];  // 128-row blocks of the group
+  const int mtf = mt >> 1;                               // full row tiles
+  const int li = item - a.cum_blocks[g] * (ntn >> 1);
+  const bool half = li >= mtf * ntn;
   int mtile, ntile;
-  item_tiles(item - a.cum_blocks[g] * ntn, mt, ntn, mtile, ntile);
+  if (half) {
+    mtile = mtf;
+    ntile = li - mtf * ntn;
+  } else {
+    item_tiles(li, mtf, ntn, mtile, ntile);
+  }
   const int rbeg = a.group_range[2 * g], rend = a.group_range[2 * g + 1];
   const int row0 = rbeg + mtile * PBM;
-  const int nr = min(PBM, rend - row0);
+  const int nr = min(half ? PRB : PBM, rend - row0);
   const bool is_shared = g == a.shared_group;
   const uint8_t* w0 = is_shared ? a.wa_s : a.wa_r + (size_t)g * a.mat_bytes;
   const uint8_t* w1 = is_shared ? a.wb_s : (a.wb_r ? a.wb_r + (size_t)g * a.mat_bytes : nullptr);
@@ -134,17 +174,18 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
   const int nsteps = a.K / PBK;
   const int j16 = lane & 15, g4 = lane >> 4;
 
-  // this wave's 16-feature tiles (matrix t / WF) and their packet streams
+  // this wave's place: row half and column slot within the item
+  const int wrow = half ? 0 : wave >> 2;
+  const int wcol = half ? wave : wave & 3;
+  // global wave-column index (units of WF 16-feature tiles per matrix)
+  const int gw = half ? ntile * 8 + wave : ntile * 4 + wcol;
   int ftile[NT];
-  const uint8_t* fbase[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    ftile[t] = (ntile * 4 + wave) * WF + t % WF;
-    fbase[t] = (t / WF == 0 ? w0 : w1) + (size_t)ftile[t] * KT * PACKET_BYTES + (size_t)lane * 16;
-  }
-  // fp8 block scales of this wave: its features of each matrix lie in one 128-wide block, so
-  // the scale depends only on the 128-deep reduction block; lane i holds block i (K <= 8192),
-  // and the loop picks the current one with a lane read (no memory access in the pipeline)
+  for (int t = 0; t < NT; ++t) ftile[t] = gw * WF + t % WF;
+
+  // fp8 block scales: this wave's features of each matrix lie in one 128-wide block, so the
+  // scale depends only on the 128-deep reduction block; lane i holds block i (K <= 8192), and
+  // the loop picks the current one with a lane read (no memory access in the pipeline)
   const int nblk = ftile[0] >> 3;
   float scv[NMAT];
 #pragma unroll
@@ -153,35 +194,68 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
     scv[m] = (C == MOE_FP8_E4M3_B128 && lane < (a.K >> 7)) ? sp[lane * (a.N >> 7) + nblk] : 1.0f;
   }
 
-  // activation fragments this wave loads per stage: f = 4 * wave + i -> row tile f / 2, half f % 2;
-  // lane l fetches row tile*16 + l%16 at the fragment's reduction offset
+  // --- DMA assignment (per wave, per stage) ---
+  // activations: full item -> row tiles 2w, 2w + 1 (x H halves); half item -> row tile w
   const uint8_t* arow[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int rr = (2 * wave + i) * 16 + j16;
+    const int rt = half ? wave : 2 * wave + i;
+    const int rr = rt * 16 + j16;
     const int r = row0 + (rr < nr ? rr : 0);
     int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
     if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
     arow[i] = (const uint8_t*)a.act + (size_t)src * a.lda * 2;
   }
+  // weights: full item -> column tiles 2 * wrow, 2 * wrow + 1 of this wave's slot (the other
+  // row half loads the other two); half item -> all 4 tiles of this wave's slot
+  const uint8_t* wsrc[4];
+  int wdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = half ? i : 2 * wrow + (i & 1);
+    wsrc[i] = (t / WF == 0 ? w0 : w1) + (size_t)(gw * WF + t % WF) * KT * PACKET_BYTES + (size_t)lane * 16;
+    wdst[i] = (wcol * NT + t) * PK * 1024;
+  }
+  const int wts_off = (half ? Ly::HALF_ACT : Ly::FULL_ACT) * 1024;
 
-  // issue the DMA of stage `step` (clamped into range) into its LDS slot
   auto dma = [&](int step) {
     const int st = min(step, nsteps - 1);
     uint8_t* base = lds + (step % D) * STAGE_B;
+    int issued = 0;
+    if (half) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = 4 * wave + i;
-      const uint8_t* src = arow[i >> 1] + (size_t)(st * PBK + Cd::boff(g4, i & 1)) * 2;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(base + f * 1024), 16, 0, 0);
+      for (int h = 0; h < H; ++h) {
+        const uint8_t* src = arow[0] + (size_t)(st * PBK + Cd::boff(g4, h)) * 2;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(base + (wave * H + h) * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int p = 0; p < PK; ++p)
+          __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + (size_t)(st * PK + p) * PACKET_BYTES),
+                                           (lds_void*)(base + wts_off + wdst[i] + p * 1024), 16, 0, 0);
+      issued = Ly::LH;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+          const uint8_t* src = arow[i] + (size_t)(st * PBK + Cd::boff(g4, h)) * 2;
+          __builtin_amdgcn_global_load_lds((const void*)src,
+                                           (lds_void*)(base + ((2 * wave + i) * H + h) * 1024), 16, 0, 0);
+        }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int p = 0; p < PK; ++p)
+          __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + (size_t)(st * PK + p) * PACKET_BYTES),
+                                           (lds_void*)(base + wts_off + wdst[i] + p * 1024), 16, 0, 0);
+      issued = Ly::LF;
     }
-    uint8_t* wb = base + ACT_B + wave * (NT * PK * 1024);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int p = 0; p < PK; ++p)
-        __builtin_amdgcn_global_load_lds((const void*)(fbase[t] + (size_t)(st * PK + p) * PACKET_BYTES),
-                                         (lds_void*)(wb + (t * PK + p) * 1024), 16, 0, 0);
+    // pad to L loads with repeats of the last weight load (same bytes to the same place)
+    for (int q = issued; q < L; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[half ? 3 : 1] + (size_t)(st * PK + PK - 1) * PACKET_BYTES),
+                                       (lds_void*)(base + wts_off + wdst[half ? 3 : 1] + (PK - 1) * 1024), 16, 0, 0);
   };
 
   f32x4 acc[NT][8];
@@ -193,6 +267,8 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
 #pragma unroll
   for (int s = 0; s < D - 1; ++s) dma(s);
 
+  const int abase = wrow * 8 * H * 1024 + lane * 16;
+  const int wbase = wts_off + wcol * NT * PK * 1024 + lane * 16;
   for (int step = 0; step < nsteps; ++step) {
     // this wave's loads of `step` have landed; after the barrier, every wave's have, and no
     // wave still reads the slot the next DMA overwrites (that of step - 1)
@@ -200,30 +276,27 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
     __builtin_amdgcn_s_barrier();
     dma(step + D - 1);
     const uint8_t* base = lds + (step % D) * STAGE_B;
-    const uint8_t* wb = base + ACT_B + wave * (NT * PK * 1024) + lane * 16;
     float sc[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
       sc[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), (step * PBK) >> 7));
-    bf16x8 af[NT][2];
+    bf16x8 af[NT][H];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       u32x4 pk[PK];
 #pragma unroll
-      for (int p = 0; p < PK; ++p) pk[p] = *(const u32x4*)(wb + (t * PK + p) * 1024);
+      for (int p = 0; p < PK; ++p) pk[p] = *(const u32x4*)(base + wbase + (t * PK + p) * 1024);
       Cd::frags(pk, sc[t / WF], af[t]);
     }
-    const uint8_t* ab = base + lane * 16;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bf16x8 b0 = *(const bf16x8*)(ab + (2 * j) * 1024);
-      const bf16x8 b1 = *(const bf16x8*)(ab + (2 * j + 1) * 1024);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][0], b0, acc[t][j], 0, 0, 0);
+      for (int h = 0; h < H; ++h) {
+        const bf16x8 b = *(const bf16x8*)(base + abase + (j * H + h) * 1024);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][1], b1, acc[t][j], 0, 0, 0);
+        for (int t = 0; t < NT; ++t)
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][h], b, acc[t][j], 0, 0, 0);
+      }
     }
   }
   MOE_WAIT_VMCNT(0);  // the clamped tail DMAs must land before the workgroup's LDS is released
@@ -243,7 +316,7 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int rr = j * 16 + j16;
+    const int rr = wrow * 128 + j * 16 + j16;
     if (rr >= nr) continue;
     const size_t row = (size_t)((long long)row0 + rr + rowoff);
 #pragma unroll
@@ -259,36 +332,36 @@ __global__ void __launch_bounds__(256, 1) grouped_prefill_kernel(GroupedArgs a) 
 }
 
 template <int C, int EPI>
-static hipError_t launch_p(const GroupedArgs& a, int max_tiles, hipStream_t st) {
+static hipError_t launch_p(const GroupedArgs& a, int max_units, hipStream_t st) {
   GroupedArgs b = a;
-  b.NTW = a.N / PEpi<EPI>::WGF;
-  long long n = (long long)max_tiles * b.NTW;
+  b.NTW = a.N / PEpi<EPI>::FULL_F;
+  long long n = (long long)max_units * (b.NTW / 2);
   n = (n + NXCD - 1) / NXCD * NXCD;
   if (n == 0) return hipSuccess;
-  grouped_prefill_kernel<C, EPI><<<(unsigned)n, 256, 0, st>>>(b);
+  grouped_prefill_kernel<C, EPI><<<(unsigned)n, PTHREADS, 0, st>>>(b);
   return hipGetLastError();
 }
 
-int prefill_row_tile() { return PBM; }
+int prefill_row_tile() { return PRB; }
 
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down) {
   auto ok = [](int c) { return c == MOE_BF16 || c == MOE_FP8_E4M3_B128; };
-  return act == MOE_BF16 && ok(cr) && cr == cs && K % PBK == 0 && K <= 64 * 128 &&
-         N_gateup % PEpi<EPI_SWIGLU>::WGF == 0 &&
-         N_down % PEpi<EPI_PLAIN>::WGF == 0;
+  const int pbk = cr == MOE_BF16 ? PCodec<MOE_BF16>::PBK : PCodec<MOE_FP8_E4M3_B128>::PBK;
+  return act == MOE_BF16 && ok(cr) && cr == cs && K % pbk == 0 && K % 128 == 0 && K <= 64 * 128 &&
+         N_gateup % (2 * PEpi<EPI_SWIGLU>::FULL_F) == 0 && N_down % (2 * PEpi<EPI_PLAIN>::FULL_F) == 0;
 }
 
-hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const GroupedArgs& a, int max_tiles,
+hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const GroupedArgs& a, int max_units,
                                   hipStream_t st) {
-  if (act != MOE_BF16 || cr != cs || a.K % PBK != 0) return hipErrorInvalidValue;
+  if (act != MOE_BF16 || cr != cs || a.K % 128 != 0) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU) {
-    if (a.N % PEpi<EPI_SWIGLU>::WGF) return hipErrorInvalidValue;
-    if (cr == MOE_BF16) return launch_p<MOE_BF16, EPI_SWIGLU>(a, max_tiles, st);
-    if (cr == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI_SWIGLU>(a, max_tiles, st);
+    if (a.N % (2 * PEpi<EPI_SWIGLU>::FULL_F)) return hipErrorInvalidValue;
+    if (cr == MOE_BF16) return launch_p<MOE_BF16, EPI_SWIGLU>(a, max_units, st);
+    if (cr == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI_SWIGLU>(a, max_units, st);
   } else if (epi == EPI_PLAIN) {
-    if (a.N % PEpi<EPI_PLAIN>::WGF) return hipErrorInvalidValue;
-    if (cr == MOE_BF16) return launch_p<MOE_BF16, EPI_PLAIN>(a, max_tiles, st);
-    if (cr == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI_PLAIN>(a, max_tiles, st);
+    if (a.N % (2 * PEpi<EPI_PLAIN>::FULL_F)) return hipErrorInvalidValue;
+    if (cr == MOE_BF16) return launch_p<MOE_BF16, EPI_PLAIN>(a, max_units, st);
+    if (cr == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI_PLAIN>(a, max_units, st);
   }
   return hipErrorInvalidValue;
 }

@@ -196,9 +196,24 @@ __global__ void fill_mxfp4_kernel(uint8_t* codes, uint8_t* scales, uint32_t k0, 
   *(uint32_t*)(scales + (size_t)m * (K / 32) * N + (size_t)kb * N + c0) = E[0] | (E[1] << 8) | (E[2] << 16) | (E[3] << 24);
 }
 
+// A plain 16-byte-per-lane copy: the known-size reference for hardware byte counters.
+__global__ void __launch_bounds__(256) copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                     long long n16) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
 
 extern "C" {
+
+// dst[0, bytes) <- src[0, bytes); bytes a multiple of 16, both pointers 16-byte aligned.
+int gen_copy(const void* src, void* dst, long long bytes, hipStream_t st) {
+  if (bytes % 16 || ((uintptr_t)src | (uintptr_t)dst) % 16) return -1;
+  if (!bytes) return 0;
+  copy16_kernel<<<4096, 256, 0, st>>>((const uint4*)src, (uint4*)dst, bytes / 16);
+  return (int)hipGetLastError();
+}
 
 int gen_fill_dense(void* out, int fmt, uint32_t k0, uint32_t k1, uint32_t stream0, int count, long long n,
                    long long start, float sigma, const int32_t* T, const int32_t* TT, hipStream_t st) {

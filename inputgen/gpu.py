@@ -42,6 +42,7 @@ def lib():
         _lib.gen_fill_dense.argtypes = [p, i32, u32, u32, u32, i32, i64, i64, f32, p, p, p]
         _lib.gen_fill_fp8.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_fill_mxfp4.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
+        _lib.gen_copy.argtypes = [p, p, i64, p]
     return _lib
 
 
@@ -62,6 +63,13 @@ def _stream():
 def _chk(rc, what):
     if rc != 0:
         raise RuntimeError("inputgen %s failed (%d)" % (what, rc))
+
+
+def copy(src, dst):
+    """dst <- src with one plain copy kernel (the known-size reference for byte counters)."""
+    n = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= n
+    _chk(lib().gen_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, _stream()), "copy")
 
 
 def fill_dense(out, fmt: str, seed: int, tid: int, stream0: int, count: int, n: int, start: int = 0,

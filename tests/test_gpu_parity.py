@@ -104,12 +104,19 @@ SMALL = [
     ("k1-f32", L.LayerSpec("s6", T=70, H=384, E=3, k=1, I=256, act="f32", w_routed="f32", w_shared="f32",
                            shared=True, seed=36)),
     ("wide-E", L.LayerSpec("s7", T=9, H=256, E=300, k=7, I=128, seed=37)),
+    # groups of several hundred rows: whole 256-row tiles, a padded last tile and a <= 128-row
+    # remainder in the prefill kernel
+    ("ragged-groups", L.LayerSpec("s8", T=600, H=512, E=6, k=2, I=256, shared=True, router="zipf",
+                                  zipf_alpha=1.0, calib_tokens=512, seed=38)),
+    ("ragged-groups-fp8", L.LayerSpec("s9", T=520, H=1024, E=5, k=2, I=512, shared=True, w_routed="fp8",
+                                      w_shared="fp8", router="zipf", zipf_alpha=0.8, calib_tokens=512,
+                                      seed=39)),
 ]
 
 
 def _prefill_ok(spec):
     return (spec.act == "bf16" and spec.w_routed in ("bf16", "fp8")
-            and (not spec.shared or spec.w_shared == spec.w_routed) and spec.I % 128 == 0 and spec.H % 256 == 0)
+            and (not spec.shared or spec.w_shared == spec.w_routed) and spec.I % 256 == 0 and spec.H % 512 == 0)
 
 
 @pytest.mark.parametrize("name,spec", SMALL, ids=[s[0] for s in SMALL])
