@@ -24,6 +24,8 @@
 // items that exist: workgroups resident at the same time on one XCD then share weight and
 // activation slices in that XCD's L2 (Chapter 6 'Supernodes' section 6.3.2: one weight read
 // serves many rows).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -51,18 +53,23 @@ struct PCodec<MOE_BF16> {
   }
 };
 
-// e4m3fn -> fp32 (exact) -> * block scale -> bf16 (round to nearest even)
+// fp8 weights: a 128 x 128 block scale s is split as s = 2^e * m with m in [1, 2). The
+// conversion e4m3 -> bf16 applies 2^e (v_cvt_scalef32_pk_bf16_fp8 uses only the exponent of its
+// scale operand), which is exact: an e4m3 value has 4 significant bits. The mantissa factor m is
+// carried by the accumulators instead: at each 128-deep reduction block they are multiplied by
+// m_previous / m_current, and the epilogue multiplies by the last block's m. The sum is
+// therefore sum_b s_b * (q_b . x_b) with the weights exact and fp32 rounding only.
+__device__ __forceinline__ float scale_mantissa(float s) {
+  return __int_as_float((__float_as_int(s) & 0x007FFFFF) | 0x3F800000);
+}
+
 __device__ __forceinline__ bf16x8 p_fp8x8(uint32_t w0, uint32_t w1, float s) {
-  typedef __attribute__((ext_vector_type(2))) float f2;
-  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
-  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
-  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
-  const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  typedef __attribute__((ext_vector_type(2))) __bf16 b2;
   u32x4 r;
-  r[0] = pack_bf16x2(a.x * s, a.y * s);
-  r[1] = pack_bf16x2(b.x * s, b.y * s);
-  r[2] = pack_bf16x2(c.x * s, c.y * s);
-  r[3] = pack_bf16x2(d.x * s, d.y * s);
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -194,68 +201,42 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     scv[m] = (C == MOE_FP8_E4M3_B128 && lane < (a.K >> 7)) ? sp[lane * (a.N >> 7) + nblk] : 1.0f;
   }
 
-  // --- DMA assignment (per wave, per stage) ---
-  // activations: full item -> row tiles 2w, 2w + 1 (x H halves); half item -> row tile w
-  const uint8_t* arow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rt = half ? wave : 2 * wave + i;
-    const int rr = rt * 16 + j16;
-    const int r = row0 + (rr < nr ? rr : 0);
-    int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
-    if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
-    arow[i] = (const uint8_t*)a.act + (size_t)src * a.lda * 2;
-  }
-  // weights: full item -> column tiles 2 * wrow, 2 * wrow + 1 of this wave's slot (the other
-  // row half loads the other two); half item -> all 4 tiles of this wave's slot
-  const uint8_t* wsrc[4];
-  int wdst[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = half ? i : 2 * wrow + (i & 1);
-    wsrc[i] = (t / WF == 0 ? w0 : w1) + (size_t)(gw * WF + t % WF) * KT * PACKET_BYTES + (size_t)lane * 16;
-    wdst[i] = (wcol * NT + t) * PK * 1024;
-  }
+  // --- DMA assignment: this wave's L loads per stage, q = 0 .. L - 1 ---
+  // full item: activation row tiles 2w, 2w + 1 (x H halves), then column tiles 2 * wrow,
+  //            2 * wrow + 1 of this wave's slot (the other row half loads the other two);
+  // half item: activation row tile w (x H halves), then all 4 column tiles of this wave's slot.
+  // Load q of stage s reads qsrc[q] + s * qstride[q] into LDS stage offset qdst[q]; the shorter
+  // kind repeats its last load (same bytes to the same place) so both issue L loads.
+  const uint8_t* qsrc[L];
+  int qdst[L], qstride[L];
   const int wts_off = (half ? Ly::HALF_ACT : Ly::FULL_ACT) * 1024;
-
-  auto dma = [&](int step) {
-    const int st = min(step, nsteps - 1);
-    uint8_t* base = lds + (step % D) * STAGE_B;
-    int issued = 0;
-    if (half) {
 #pragma unroll
-      for (int h = 0; h < H; ++h) {
-        const uint8_t* src = arow[0] + (size_t)(st * PBK + Cd::boff(g4, h)) * 2;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(base + (wave * H + h) * 1024), 16, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int p = 0; p < PK; ++p)
-          __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + (size_t)(st * PK + p) * PACKET_BYTES),
-                                           (lds_void*)(base + wts_off + wdst[i] + p * 1024), 16, 0, 0);
-      issued = Ly::LH;
+  for (int q = 0; q < L; ++q) {
+    const int nact = half ? H : 2 * H;
+    const int nw = half ? 4 * PK : 2 * PK;
+    const int qq = q < nact + nw ? q : nact + nw - 1;
+    if (qq < nact) {
+      const int i = qq / H, h = qq % H;
+      const int rt = half ? wave : 2 * wave + i;
+      const int rr = rt * 16 + j16;
+      const int r = row0 + (rr < nr ? rr : 0);
+      int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
+      if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
+      qsrc[q] = (const uint8_t*)a.act + ((size_t)src * a.lda + Cd::boff(g4, h)) * 2;
+      qdst[q] = (rt * H + h) * 1024;
+      qstride[q] = PBK * 2;
     } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int h = 0; h < H; ++h) {
-          const uint8_t* src = arow[i] + (size_t)(st * PBK + Cd::boff(g4, h)) * 2;
-          __builtin_amdgcn_global_load_lds((const void*)src,
-                                           (lds_void*)(base + ((2 * wave + i) * H + h) * 1024), 16, 0, 0);
-        }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int p = 0; p < PK; ++p)
-          __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + (size_t)(st * PK + p) * PACKET_BYTES),
-                                           (lds_void*)(base + wts_off + wdst[i] + p * 1024), 16, 0, 0);
-      issued = Ly::LF;
+      const int i = (qq - nact) / PK, p = (qq - nact) % PK;
+      const int t = half ? i : 2 * wrow + i;
+      qsrc[q] = (t / WF == 0 ? w0 : w1) + ((size_t)(gw * WF + t % WF) * KT + p) * PACKET_BYTES + (size_t)lane * 16;
+      qdst[q] = wts_off + ((wcol * NT + t) * PK + p) * 1024;
+      qstride[q] = PK * PACKET_BYTES;
     }
-    // pad to L loads with repeats of the last weight load (same bytes to the same place)
-    for (int q = issued; q < L; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc[half ? 3 : 1] + (size_t)(st * PK + PK - 1) * PACKET_BYTES),
-                                       (lds_void*)(base + wts_off + wdst[half ? 3 : 1] + (PK - 1) * 1024), 16, 0, 0);
+  }
+  auto dma_one = [&](int q, int step) {
+    const int st = min(step, nsteps - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(qsrc[q] + (size_t)st * qstride[q]),
+                                     (lds_void*)(lds + (step % D) * STAGE_B + qdst[q]), 16, 0, 0);
   };
 
   f32x4 acc[NT][8];
@@ -265,21 +246,36 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     for (int j = 0; j < 8; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int s = 0; s < D - 1; ++s) dma(s);
+  for (int s = 0; s < D - 1; ++s)
+#pragma unroll
+    for (int q = 0; q < L; ++q) dma_one(q, s);
 
   const int abase = wrow * 8 * H * 1024 + lane * 16;
   const int wbase = wts_off + wcol * NT * PK * 1024 + lane * 16;
-  for (int step = 0; step < nsteps; ++step) {
+  // fp8: mantissa factor of the current block scale, per matrix (see scale_mantissa)
+  constexpr bool SCALED = C == MOE_FP8_E4M3_B128;
+  constexpr int SPB = SCALED ? 128 / PBK : 1;  // pipeline steps per scale block
+  float mcur[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) mcur[m] = scale_mantissa(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), 0)));
+
+  auto step_body = [&](int step, auto first_of_block) {
+    constexpr bool RESCALE = SCALED && decltype(first_of_block)::value;
     // this wave's loads of `step` have landed; after the barrier, every wave's have, and no
     // wave still reads the slot the next DMA overwrites (that of step - 1)
     MOE_WAIT_VMCNT((D - 2) * L);
     __builtin_amdgcn_s_barrier();
-    dma(step + D - 1);
     const uint8_t* base = lds + (step % D) * STAGE_B;
-    float sc[NMAT];
+    float sc[NMAT], rs[NMAT];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int m = 0; m < NMAT; ++m) {
       sc[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), (step * PBK) >> 7));
+      if constexpr (RESCALE) {
+        const float mn = scale_mantissa(sc[m]);
+        rs[m] = mcur[m] / mn;
+        mcur[m] = mn;
+      }
+    }
     bf16x8 af[NT][H];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -288,16 +284,37 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       for (int p = 0; p < PK; ++p) pk[p] = *(const u32x4*)(base + wbase + (t * PK + p) * 1024);
       Cd::frags(pk, sc[t / WF], af[t]);
     }
+    // the next stage's DMA is spread over the MFMA stream, one load per row tile, so the
+    // loads never queue up in front of the matrix work
+    bf16x8 bn[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) bn[h] = *(const bf16x8*)(base + abase + h * 1024);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      bf16x8 b[H];
 #pragma unroll
-      for (int h = 0; h < H; ++h) {
-        const bf16x8 b = *(const bf16x8*)(base + abase + (j * H + h) * 1024);
+      for (int h = 0; h < H; ++h) b[h] = bn[h];
+      if (j + 1 < 8) {
+#pragma unroll
+        for (int h = 0; h < H; ++h) bn[h] = *(const bf16x8*)(base + abase + ((j + 1) * H + h) * 1024);
+      }
+      if constexpr (RESCALE) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][j] *= rs[t / WF];
+      }
+#pragma unroll
+      for (int h = 0; h < H; ++h)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][h], b, acc[t][j], 0, 0, 0);
-      }
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][h], b[h], acc[t][j], 0, 0, 0);
+      if (j < L) dma_one(j, step + D - 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  for (int step = 0; step < nsteps; step += SPB) {
+    step_body(step, std::true_type{});
+#pragma unroll
+    for (int u = 1; u < SPB; ++u) step_body(step + u, std::false_type{});
   }
   MOE_WAIT_VMCNT(0);  // the clamped tail DMAs must land before the workgroup's LDS is released
 
@@ -325,7 +342,8 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        v[i] = (EPI == EPI_SWIGLU) ? silu(acc[f][j][i]) * acc[WF + f][j][i] : acc[f][j][i];
+        v[i] = (EPI == EPI_SWIGLU) ? silu(acc[f][j][i] * mcur[0]) * (acc[WF + f][j][i] * mcur[NMAT - 1])
+                                   : acc[f][j][i] * mcur[0];
       *(u32x2*)(out + (row * ldo + n) * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }
