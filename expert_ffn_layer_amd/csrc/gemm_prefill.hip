@@ -46,8 +46,13 @@ struct PCodec<MOE_BF16> {
   static constexpr int PBK = 32;     // reduction elements per pipeline step
   static constexpr int H = 1;        // 32-deep MFMA steps per pipeline step
   static constexpr int PK = 1;       // packets per 16-column tile per pipeline step
-  // element offset (within a step) of the B fragment of half h for lane group g
-  __device__ static int boff(int g, int) { return 8 * g; }
+  // Activation layout of one 16-row tile per step (H KiB of LDS): DMA unit u, lane l reads
+  // 16 bytes of row dma_row(l, u) at byte dma_off(l, u) of the row's step slice and lands them
+  // at u * 1024 + 16 * l; the B fragment of MFMA half h is the 16 bytes at read_off(l, h).
+  // bf16: lane l holds row l % 16, reduction elements 8 * (l / 16) .. + 8 (the packet's order).
+  __device__ static int dma_row(int l, int) { return l & 15; }
+  __device__ static int dma_off(int l, int) { return 16 * (l >> 4); }
+  __device__ static int read_off(int l, int) { return 16 * l; }
   __device__ static void frags(const u32x4 (&w)[PK], float, bf16x8 (&a)[H]) {
     a[0] = __builtin_bit_cast(bf16x8, w[0]);
   }
@@ -79,9 +84,18 @@ struct PCodec<MOE_FP8_E4M3_B128> {
   static constexpr int PBK = 64;
   static constexpr int H = 2;
   static constexpr int PK = 1;
-  // lane group g of a packet holds reduction elements 16g .. 16g + 15; MFMA half h takes the
-  // h-th run of 8 of them, so the activation fragment must carry the same elements
-  __device__ static int boff(int g, int h) { return 16 * g + 8 * h; }
+  // Lane group g of a packet holds reduction elements 16g .. 16g + 15 and MFMA half h takes the
+  // h-th run of 8 of them, so the B fragment of half h for lane (g, row j) is the 16-byte chunk
+  // c = 2g + h of row j's 128-byte step slice. DMA unit u moves rows 8u .. 8u + 7 as whole
+  // 128-byte lines (lane l: row l / 8, chunk (l % 8) ^ (l / 8) ^ u), so row r of unit u stores
+  // chunk c at position c ^ (r % 8) ^ u: the XOR swizzle spreads the 16 lanes of each read phase
+  // over all 64 LDS banks.
+  __device__ static int dma_row(int l, int u) { return 8 * u + (l >> 3); }
+  __device__ static int dma_off(int l, int u) { return 16 * ((l & 7) ^ (l >> 3) ^ u); }
+  __device__ static int read_off(int l, int h) {
+    const int j = l & 15, g = l >> 4;
+    return (j >> 3) * 1024 + (j & 7) * 128 + 16 * ((2 * g + h) ^ (j & 7) ^ (j >> 3));
+  }
   __device__ static void frags(const u32x4 (&w)[PK], float s, bf16x8 (&a)[H]) {
     a[0] = p_fp8x8(w[0][0], w[0][1], s);
     a[1] = p_fp8x8(w[0][2], w[0][3], s);
@@ -202,9 +216,9 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   }
 
   // --- DMA assignment: this wave's L loads per stage, q = 0 .. L - 1 ---
-  // full item: activation row tiles 2w, 2w + 1 (x H halves), then column tiles 2 * wrow,
+  // full item: activation row tiles 2w, 2w + 1 (x H DMA units), then column tiles 2 * wrow,
   //            2 * wrow + 1 of this wave's slot (the other row half loads the other two);
-  // half item: activation row tile w (x H halves), then all 4 column tiles of this wave's slot.
+  // half item: activation row tile w (x H DMA units), then all 4 column tiles of this wave's slot.
   // Load q of stage s reads qsrc[q] + s * qstride[q] into LDS stage offset qdst[q]; the shorter
   // kind repeats its last load (same bytes to the same place) so both issue L loads.
   const uint8_t* qsrc[L];
@@ -218,11 +232,11 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     if (qq < nact) {
       const int i = qq / H, h = qq % H;
       const int rt = half ? wave : 2 * wave + i;
-      const int rr = rt * 16 + j16;
+      const int rr = rt * 16 + Cd::dma_row(lane, h);
       const int r = row0 + (rr < nr ? rr : 0);
       int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
       if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
-      qsrc[q] = (const uint8_t*)a.act + ((size_t)src * a.lda + Cd::boff(g4, h)) * 2;
+      qsrc[q] = (const uint8_t*)a.act + (size_t)src * a.lda * 2 + Cd::dma_off(lane, h);
       qdst[q] = (rt * H + h) * 1024;
       qstride[q] = PBK * 2;
     } else {
@@ -250,7 +264,9 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
 #pragma unroll
     for (int q = 0; q < L; ++q) dma_one(q, s);
 
-  const int abase = wrow * 8 * H * 1024 + lane * 16;
+  int aoff[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) aoff[h] = wrow * 8 * H * 1024 + Cd::read_off(lane, h);
   const int wbase = wts_off + wcol * NT * PK * 1024 + lane * 16;
   // fp8: mantissa factor of the current block scale, per matrix (see scale_mantissa)
   constexpr bool SCALED = C == MOE_FP8_E4M3_B128;
@@ -288,7 +304,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     // loads never queue up in front of the matrix work
     bf16x8 bn[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h) bn[h] = *(const bf16x8*)(base + abase + h * 1024);
+    for (int h = 0; h < H; ++h) bn[h] = *(const bf16x8*)(base + aoff[h]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       bf16x8 b[H];
@@ -296,7 +312,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       for (int h = 0; h < H; ++h) b[h] = bn[h];
       if (j + 1 < 8) {
 #pragma unroll
-        for (int h = 0; h < H; ++h) bn[h] = *(const bf16x8*)(base + abase + ((j + 1) * H + h) * 1024);
+        for (int h = 0; h < H; ++h) bn[h] = *(const bf16x8*)(base + aoff[h] + (j + 1) * H * 1024);
       }
       if constexpr (RESCALE) {
 #pragma unroll
