@@ -26,7 +26,10 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 # (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads for the plain copy
 # kernel of known size that --calib-copy appends. Keyed by workload; an entry holds only while
 # the kernel sources it was measured on are unchanged (sha256 of those files).
-TRAFFIC = {}
+TRAFFIC = {
+    "c2": {"sha": "9feeb668f9ef2a50", "bytes": 3177000000},  # gate/up decode kernel
+    "c5": {"sha": "ba3731e3ed1b87bb", "bytes": 17442000000},  # gate/up prefill kernel
+}
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
                   "prefill": ("gemm_prefill.hip", "common.h", "kernels.h")}
