@@ -4,10 +4,12 @@
 // The weights are the MFMA A operand (16 features x KP reduction elements per 1 KiB packet, one
 // 128-bit load per lane), the gathered activations the B operand (16 rows), so one
 // v_mfma_f32_16x16x32_bf16 (or 16x16x4_f32) consumes a packet with no data shuffles. The four
-// waves of a workgroup split the rows into 16-row slices and, when there are fewer than 64
-// rows, split the reduction into 2 or 4 contiguous parts whose fp32 partial sums are added in
-// LDS in a fixed order. Each selected expert's weights are therefore streamed once per block
-// of 64 rows (the within-batch reuse of Chapter 6 'Supernodes', section 6.3.2).
+// waves of a workgroup split the reduction into contiguous parts and, for f32/bf16, each wave
+// runs all 1, 2 or 4 row tiles of the block, so every weight packet is loaded once per item
+// and feeds one MFMA per row tile (the converted formats split thick blocks' rows over the
+// waves instead); the fp32 partial sums are added in LDS in a fixed order. Each selected
+// expert's weights are therefore streamed once per block of 64 rows (the within-batch reuse of
+// Chapter 6 'Supernodes', section 6.3.2).
 //
 // Epilogues: SwiGLU (gate and up tiles of the same features, h = SiLU(g) * u,
 // Chapter 6 section 6.2.2), plain store in the activation type, or plain fp32 store (router
@@ -109,28 +111,26 @@ struct EpiTraits {
 };
 
 // Registers of one pipeline stage: U consecutive packets of each of the NMAT x NF streams,
-// the matching activation chunks and the packets' scales.
-template <int C, int NMAT, int NF, int U>
+// the matching activation chunks of the MT row tiles and the packets' scales.
+template <int C, int NMAT, int NF, int MT, int U>
 struct Stage {
-  u32x4 x[U][Codec<C>::ACT16];
+  u32x4 x[U][MT][Codec<C>::ACT16];
   u32x4 w[U][NMAT][NF];
   float s[U][NMAT][NF];
 };
 
 // Issue the loads of packets kt .. kt+U-1 (indices past kt1-1 re-read packet kt1-1 and are
 // not used, so every address stays inside the stream).
-template <int C, int ACT, int NMAT, int NF, int U>
-__device__ __forceinline__ void load_stage(Stage<C, NMAT, NF, U>& st, const uint8_t* __restrict__ w0,
+template <int C, int ACT, int NMAT, int NF, int MT, int U>
+__device__ __forceinline__ void load_stage(Stage<C, NMAT, NF, MT, U>& st, const uint8_t* __restrict__ w0,
                                            const uint8_t* __restrict__ w1, const uint8_t* __restrict__ s0,
-                                           const uint8_t* __restrict__ s1, const uint8_t* __restrict__ xrow, int N,
+                                           const uint8_t* __restrict__ s1, const uint8_t* const (&xrow)[MT], int N,
                                            int KT, int nt0, int kt, int kt1, int lane) {
   using Cd = Codec<C>;
   constexpr int AB = ACT == MOE_F32 ? 4 : 2;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int k = min(kt + u, kt1 - 1);
-#pragma unroll
-    for (int i = 0; i < Cd::ACT16; ++i) st.x[u][i] = *(const u32x4*)(xrow + (size_t)k * Cd::KP * AB + i * 16);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const size_t off = ((size_t)(nt0 + f) * KT + k) * PACKET_BYTES + (size_t)lane * 16;
@@ -141,95 +141,110 @@ __device__ __forceinline__ void load_stage(Stage<C, NMAT, NF, U>& st, const uint
         st.s[u][NMAT - 1][f] = packet_scale<C>(s1, N, KT, nt0 + f, k, lane);
       }
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < Cd::ACT16; ++i)
+        st.x[u][m][i] = *(const u32x4*)(xrow[m] + (size_t)k * Cd::KP * AB + i * 16);
   }
 }
 
-template <int C, int NMAT, int NF, int U>
-__device__ __forceinline__ void mma_stage(const Stage<C, NMAT, NF, U>& st, f32x4 (&acc)[NMAT][NF]) {
+template <int C, int NMAT, int NF, int MT, int U>
+__device__ __forceinline__ void mma_stage(const Stage<C, NMAT, NF, MT, U>& st, f32x4 (&acc)[MT][NMAT][NF]) {
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+    for (int r = 0; r < MT; ++r)
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) Codec<C>::mma(st.w[u][m][f], st.x[u], st.s[u][m][f], acc[m][f]);
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) Codec<C>::mma(st.w[u][m][f], st.x[u][r], st.s[u][m][f], acc[r][m][f]);
 }
 
 // The same with the weight operand of packets kt + u >= kt1 replaced by zero codes (which
 // decode to 0 in every format), so the MFMAs stay unconditional: no branches around them.
-template <int C, int NMAT, int NF, int U>
-__device__ __forceinline__ void mma_stage_masked(const Stage<C, NMAT, NF, U>& st, int kt, int kt1,
-                                                 f32x4 (&acc)[NMAT][NF]) {
+template <int C, int NMAT, int NF, int MT, int U>
+__device__ __forceinline__ void mma_stage_masked(const Stage<C, NMAT, NF, MT, U>& st, int kt, int kt1,
+                                                 f32x4 (&acc)[MT][NMAT][NF]) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const bool valid = kt + u < kt1;
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+    for (int r = 0; r < MT; ++r)
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-        Codec<C>::mma(valid ? st.w[u][m][f] : zero, st.x[u], st.s[u][m][f], acc[m][f]);
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+          Codec<C>::mma(valid ? st.w[u][m][f] : zero, st.x[u][r], st.s[u][m][f], acc[r][m][f]);
   }
 }
 
 // Packets per pipeline stage along K, chosen so a stage keeps about 8 weight packets (4 for the
 // formats converted in registers, whose temporaries would otherwise cost occupancy) and at most
-// 8 activation chunks per lane in flight.
-template <int C, int NMAT, int NF>
+// 8 activation chunks per lane in flight (4 with several row tiles, whose accumulators and
+// activation chunks would otherwise raise the register count of the whole kernel and cost the
+// thin items occupancy).
+template <int C, int NMAT, int NF, int MT>
 constexpr int stage_depth() {
   constexpr int per_stage = (C == MOE_BF16 || C == MOE_F32) ? 8 : 4;
-  constexpr int a = per_stage / (NF * NMAT), b = 8 / Codec<C>::ACT16;
+  constexpr int a = per_stage / (NF * NMAT), b = (MT == 1 ? 8 : 4) / (Codec<C>::ACT16 * MT);
   constexpr int u = a < b ? a : b;
   return u < 1 ? 1 : u;
 }
 
-// One wave: 16 rows x (16*NF) features of NMAT matrices over packets [kt0, kt1), with the
-// loads of the next stage in flight while the current stage feeds the MFMAs.
-template <int C, int ACT, int NMAT, int NF>
+// One wave: MT row tiles of 16 rows x (16*NF) features of NMAT matrices over packets
+// [kt0, kt1), with the loads of the next stage in flight while the current stage feeds the
+// MFMAs. Every weight packet the wave loads feeds all MT row tiles.
+template <int C, int ACT, int NMAT, int NF, int MT>
 __device__ __forceinline__ void wave_mma(const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
                                          const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,
-                                         const uint8_t* __restrict__ xrow, int N, int KT, int nt0,
-                                         int kt0, int kt1, int lane, f32x4 (&acc)[NMAT][NF]) {
-  constexpr int U = stage_depth<C, NMAT, NF>();
+                                         const uint8_t* const (&xrow)[MT], int N, int KT, int nt0, int kt0, int kt1,
+                                         int lane, f32x4 (&acc)[MT][NMAT][NF]) {
+  constexpr int U = stage_depth<C, NMAT, NF, MT>();
   if (kt0 >= kt1) return;
-  Stage<C, NMAT, NF, U> A, B;
-  load_stage<C, ACT, NMAT, NF, U>(A, w0, w1, s0, s1, xrow, N, KT, nt0, kt0, kt1, lane);
+  Stage<C, NMAT, NF, MT, U> A, B;
+  load_stage<C, ACT, NMAT, NF, MT, U>(A, w0, w1, s0, s1, xrow, N, KT, nt0, kt0, kt1, lane);
   int kt = kt0;
   // steady state: both stages entirely inside the range, so every load and MFMA is
   // unconditional and the wait counts stay exact (the next stage's loads remain in flight)
   for (; kt + 2 * U < kt1; kt += 2 * U) {
-    load_stage<C, ACT, NMAT, NF, U>(B, w0, w1, s0, s1, xrow, N, KT, nt0, kt + U, kt1, lane);
+    load_stage<C, ACT, NMAT, NF, MT, U>(B, w0, w1, s0, s1, xrow, N, KT, nt0, kt + U, kt1, lane);
     mma_stage(A, acc);
-    load_stage<C, ACT, NMAT, NF, U>(A, w0, w1, s0, s1, xrow, N, KT, nt0, kt + 2 * U, kt1, lane);
+    load_stage<C, ACT, NMAT, NF, MT, U>(A, w0, w1, s0, s1, xrow, N, KT, nt0, kt + 2 * U, kt1, lane);
     mma_stage(B, acc);
   }
   // remainder (1 .. 2U packets), branch-free: packets past the range are masked to zero
-  load_stage<C, ACT, NMAT, NF, U>(B, w0, w1, s0, s1, xrow, N, KT, nt0, kt + U, kt1, lane);
+  load_stage<C, ACT, NMAT, NF, MT, U>(B, w0, w1, s0, s1, xrow, N, KT, nt0, kt + U, kt1, lane);
   mma_stage_masked(A, kt, kt1, acc);
   mma_stage_masked(B, kt + U, kt1, acc);
 }
 
-template <int C, int ACT, int EPI, int NF>
-__device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_shared, int blk, int ntw,
+// One work item: rows row0 .. row0 + nr - 1 (nr <= 16 * MT * MTP) of group g, features
+// ntw * 16 * NF .. + 16 * NF. The four waves form MTP row groups of MT row tiles each and split
+// the reduction into KS = 4 / MTP contiguous parts (wave = row group + MTP * part); a wave runs
+// all MT row tiles of its group, so within a row group every weight byte is loaded once and
+// feeds MT MFMAs. The KS partial sums of row tile r are added in LDS in ascending part order by
+// the wave of part r % KS, which then writes the row tile: the result does not depend on
+// scheduling.
+template <int C, int ACT, int EPI, int NF, int MT, int MTP>
+__device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_shared, int row0, int nr, int ntw,
                                          float* red) {
   constexpr int NMAT = EpiTraits<EPI>::NMAT;
   constexpr int KP = Codec<C>::KP;
+  constexpr int NREG = NMAT * NF * 4;
+  constexpr int KS = 4 / MTP;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rbeg = a.group_range ? a.group_range[2 * g] : 0;
-  const int rend = a.group_range ? a.group_range[2 * g + 1] : a.M;
-  const int row0 = rbeg + RB * blk;
-  const int nr = min(RB, rend - row0);
-  const int mtp = nr <= 16 ? 1 : (nr <= 32 ? 2 : 4);
-  const int ks = 4 / mtp;
-  const int msub = wave % mtp, kpart = wave / mtp;
-  const int wr0 = row0 + 16 * msub;
-  const int wnr = nr - 16 * msub;
+  const int msub = wave % MTP, kpart = wave / MTP;
   const int KT = a.K / KP;
   // reduction range of this workgroup (split-K across workgroups for fp32 partial outputs), then
   // of this wave
-  const int KS = a.ksplit > 1 ? a.ksplit : 1;
-  const int ktA = blockIdx.y * KT / KS, ktB = (blockIdx.y + 1) * KT / KS;
-  const int kt0 = ktA + kpart * (ktB - ktA) / ks, kt1 = ktA + (kpart + 1) * (ktB - ktA) / ks;
+  const int KSG = a.ksplit > 1 ? a.ksplit : 1;
+  const int ktA = blockIdx.y * KT / KSG, ktB = (blockIdx.y + 1) * KT / KSG;
+  const int kt0 = ktA + kpart * (ktB - ktA) / KS, kt1 = ktA + (kpart + 1) * (ktB - ktA) / KS;
   const int nt0 = ntw * NF;
+  const int wrow0 = row0 + 16 * MT * msub;  // first row of this wave's row group
+  const int wnr = nr - 16 * MT * msub;      // rows of the group (may be <= 0)
 
   // operand pointers
   const uint8_t* w0 = is_shared ? a.wa_s : a.wa_r + (size_t)g * a.mat_bytes;
@@ -238,69 +253,119 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
   const uint8_t* s1 = is_shared ? a.sb_s : (a.sb_r ? a.sb_r + (size_t)g * a.scale_bytes : nullptr);
 
   const int rl = lane & 15;
-  const int r = (wnr > 0) ? wr0 + (rl < wnr ? rl : 0) : row0;
-  int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
-  if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
   constexpr int AB = ACT == MOE_F32 ? 4 : 2;
-  const uint8_t* xrow = (const uint8_t*)a.act + ((size_t)src * a.lda + (lane >> 4) * (KP / 4)) * AB;
+  const uint8_t* xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int rr = 16 * m + rl;
+    const int r = rr < wnr ? wrow0 + rr : row0;
+    int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
+    if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
+    xrow[m] = (const uint8_t*)a.act + ((size_t)src * a.lda + (lane >> 4) * (KP / 4)) * AB;
+  }
 
-  f32x4 acc[NMAT][NF];
+  f32x4 acc[MT][NMAT][NF];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+  for (int r = 0; r < MT; ++r)
 #pragma unroll
-    for (int f = 0; f < NF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[r][m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (wnr > 0) wave_mma<C, ACT, NMAT, NF>(w0, w1, s0, s1, xrow, a.N, KT, nt0, kt0, kt1, lane, acc);
+  if (wnr > 0) wave_mma<C, ACT, NMAT, NF, MT>(w0, w1, s0, s1, xrow, a.N, KT, nt0, kt0, kt1, lane, acc);
 
-  if (ks > 1) {  // fixed-order reduction of the reduction-dimension parts
-    constexpr int NREG = NMAT * NF * 4;
-    if (kpart > 0) {
+  // fixed-order reduction of the KS reduction parts, one row tile per round
+  if constexpr (KS > 1) {
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+    for (int r = 0; r < MT; ++r) {
+      const int owner = r % KS;
+      if (kpart != owner) {
+        const int slot = msub * (KS - 1) + (kpart < owner ? kpart : kpart - 1);
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[((wave - 1) * NREG + (m * NF + f) * 4 + i) * 64 + lane] = acc[m][f][i];
-    }
-    __syncthreads();
-    if (kpart > 0) return;
-    for (int p = 1; p < ks; ++p) {
-      const int wsrc = msub + mtp * p;
+          for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+            for (int i = 0; i < 4; ++i) red[(slot * NREG + (m * NF + f) * 4 + i) * 64 + lane] = acc[r][m][f][i];
+      }
+      __syncthreads();
+      if (kpart == owner) {
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][f][i] += red[((wsrc - 1) * NREG + (m * NF + f) * 4 + i) * 64 + lane];
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float sum = 0.0f;
+#pragma unroll
+              for (int p = 0; p < KS; ++p) {
+                const int slot = msub * (KS - 1) + (p < owner ? p : p - 1);
+                sum += p == owner ? acc[r][m][f][i] : red[(slot * NREG + (m * NF + f) * 4 + i) * 64 + lane];
+              }
+              acc[r][m][f][i] = sum;
+            }
+      }
+      __syncthreads();
     }
   }
-  if (wnr <= 0 || rl >= wnr) return;
 
-  // epilogue: lane holds features n = (nt0+f)*16 + 4*(lane/16) + i of row wr0 + rl
-  const int orow = wr0 + rl;
-  uint8_t* out;
-  int ldo;
-  size_t row;
-  if (a.out_s && orow >= a.P) {
-    out = (uint8_t*)a.out_s;
-    ldo = a.ldo_s;
-    row = (size_t)(orow - a.P);
-  } else {
-    out = (uint8_t*)a.out;
-    ldo = a.ldo;
-    row = (size_t)orow + (size_t)blockIdx.y * a.M;  // split-K part y of an fp32 output
-  }
+  // epilogue: the owner of row tile r writes it; lane holds features
+  // n = (nt0+f)*16 + 4*(lane/16) + i of row wrow0 + 16r + rl
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int n = (nt0 + f) * 16 + 4 * (lane >> 4);
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (EPI == EPI_SWIGLU) ? silu(acc[0][f][i]) * acc[NMAT - 1][f][i] : acc[0][f][i];
-    if (EPI == EPI_F32 || ACT == MOE_F32) {
-      *(f32x4*)(out + (row * ldo + n) * 4) = f32x4{v[0], v[1], v[2], v[3]};
+  for (int r = 0; r < MT; ++r) {
+    if (r % KS != kpart || 16 * r + rl >= wnr) continue;
+    const int orow = wrow0 + 16 * r + rl;
+    uint8_t* out;
+    int ldo;
+    size_t row;
+    if (a.out_s && orow >= a.P) {
+      out = (uint8_t*)a.out_s;
+      ldo = a.ldo_s;
+      row = (size_t)(orow - a.P);
     } else {
-      *(u32x2*)(out + (row * ldo + n) * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      out = (uint8_t*)a.out;
+      ldo = a.ldo;
+      row = (size_t)orow + (size_t)blockIdx.y * a.M;  // split-K part y of an fp32 output
     }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int n = (nt0 + f) * 16 + 4 * (lane >> 4);
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = (EPI == EPI_SWIGLU) ? silu(acc[r][0][f][i]) * acc[r][NMAT - 1][f][i] : acc[r][0][f][i];
+      if (EPI == EPI_F32 || ACT == MOE_F32) {
+        *(f32x4*)(out + (row * ldo + n) * 4) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        *(u32x2*)(out + (row * ldo + n) * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    }
+  }
+}
+
+// Row layout of an item by its row count: 1, 2 or 4 row tiles, split into MTP row groups of MT
+// tiles. Formats with one 16-byte activation chunk per packet (f32, bf16) give each wave as
+// many row tiles as 64 accumulator registers allow, so a packet is loaded once per row group
+// and feeds MT MFMAs. The converted formats, whose activation chunks per packet are 2x-4x
+// larger, split the rows over the waves (each row group loads the packets of its part of K).
+// Both keep the kernel's register count, and so the occupancy of the thin items, near that of
+// the one-row-tile path. LEAN (the shared expert's path in a kernel whose routed experts use
+// another format) always splits rows, so the rarely used path does not set the register count.
+template <int C, int ACT, int EPI, int NF, bool LEAN>
+__device__ __forceinline__ void run_rows(const GroupedArgs& a, int g, bool is_shared, int row0, int nr, int ntw,
+                                         float* red) {
+  constexpr int ACC = EpiTraits<EPI>::NMAT * NF * 4;  // accumulator registers per row tile
+  constexpr int MTMAX =
+      (LEAN || Codec<C>::ACT16 != 1) ? 1 : (4 * ACC <= 64 ? 4 : (2 * ACC <= 64 ? 2 : 1));
+  if (nr <= 16) {
+    run_item<C, ACT, EPI, NF, 1, 1>(a, g, is_shared, row0, nr, ntw, red);
+  } else if (nr <= 32) {
+    if constexpr (MTMAX >= 2) run_item<C, ACT, EPI, NF, 2, 1>(a, g, is_shared, row0, nr, ntw, red);
+    else run_item<C, ACT, EPI, NF, 1, 2>(a, g, is_shared, row0, nr, ntw, red);
+  } else {
+    if constexpr (MTMAX >= 4) run_item<C, ACT, EPI, NF, 4, 1>(a, g, is_shared, row0, nr, ntw, red);
+    else if constexpr (MTMAX == 2) run_item<C, ACT, EPI, NF, 2, 2>(a, g, is_shared, row0, nr, ntw, red);
+    else run_item<C, ACT, EPI, NF, 1, 4>(a, g, is_shared, row0, nr, ntw, red);
   }
 }
 
@@ -322,11 +387,16 @@ __global__ void __launch_bounds__(256) grouped_decode_kernel(GroupedArgs a) {
   } else if (rbi * RB >= a.M) {
     return;
   }
+  const int rbeg = a.group_range ? a.group_range[2 * g] : 0;
+  const int rend = a.group_range ? a.group_range[2 * g + 1] : a.M;
+  const int row0 = rbeg + RB * blk;
+  const int nr = min(RB, rend - row0);
+  if (nr <= 0) return;
   const bool is_shared = g == a.shared_group;
   if (CR == CS || !is_shared)
-    run_item<CR, ACT, EPI, NF>(a, g, is_shared, blk, ntw, red);
+    run_rows<CR, ACT, EPI, NF, false>(a, g, is_shared, row0, nr, ntw, red);
   else
-    run_item<CS, ACT, EPI, NF>(a, g, is_shared, blk, ntw, red);
+    run_rows<CS, ACT, EPI, NF, true>(a, g, is_shared, row0, nr, ntw, red);
 }
 
 // ------------------------------------------------------------------------------------------
