@@ -97,6 +97,25 @@ int router_ksplit(const moe_shape& s) {
   return std::max(ks, 1);
 }
 
+// Router scores of many tokens run on the prefill kernel (256 x 256 MFMA tiles, x read once per
+// 256 experts), split along H so that about one workgroup per CU is busy; few tokens use the
+// decode kernel with router_ksplit.
+struct RouterPlan {
+  bool prefill;
+  int ksplit;
+};
+
+RouterPlan router_plan(const moe_shape& s) {
+  const int Ep = pad64(s.E);
+  if (s.T >= 2048 && prefill_scores_supported(s.act, s.H, Ep)) {
+    const int items = (s.T + 255) / 256 * (Ep / 256);
+    int ks = (256 + items - 1) / items;
+    ks = std::min(ks, std::max(1, s.H / 32 / 16));  // at least 16 reduction steps per part
+    return {true, std::max(ks, 1)};
+  }
+  return {false, router_ksplit(s)};
+}
+
 struct Ws {
   size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, h, y_perm,
       y_shared, total;
@@ -112,7 +131,7 @@ Ws ws_layout(const moe_shape& s) {
     o += up(bytes ? bytes : 1);
     return at;
   };
-  w.logits = take((size_t)router_ksplit(s) * s.T * pad64(s.E) * 4);
+  w.logits = take((size_t)router_plan(s).ksplit * s.T * pad64(s.E) * 4);
   w.idx = take(P * 4);
   w.w = take(P * 4);
   w.offsets = take(((size_t)s.E + 1) * 4);
@@ -173,8 +192,10 @@ moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const flo
   a.N = Ep;
   a.out = at<float>(ws, L.logits);
   a.ldo = Ep;
-  a.ksplit = router_ksplit(s);
-  hipError_t e = launch_grouped_decode(s.act, EPI_F32, s.act, s.act, a, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
+  const RouterPlan rp = router_plan(s);
+  a.ksplit = rp.ksplit;
+  hipError_t e = rp.prefill ? launch_prefill_scores(a, st)
+                            : launch_grouped_decode(s.act, EPI_F32, s.act, s.act, a, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
   if (e != hipSuccess) return hip_status(e, "router scores");
   e = launch_topk(at<float>(ws, L.logits), Ep, a.ksplit, bias, s.T, s.E, s.k, idx, w, st);
   return hip_status(e, "router top-k");

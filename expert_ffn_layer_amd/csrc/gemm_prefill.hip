@@ -157,33 +157,42 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ntn = a.NTW;  // full-item column tiles (even)
-  const int units = a.cum_blocks[a.G];  // 128-row blocks over all groups
-  const int total = units * (ntn >> 1);
+  const int ntn = a.NTW;  // full-item column tiles
+  // Grouped mode (a plan is given): group g has mt 128-row blocks, i.e. mt / 2 full items and a
+  // half item for an odd block, per pair of full-item column tiles (ntn is even). Single-group
+  // mode (no plan, the router scores): ceil(M / 256) full items per column tile.
+  const bool planned = a.cum_blocks != nullptr;
+  const int total = planned ? a.cum_blocks[a.G] * (ntn >> 1) : (a.M + PBM - 1) / PBM * ntn;
   // XCD-aware workgroup -> item map over the items that exist: XCD x (= blockIdx % 8) takes
   // items [x * per_xcd, (x + 1) * per_xcd)
   const int per_xcd = (total + NXCD - 1) / NXCD;
   if ((int)(blockIdx.x / NXCD) >= per_xcd) return;
   const int item = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
   if (item >= total) return;
-  int lo = 0, hi = a.G - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.cum_blocks[mid] * (ntn >> 1) <= item) lo = mid; else hi = mid - 1;
-  }
-  const int g = lo;
-  const int mt = a.cum_blocks[g + 1] - a.cum_blocks[g];  // 128-row blocks of the group
-  const int mtf = mt >> 1;                               // full row tiles
-  const int li = item - a.cum_blocks[g] * (ntn >> 1);
-  const bool half = li >= mtf * ntn;
-  int mtile, ntile;
-  if (half) {
-    mtile = mtf;
-    ntile = li - mtf * ntn;
+  int g = 0, mtile, ntile, rbeg = 0, rend = a.M;
+  bool half = false;
+  if (planned) {
+    int lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cum_blocks[mid] * (ntn >> 1) <= item) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int mt = a.cum_blocks[g + 1] - a.cum_blocks[g];  // 128-row blocks of the group
+    const int mtf = mt >> 1;                               // full row tiles
+    const int li = item - a.cum_blocks[g] * (ntn >> 1);
+    half = li >= mtf * ntn;
+    if (half) {
+      mtile = mtf;
+      ntile = li - mtf * ntn;
+    } else {
+      item_tiles(li, mtf, ntn, mtile, ntile);
+    }
+    rbeg = a.group_range[2 * g];
+    rend = a.group_range[2 * g + 1];
   } else {
-    item_tiles(li, mtf, ntn, mtile, ntile);
+    item_tiles(item, (a.M + PBM - 1) / PBM, ntn, mtile, ntile);
   }
-  const int rbeg = a.group_range[2 * g], rend = a.group_range[2 * g + 1];
   const int row0 = rbeg + mtile * PBM;
   const int nr = min(half ? PRB : PBM, rend - row0);
   const bool is_shared = g == a.shared_group;
@@ -192,7 +201,10 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   const float* s0 = (const float*)(is_shared ? a.sa_s : (a.sa_r ? a.sa_r + (size_t)g * a.scale_bytes : nullptr));
   const float* s1 = (const float*)(is_shared ? a.sb_s : (a.sb_r ? a.sb_r + (size_t)g * a.scale_bytes : nullptr));
   const int KT = a.K / KP;
-  const int nsteps = a.K / PBK;
+  // reduction steps of this workgroup: split-K part blockIdx.y of ksplit (fp32 partial outputs)
+  const int KSG = a.ksplit > 1 ? a.ksplit : 1;
+  const int kstep0 = (int)blockIdx.y * (a.K / PBK) / KSG;
+  const int nsteps = ((int)blockIdx.y + 1) * (a.K / PBK) / KSG - kstep0;
   const int j16 = lane & 15, g4 = lane >> 4;
 
   // this wave's place: row half and column slot within the item
@@ -248,7 +260,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     }
   }
   auto dma_one = [&](int q, int step) {
-    const int st = min(step, nsteps - 1);
+    const int st = kstep0 + min(step, nsteps - 1);
     __builtin_amdgcn_global_load_lds((const void*)(qsrc[q] + (size_t)st * qstride[q]),
                                      (lds_void*)(lds + (step % D) * STAGE_B + qdst[q]), 16, 0, 0);
   };
@@ -273,7 +285,8 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   constexpr int SPB = SCALED ? 128 / PBK : 1;  // pipeline steps per scale block
   float mcur[NMAT];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) mcur[m] = scale_mantissa(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), 0)));
+  for (int m = 0; m < NMAT; ++m)
+    mcur[m] = scale_mantissa(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), (kstep0 * PBK) >> 7)));
 
   auto step_body = [&](int step, auto first_of_block) {
     constexpr bool RESCALE = SCALED && decltype(first_of_block)::value;
@@ -285,7 +298,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     float sc[NMAT], rs[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-      sc[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), (step * PBK) >> 7));
+      sc[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), ((kstep0 + step) * PBK) >> 7));
       if constexpr (RESCALE) {
         const float mn = scale_mantissa(sc[m]);
         rs[m] = mcur[m] / mn;
@@ -352,6 +365,16 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     const int rr = wrow * 128 + j * 16 + j16;
     if (rr >= nr) continue;
     const size_t row = (size_t)((long long)row0 + rr + rowoff);
+    if constexpr (EPI == EPI_F32) {
+      // fp32 partial scores of split-K part blockIdx.y
+      const size_t prow = row + (size_t)blockIdx.y * a.M;
+#pragma unroll
+      for (int f = 0; f < WF; ++f) {
+        const int n = ftile[f] * 16 + 4 * g4;
+        *(f32x4*)(out + (prow * ldo + n) * 4) = acc[f][j];
+      }
+      continue;
+    }
 #pragma unroll
     for (int f = 0; f < WF; ++f) {
       const int n = ftile[f] * 16 + 4 * g4;
@@ -377,6 +400,24 @@ static hipError_t launch_p(const GroupedArgs& a, int max_units, hipStream_t st) 
 }
 
 int prefill_row_tile() { return PRB; }
+
+// Router scores of many tokens: x[M, K] (bf16) times the packed bf16 Wr[K, N] -> fp32
+// partials out[ksplit][M][ldo]; N a multiple of 256, K a multiple of 32.
+bool prefill_scores_supported(int act, int K, int N) {
+  return act == MOE_BF16 && K % PCodec<MOE_BF16>::PBK == 0 && K <= 64 * 128 && N % PEpi<EPI_F32>::FULL_F == 0;
+}
+
+hipError_t launch_prefill_scores(const GroupedArgs& a, hipStream_t st) {
+  if (a.cum_blocks || a.gather || !prefill_scores_supported(MOE_BF16, a.K, a.N)) return hipErrorInvalidValue;
+  GroupedArgs b = a;
+  b.NTW = a.N / PEpi<EPI_F32>::FULL_F;
+  long long n = (long long)(a.M + PBM - 1) / PBM * b.NTW;
+  n = (n + NXCD - 1) / NXCD * NXCD;
+  if (n == 0) return hipSuccess;
+  const int ks = a.ksplit > 1 ? a.ksplit : 1;
+  grouped_prefill_kernel<MOE_BF16, EPI_F32><<<dim3((unsigned)n, (unsigned)ks), PTHREADS, 0, st>>>(b);
+  return hipGetLastError();
+}
 
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down) {
   auto ok = [](int c) { return c == MOE_BF16 || c == MOE_FP8_E4M3_B128; };

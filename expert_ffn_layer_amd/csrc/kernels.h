@@ -51,7 +51,9 @@ inline int decode_nf(int codec, int epi, int K, int N) {
   if (epi == EPI_F32) return 1;
   const double bpw = codec == 0 ? 4.0 : codec == 1 ? 2.0 : codec == 2 ? 1.0 : 0.53125;
   const int nmat = epi == EPI_SWIGLU ? 2 : 1;
-  const int lo = epi == EPI_SWIGLU ? 1 : 2, hi = epi == EPI_SWIGLU ? 2 : 8;
+  // converted formats (fp8, MXFP4) stop at 4 tiles for the plain epilogue: their conversion
+  // temporaries make 8 tiles cost a wave of occupancy per SIMD, which streams slower
+  const int lo = epi == EPI_SWIGLU ? 1 : 2, hi = epi == EPI_SWIGLU ? 2 : (codec >= 2 ? 4 : 8);
   int nf = lo;
   while (nf < hi && 16.0 * nf * K * bpw * nmat < 128.0 * 1024 && N % (32 * nf) == 0) nf *= 2;
   return nf;
@@ -62,6 +64,8 @@ hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const Groupe
                                   hipStream_t st);
 int prefill_row_tile();
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down);
+bool prefill_scores_supported(int act, int K, int N);
+hipError_t launch_prefill_scores(const GroupedArgs& a, hipStream_t st);
 hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
                        int32_t* group_range, int32_t* cum_blocks, hipStream_t st);
 hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,

@@ -26,18 +26,34 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float NEG = -__builtin_huge_valf();
+  // split-K partial scores, summed in ascending part order; the loads of PB parts of every
+  // score are issued together, so the sum costs nparts / PB memory round trips, not nparts
+  constexpr int PB = 8;
   float v[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) v[j] = 0.0f;
+  const float* lt = logits + (size_t)t * ldl;
+  for (int p0 = 0; p0 < nparts; p0 += PB) {
+    float part[PB][PL];
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      const int p = min(p0 + q, nparts - 1);
+#pragma unroll
+      for (int j = 0; j < PL; ++j) {
+        const int e = min(lane + 64 * j, E - 1);
+        part[q][j] = lt[p * part_stride + e];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q)
+#pragma unroll
+      for (int j = 0; j < PL; ++j)
+        if (p0 + q < nparts) v[j] += part[q][j];
+  }
 #pragma unroll
   for (int j = 0; j < PL; ++j) {
     const int e = lane + 64 * j;
-    float s = NEG;
-    if (e < E) {
-      // split-K partial scores, summed in a fixed order
-      s = logits[(size_t)t * ldl + e];
-      for (int p = 1; p < nparts; ++p) s += logits[p * part_stride + (size_t)t * ldl + e];
-      if (bias) s += bias[e];
-    }
-    v[j] = s;
+    v[j] = e < E ? (bias ? v[j] + bias[e] : v[j]) : NEG;
   }
   int sel[TOPK_MAX];
   float sv[TOPK_MAX];

@@ -111,6 +111,9 @@ SMALL = [
     ("ragged-groups-fp8", L.LayerSpec("s9", T=520, H=1024, E=5, k=2, I=512, shared=True, w_routed="fp8",
                                       w_shared="fp8", router="zipf", zipf_alpha=0.8, calib_tokens=512,
                                       seed=39)),
+    # enough tokens for the router scores to run on the 256 x 256 MFMA tiles (split along H), with
+    # a ragged last row tile
+    ("many-tokens-router", L.LayerSpec("s10", T=2304, H=512, E=256, k=2, I=256, seed=40)),
 ]
 
 
