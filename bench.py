@@ -27,8 +27,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 # kernel of known size that --calib-copy appends. Keyed by workload; an entry holds only while
 # the kernel sources it was measured on are unchanged (sha256 of those files).
 TRAFFIC = {
-    "c2": {"sha": "9feeb668f9ef2a50", "bytes": 3177000000},  # gate/up decode kernel
-    "c5": {"sha": "ba3731e3ed1b87bb", "bytes": 17442000000},  # gate/up prefill kernel
+    "c2": {"sha": "9bd53d272c2b8ba1", "bytes": 3177000000},  # gate/up decode kernel
+    "c5": {"sha": "0d982f50a73d8e88", "bytes": 16323000000},  # gate/up prefill kernel
 }
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
