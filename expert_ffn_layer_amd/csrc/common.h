@@ -52,7 +52,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp) instead of an IEEE
+// division sequence; e^-z -> inf for very negative z gives z * 0 = -0, the right limit.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) {
