@@ -117,7 +117,7 @@ RouterPlan router_plan(const moe_shape& s) {
 }
 
 struct Ws {
-  size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, h, y_perm,
+  size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, zero, h, y_perm,
       y_shared, total;
 };
 
@@ -144,6 +144,7 @@ Ws ws_layout(const moe_shape& s) {
   w.h = take(R * s.I * ab);
   w.y_perm = take(P * s.H * ab);
   w.y_shared = take(S * s.T * s.H * ab);
+  w.zero = take((size_t)std::max(s.H, s.I) * ab);  // zero activations for prefill padding rows
   w.total = o;
   return w;
 }
@@ -248,13 +249,16 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   const bool prefill = use_prefill(s);
   const int rb = prefill ? prefill_row_tile() : ROW_BLOCK;
   hipError_t e = hipSuccess;
-  if (!plan_ready || prefill) e = launch_plan(off, s.E, P, s.T, S, rb, gr, cb, st);
+  uint32_t* zero = prefill ? at<uint32_t>(ws, L.zero) : nullptr;
+  const int zero_words = (int)((size_t)std::max(s.H, s.I) * act_bytes(s.act) / 4);
+  if (!plan_ready || prefill) e = launch_plan(off, s.E, P, s.T, S, rb, gr, cb, zero, zero_words, st);
   if (e != hipSuccess) return hip_status(e, "plan");
   moe_status rs;
   if (ev && (rs = record(ev[0], st)) != MOE_OK) return rs;
   const int max_rb = std::min(s.E, P) + (P + rb - 1) / rb + S * ((s.T + rb - 1) / rb);
 
   GroupedArgs a{};
+  a.zero_row = zero;
   a.group_range = gr;
   a.cum_blocks = cb;
   a.G = G;

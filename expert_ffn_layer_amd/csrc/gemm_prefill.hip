@@ -248,7 +248,11 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       const int r = row0 + (rr < nr ? rr : 0);
       int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
       if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
-      qsrc[q] = (const uint8_t*)a.act + (size_t)src * a.lda * 2 + Cd::dma_off(lane, h);
+      // rows past the group's end feed zeros when a zero row is given (their results are
+      // discarded either way; zero operands keep the padding MFMAs cheap in power)
+      const uint8_t* rowp = (rr >= nr && a.zero_row) ? (const uint8_t*)a.zero_row
+                                                      : (const uint8_t*)a.act + (size_t)src * a.lda * 2;
+      qsrc[q] = rowp + Cd::dma_off(lane, h);
       qdst[q] = (rt * H + h) * 1024;
       qstride[q] = PBK * 2;
     } else {

@@ -41,6 +41,7 @@ struct GroupedArgs {
   void* out_s;
   int ldo_s;
   int ksplit;  // > 1: fp32 output only; workgroup y sums K part y into out + y * M * ldo
+  const void* zero_row;  // prefill: K zero activations that rows past a group's end read, or null
 };
 
 // Output features (in units of 16) per decode work item, chosen from the instantiated set so an
@@ -67,7 +68,7 @@ bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down)
 bool prefill_scores_supported(int act, int K, int N);
 hipError_t launch_prefill_scores(const GroupedArgs& a, hipStream_t st);
 hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
-                       int32_t* group_range, int32_t* cum_blocks, hipStream_t st);
+                       int32_t* group_range, int32_t* cum_blocks, uint32_t* zero, int zero_words, hipStream_t st);
 hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
                        int32_t* idx, float* w, hipStream_t st);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,

@@ -143,12 +143,15 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 // Grouped-GEMM plan: the row range [begin, end) of each group (routed expert g from
 // expert_offsets, then the shared expert as group E with rows [P, P+T)), and the prefix count
 // of row blocks of rb rows per group. Offsets are clamped into [0, P] so malformed input
-// cannot produce rows outside the buffers.
+// cannot produce rows outside the buffers. It also clears `zero` (zero_words words): the zero
+// activations the prefill GEMM feeds to the padding rows of a group's last tile.
 // ------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ off, int E, int P, int T,
                                                      int shared, int rb, int32_t* __restrict__ group_range,
-                                                     int32_t* __restrict__ cum_blocks) {
+                                                     int32_t* __restrict__ cum_blocks, uint32_t* __restrict__ zero,
+                                                     int zero_words) {
   __shared__ int32_t blk[2048], tmp[2048];
+  for (int i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
   const int G = E + (shared ? 1 : 0);
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     int b0, b1;
@@ -170,9 +173,10 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 }
 
 hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
-                       int32_t* group_range, int32_t* cum_blocks, hipStream_t st) {
+                       int32_t* group_range, int32_t* cum_blocks, uint32_t* zero, int zero_words, hipStream_t st) {
   if (E + 1 > 2048) return hipErrorInvalidValue;
-  plan_kernel<<<1, 1024, 0, st>>>(expert_offsets, E, P, T, shared, rb, group_range, cum_blocks);
+  plan_kernel<<<1, 1024, 0, st>>>(expert_offsets, E, P, T, shared, rb, group_range, cum_blocks, zero,
+                                  zero ? zero_words : 0);
   return hipGetLastError();
 }
 
