@@ -81,7 +81,8 @@ moe_status check_shape(const moe_shape* s) {
       (!prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
        !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->I, s->I, s->H)))
     return fail(MOE_ERR_UNSUPPORTED,
-                "the prefill path needs BF16 activations and one BF16 or FP8 format for all experts");
+                "the prefill path needs BF16 activations, BF16 / FP8 / MXFP4 weights, I a multiple of 256 "
+                "and H a multiple of 512");
   return MOE_OK;
 }
 

@@ -46,6 +46,8 @@ struct PCodec<MOE_BF16> {
   static constexpr int PBK = 32;     // reduction elements per pipeline step
   static constexpr int H = 1;        // 32-deep MFMA steps per pipeline step
   static constexpr int PK = 1;       // packets per 16-column tile per pipeline step
+  static constexpr bool HALF_ONLY = false;  // every item 128 rows x 512 columns
+  static constexpr bool SCALE_DMA = false;  // per-packet scales reach LDS with the weights
   // Activation layout of one 16-row tile per step (H KiB of LDS): DMA unit u, lane l reads
   // 16 bytes of row dma_row(l, u) at byte dma_off(l, u) of the row's step slice and lands them
   // at u * 1024 + 16 * l; the B fragment of MFMA half h is the 16 bytes at read_off(l, h).
@@ -84,6 +86,8 @@ struct PCodec<MOE_FP8_E4M3_B128> {
   static constexpr int PBK = 64;
   static constexpr int H = 2;
   static constexpr int PK = 1;
+  static constexpr bool HALF_ONLY = false;
+  static constexpr bool SCALE_DMA = false;
   // Lane group g of a packet holds reduction elements 16g .. 16g + 15 and MFMA half h takes the
   // h-th run of 8 of them, so the B fragment of half h for lane (g, row j) is the 16-byte chunk
   // c = 2g + h of row j's 128-byte step slice. DMA unit u moves rows 8u .. 8u + 7 as whole
@@ -102,6 +106,45 @@ struct PCodec<MOE_FP8_E4M3_B128> {
   }
 };
 
+// 8 e2m1 codes (one dword, element 2b in the low nibble of byte b) -> 8 bf16 times 2^(E-127):
+// v_cvt_scalef32_pk_bf16_fp4 is exact here and applies the exponent of `scale`.
+__device__ __forceinline__ bf16x8 p_fp4x8(uint32_t w, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// MXFP4: a packet is 16 features x 128 reduction elements, lane (g, f) holding elements
+// 32g .. 32g + 31 as 4 dwords of 8 codes, with one e8m0 exponent per lane. A pipeline step
+// is one packet deep, so a 16-row activation tile is 16 rows x 256 bytes per step; to keep the
+// stage small every item is 128 rows x 512 columns (2 stages of 72 KiB). MFMA half h takes
+// dword h of each lane: elements 32g + 8h .. + 8, i.e. the 16-byte activation chunk
+// c = 4g + h of the row. DMA unit u moves rows 4u .. 4u + 3 (lane l: row 4u + l / 16, chunk
+// (l % 16) ^ row), so row r stores chunk c at position c ^ r: the XOR swizzle spreads every
+// read phase over all 64 LDS banks.
+template <>
+struct PCodec<MOE_MXFP4_B32> {
+  static constexpr int KP = 128;
+  static constexpr int PBK = 128;
+  static constexpr int H = 4;
+  static constexpr int PK = 1;
+  static constexpr bool HALF_ONLY = true;
+  static constexpr bool SCALE_DMA = true;
+  __device__ static int dma_row(int l, int u) { return 4 * u + (l >> 4); }
+  __device__ static int dma_off(int l, int u) { return 16 * ((l & 15) ^ (4 * u + (l >> 4))); }
+  __device__ static int read_off(int l, int h) {
+    const int j = l & 15, g = l >> 4;
+    return j * 256 + 16 * ((4 * g + h) ^ j);
+  }
+  __device__ static void frags(const u32x4 (&w)[PK], float s, bf16x8 (&a)[H]) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) a[h] = p_fp4x8(w[0][h], s);
+  }
+};
+
 template <int EPI>
 struct PEpi {
   static constexpr int NMAT = EPI == EPI_SWIGLU ? 2 : 1;
@@ -114,16 +157,21 @@ struct PLayout {
   using Cd = PCodec<C>;
   static constexpr int H = Cd::H, PK = Cd::PK;
   // per stage: activation fragments (16 row tiles x H for a full item, 8 x H for a half item)
-  // followed by weight packets (16 column tiles x PK, or 32 x PK), in KiB
+  // followed by weight packets (16 column tiles x PK, or 32 x PK), then (MXFP4) each wave's
+  // 1 KiB of packet scales; in KiB
   static constexpr int FULL_ACT = 16 * H, HALF_ACT = 8 * H;
   static constexpr int FULL_W = 16 * PK, HALF_W = 32 * PK;
-  static constexpr int STAGE_KIB = (FULL_ACT + FULL_W) > (HALF_ACT + HALF_W) ? (FULL_ACT + FULL_W)
-                                                                             : (HALF_ACT + HALF_W);
-  static constexpr int STAGES = 3;
+  static constexpr int SC_KIB = Cd::SCALE_DMA ? 8 : 0;
+  static constexpr int ITEM_KIB = (!Cd::HALF_ONLY && FULL_ACT + FULL_W > HALF_ACT + HALF_W) ? FULL_ACT + FULL_W
+                                                                                         : HALF_ACT + HALF_W;
+  static constexpr int SC_OFF = ITEM_KIB * 1024;
+  static constexpr int STAGE_KIB = ITEM_KIB + SC_KIB;
+  static constexpr int STAGES = Cd::HALF_ONLY ? 2 : 3;
   // DMA instructions per wave per stage; the shorter kind is padded with repeats of its last
   // load so both kinds issue the same count (the wait counts are compile-time)
-  static constexpr int LF = 2 * H + 2 * PK, LH = H + 4 * PK;
-  static constexpr int L = LF > LH ? LF : LH;
+  static constexpr int LF = Cd::HALF_ONLY ? 0 : 2 * H + 2 * PK, LH = H + 4 * PK;
+  static constexpr int L = (LF > LH ? LF : LH) + (Cd::SCALE_DMA ? 1 : 0);
+  static_assert(STAGES * STAGE_KIB <= 160, "LDS");
 };
 
 // (group-local full item) -> (row tile, column tile): runs of up to 8 column tiles over all
@@ -153,53 +201,71 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   constexpr int D = Ly::STAGES;
   constexpr int STAGE_B = Ly::STAGE_KIB * 1024;
   constexpr int L = Ly::L;
+  constexpr int QJ = (L + 7) / 8;  // DMA loads issued per row tile of a step
   __shared__ __attribute__((aligned(1024))) uint8_t lds[D * STAGE_B];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntn = a.NTW;  // full-item column tiles
   // Grouped mode (a plan is given): group g has mt 128-row blocks, i.e. mt / 2 full items and a
-  // half item for an odd block, per pair of full-item column tiles (ntn is even). Single-group
-  // mode (no plan, the router scores): ceil(M / 256) full items per column tile.
+  // half item for an odd block, per pair of full-item column tiles (ntn is even), or mt half
+  // items with HALF_ONLY; the launch covers groups [g_begin, g_end). Single-group mode (no plan,
+  // the router scores): ceil(M / 256) full items per column tile.
   const bool planned = a.cum_blocks != nullptr;
-  const int total = planned ? a.cum_blocks[a.G] * (ntn >> 1) : (a.M + PBM - 1) / PBM * ntn;
+  const int gb = planned && a.g_end > a.g_begin ? a.g_begin : 0;
+  const int ge = planned && a.g_end > a.g_begin ? a.g_end : a.G;
+  const int ibase = planned ? a.cum_blocks[gb] * (ntn >> 1) : 0;
+  const int total = planned ? a.cum_blocks[ge] * (ntn >> 1) - ibase : (a.M + PBM - 1) / PBM * ntn;
   // XCD-aware workgroup -> item map over the items that exist: XCD x (= blockIdx % 8) takes
   // items [x * per_xcd, (x + 1) * per_xcd)
   const int per_xcd = (total + NXCD - 1) / NXCD;
   if ((int)(blockIdx.x / NXCD) >= per_xcd) return;
   const int item = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
   if (item >= total) return;
-  int g = 0, mtile, ntile, rbeg = 0, rend = a.M;
+  int g = 0, row0, ntile, rbeg = 0, rend = a.M;
   bool half = false;
   if (planned) {
-    int lo = 0, hi = a.G - 1;
+    const int gi = item + ibase;
+    int lo = gb, hi = ge - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (a.cum_blocks[mid] * (ntn >> 1) <= item) lo = mid; else hi = mid - 1;
+      if (a.cum_blocks[mid] * (ntn >> 1) <= gi) lo = mid; else hi = mid - 1;
     }
     g = lo;
-    const int mt = a.cum_blocks[g + 1] - a.cum_blocks[g];  // 128-row blocks of the group
-    const int mtf = mt >> 1;                               // full row tiles
-    const int li = item - a.cum_blocks[g] * (ntn >> 1);
-    half = li >= mtf * ntn;
-    if (half) {
-      mtile = mtf;
-      ntile = li - mtf * ntn;
-    } else {
-      item_tiles(li, mtf, ntn, mtile, ntile);
-    }
     rbeg = a.group_range[2 * g];
     rend = a.group_range[2 * g + 1];
+    const int mt = a.cum_blocks[g + 1] - a.cum_blocks[g];  // 128-row blocks of the group
+    const int li = gi - a.cum_blocks[g] * (ntn >> 1);
+    if constexpr (Cd::HALF_ONLY) {
+      int blk;
+      item_tiles(li, mt, ntn >> 1, blk, ntile);
+      half = true;
+      row0 = rbeg + blk * PRB;
+    } else {
+      const int mtf = mt >> 1;  // full row tiles
+      int mtile;
+      half = li >= mtf * ntn;
+      if (half) {
+        mtile = mtf;
+        ntile = li - mtf * ntn;
+      } else {
+        item_tiles(li, mtf, ntn, mtile, ntile);
+      }
+      row0 = rbeg + mtile * PBM;
+    }
   } else {
+    int mtile;
     item_tiles(item, (a.M + PBM - 1) / PBM, ntn, mtile, ntile);
+    row0 = mtile * PBM;
   }
-  const int row0 = rbeg + mtile * PBM;
   const int nr = min(half ? PRB : PBM, rend - row0);
   const bool is_shared = g == a.shared_group;
   const uint8_t* w0 = is_shared ? a.wa_s : a.wa_r + (size_t)g * a.mat_bytes;
   const uint8_t* w1 = is_shared ? a.wb_s : (a.wb_r ? a.wb_r + (size_t)g * a.mat_bytes : nullptr);
-  const float* s0 = (const float*)(is_shared ? a.sa_s : (a.sa_r ? a.sa_r + (size_t)g * a.scale_bytes : nullptr));
-  const float* s1 = (const float*)(is_shared ? a.sb_s : (a.sb_r ? a.sb_r + (size_t)g * a.scale_bytes : nullptr));
+  const uint8_t* ws0 = is_shared ? a.sa_s : (a.sa_r ? a.sa_r + (size_t)g * a.scale_bytes : nullptr);
+  const uint8_t* ws1 = is_shared ? a.sb_s : (a.sb_r ? a.sb_r + (size_t)g * a.scale_bytes : nullptr);
+  const float* s0 = (const float*)ws0;
+  const float* s1 = (const float*)ws1;
   const int KT = a.K / KP;
   // reduction steps of this workgroup: split-K part blockIdx.y of ksplit (fp32 partial outputs)
   const int KSG = a.ksplit > 1 ? a.ksplit : 1;
@@ -236,12 +302,21 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   const uint8_t* qsrc[L];
   int qdst[L], qstride[L];
   const int wts_off = (half ? Ly::HALF_ACT : Ly::FULL_ACT) * 1024;
+  constexpr int LSC = Cd::SCALE_DMA ? 1 : 0;  // the last load moves the packet scales
 #pragma unroll
   for (int q = 0; q < L; ++q) {
     const int nact = half ? H : 2 * H;
     const int nw = half ? 4 * PK : 2 * PK;
     const int qq = q < nact + nw ? q : nact + nw - 1;
-    if (qq < nact) {
+    if (LSC && q == L - 1) {
+      // this wave's 4 column tiles' e8m0 bytes of the step's packets (64 per tile): lane l
+      // fetches 16 bytes of tile (l % 16) / 4; lanes 16..63 repeat lanes 0..15
+      const int t = (lane & 15) >> 2;
+      const uint8_t* sp = t / WF == 0 ? ws0 : ws1;
+      qsrc[q] = sp + ((size_t)(gw * WF + t % WF) * KT) * 64 + (size_t)(lane & 3) * 16;
+      qdst[q] = Ly::SC_OFF + wave * 1024;
+      qstride[q] = PK * 64;
+    } else if (qq < nact) {
       const int i = qq / H, h = qq % H;
       const int rt = half ? wave : 2 * wave + i;
       const int rr = rt * 16 + Cd::dma_row(lane, h);
@@ -315,7 +390,9 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       u32x4 pk[PK];
 #pragma unroll
       for (int p = 0; p < PK; ++p) pk[p] = *(const u32x4*)(base + wbase + (t * PK + p) * 1024);
-      Cd::frags(pk, sc[t / WF], af[t]);
+      float st = sc[t / WF];
+      if constexpr (Cd::SCALE_DMA) st = __uint_as_float((uint32_t)base[Ly::SC_OFF + wave * 1024 + t * 64 + lane] << 23);
+      Cd::frags(pk, st, af[t]);
     }
     // the next stage's DMA is spread over the MFMA stream, one load per row tile, so the
     // loads never queue up in front of the matrix work
@@ -340,7 +417,9 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][h], b[h], acc[t][j], 0, 0, 0);
-      if (j < L) dma_one(j, step + D - 1);
+#pragma unroll
+      for (int u = 0; u < QJ; ++u)
+        if (j * QJ + u < L) dma_one(j * QJ + u, step + D - 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -403,6 +482,14 @@ static hipError_t launch_p(const GroupedArgs& a, int max_units, hipStream_t st) 
   return hipGetLastError();
 }
 
+template <int EPI>
+static hipError_t launch_codec(int c, const GroupedArgs& a, int max_units, hipStream_t st) {
+  if (c == MOE_BF16) return launch_p<MOE_BF16, EPI>(a, max_units, st);
+  if (c == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI>(a, max_units, st);
+  if (c == MOE_MXFP4_B32) return launch_p<MOE_MXFP4_B32, EPI>(a, max_units, st);
+  return hipErrorInvalidValue;
+}
+
 int prefill_row_tile() { return PRB; }
 
 // Router scores of many tokens: x[M, K] (bf16) times the packed bf16 Wr[K, N] -> fp32
@@ -423,26 +510,39 @@ hipError_t launch_prefill_scores(const GroupedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+static bool prefill_codec_ok(int c, int K) {
+  int pbk = 0;
+  if (c == MOE_BF16) pbk = PCodec<MOE_BF16>::PBK;
+  else if (c == MOE_FP8_E4M3_B128) pbk = PCodec<MOE_FP8_E4M3_B128>::PBK;
+  else if (c == MOE_MXFP4_B32) pbk = PCodec<MOE_MXFP4_B32>::PBK;
+  else return false;
+  return K % pbk == 0 && K % 128 == 0 && K <= 64 * 128;
+}
+
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down) {
-  auto ok = [](int c) { return c == MOE_BF16 || c == MOE_FP8_E4M3_B128; };
-  const int pbk = cr == MOE_BF16 ? PCodec<MOE_BF16>::PBK : PCodec<MOE_FP8_E4M3_B128>::PBK;
-  return act == MOE_BF16 && ok(cr) && cr == cs && K % pbk == 0 && K % 128 == 0 && K <= 64 * 128 &&
+  return act == MOE_BF16 && prefill_codec_ok(cr, K) && prefill_codec_ok(cs, K) &&
          N_gateup % (2 * PEpi<EPI_SWIGLU>::FULL_F) == 0 && N_down % (2 * PEpi<EPI_PLAIN>::FULL_F) == 0;
 }
 
+// One launch over all groups when routed and shared experts share a format; else one launch
+// per format, over the routed groups [0, shared_group) and over the shared group.
 hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const GroupedArgs& a, int max_units,
                                   hipStream_t st) {
-  if (act != MOE_BF16 || cr != cs || a.K % 128 != 0) return hipErrorInvalidValue;
-  if (epi == EPI_SWIGLU) {
-    if (a.N % (2 * PEpi<EPI_SWIGLU>::FULL_F)) return hipErrorInvalidValue;
-    if (cr == MOE_BF16) return launch_p<MOE_BF16, EPI_SWIGLU>(a, max_units, st);
-    if (cr == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI_SWIGLU>(a, max_units, st);
-  } else if (epi == EPI_PLAIN) {
-    if (a.N % (2 * PEpi<EPI_PLAIN>::FULL_F)) return hipErrorInvalidValue;
-    if (cr == MOE_BF16) return launch_p<MOE_BF16, EPI_PLAIN>(a, max_units, st);
-    if (cr == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI_PLAIN>(a, max_units, st);
-  }
-  return hipErrorInvalidValue;
+  if (act != MOE_BF16 || !prefill_codec_ok(cr, a.K) || !prefill_codec_ok(cs, a.K)) return hipErrorInvalidValue;
+  if (epi != EPI_SWIGLU && epi != EPI_PLAIN) return hipErrorInvalidValue;
+  if (a.N % (2 * (epi == EPI_SWIGLU ? PEpi<EPI_SWIGLU>::FULL_F : PEpi<EPI_PLAIN>::FULL_F))) return hipErrorInvalidValue;
+  auto launch = [&](int c, const GroupedArgs& b, int units) {
+    return epi == EPI_SWIGLU ? launch_codec<EPI_SWIGLU>(c, b, units, st) : launch_codec<EPI_PLAIN>(c, b, units, st);
+  };
+  if (cr == cs || a.shared_group < 0) return launch(cr, a, max_units);
+  GroupedArgs r = a, sh = a;
+  r.g_begin = 0;
+  r.g_end = a.shared_group;
+  sh.g_begin = a.shared_group;
+  sh.g_end = a.shared_group + 1;
+  hipError_t e = launch(cr, r, max_units);
+  if (e != hipSuccess) return e;
+  return launch(cs, sh, (a.M - a.P + PRB - 1) / PRB);
 }
 
 }  // namespace moe

@@ -42,6 +42,7 @@ struct GroupedArgs {
   int ldo_s;
   int ksplit;  // > 1: fp32 output only; workgroup y sums K part y into out + y * M * ldo
   const void* zero_row;  // prefill: K zero activations that rows past a group's end read, or null
+  int g_begin, g_end;    // prefill: groups of this launch (g_end <= g_begin: all groups)
 };
 
 // Output features (in units of 16) per decode work item, chosen from the instantiated set so an

@@ -58,9 +58,12 @@ typedef enum {
 } moe_dtype;
 
 typedef enum {
-  MOE_PATH_AUTO = 0,      /* pick by the average rows per expert */
+  MOE_PATH_AUTO = 0,      /* prefill when T * k >= 64 * E and the prefill kernel takes the
+                             shape, else decode */
   MOE_PATH_DECODE = 1,    /* weight-streaming grouped GEMM (few rows per expert) */
-  MOE_PATH_PREFILL = 2    /* LDS-tiled MFMA grouped GEMM (many rows per expert) */
+  MOE_PATH_PREFILL = 2    /* LDS-tiled MFMA grouped GEMM (many rows per expert): BF16
+                             activations, BF16 / FP8 / MXFP4 weights, I a multiple of 256, H a
+                             multiple of 512; MOE_ERR_UNSUPPORTED otherwise */
 } moe_path;
 
 typedef struct {

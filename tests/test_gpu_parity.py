@@ -114,19 +114,29 @@ SMALL = [
     # enough tokens for the router scores to run on the 256 x 256 MFMA tiles (split along H), with
     # a ragged last row tile
     ("many-tokens-router", L.LayerSpec("s10", T=2304, H=512, E=256, k=2, I=256, seed=40)),
+    # MXFP4 routed experts in the prefill kernel, with a bf16 shared expert (one launch per
+    # format) and with an MXFP4 one; fp8 routed with a bf16 shared expert
+    ("mxfp4-bf16-prefill", L.LayerSpec("s11", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="mxfp4",
+                                       w_shared="bf16", router="zipf", zipf_alpha=1.0, calib_tokens=512,
+                                       seed=41)),
+    ("mxfp4-prefill", L.LayerSpec("s12", T=520, H=1024, E=5, k=2, I=512, shared=True, w_routed="mxfp4",
+                                  w_shared="mxfp4", seed=42)),
+    ("fp8-bf16-prefill", L.LayerSpec("s13", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="fp8",
+                                     w_shared="bf16", seed=43)),
 ]
 
 
 def _prefill_ok(spec):
-    return (spec.act == "bf16" and spec.w_routed in ("bf16", "fp8")
-            and (not spec.shared or spec.w_shared == spec.w_routed) and spec.I % 256 == 0 and spec.H % 512 == 0)
+    fmts = ("bf16", "fp8", "mxfp4")
+    return (spec.act == "bf16" and spec.w_routed in fmts and (not spec.shared or spec.w_shared in fmts)
+            and spec.I % 256 == 0 and spec.H % 512 == 0)
 
 
 @pytest.mark.parametrize("name,spec", SMALL, ids=[s[0] for s in SMALL])
 @pytest.mark.parametrize("path", ["auto", "decode", "prefill"])
 def test_layer_small(name, spec, path):
     if path == "prefill" and not _prefill_ok(spec):
-        pytest.skip("the prefill kernel takes bf16 activations and one bf16/fp8 weight format")
+        pytest.skip("the prefill kernel takes bf16 activations, I % 256 == 0 and H % 512 == 0")
     say("layer", name, path, spec)
     lay, pl = build(spec, DEV, path)
     y, idx, w = run(spec, lay, pl)
@@ -231,7 +241,10 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
 
 # ------------------------------------------------------------------ full-size layers
 
-FULL = ["c2", "c3", "c4", "c5"]
+FULL = ["c2", "c3", "c4", "c5", "v4pro-prefill"]
+# the DeepSeek-V4-Pro-shaped layer at a prefill batch: MXFP4 routed experts in the prefill
+# kernel, the bf16 shared expert in a launch of its own
+EXTRA = {"v4pro-prefill": L.CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096)}
 
 
 @pytest.mark.slow
@@ -239,7 +252,7 @@ FULL = ["c2", "c3", "c4", "c5"]
 def test_full_size_layer(cfg):
     """The bench's launch configuration at full size: routing and permutation identical for
     every token, outputs against the oracle on sampled tokens."""
-    spec = L.CONFIGS[cfg]
+    spec = L.CONFIGS[cfg] if cfg in L.CONFIGS else EXTRA[cfg]
     say("full-size", cfg, spec)
     lay, pl = build(spec, DEV)
     y, idx, w = run(spec, lay, pl)
