@@ -68,6 +68,7 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read HBM ceiling")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
                     help="end with one plain copy kernel of this size (byte-counter calibration)")
     args = ap.parse_args()
@@ -141,6 +142,21 @@ def main():
     stage_ms = acc / args.steps
     timed_ms = sum(evs[0].elapsed_time(evs[-1]) for evs in evsets) / args.steps
 
+    ceiling = None
+    if not args.no_ceiling:
+        # the achievable HBM read rate on this GPU: a plain streaming read of 4 GiB, 5 times
+        buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        G.stream_read(buf, sink)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            G.stream_read(buf, sink)
+        c1.record()
+        torch.cuda.synchronize()
+        ceiling = round(5 * buf.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
+        del buf
+
     if args.calib_copy:
         # one plain copy of known size, the reference that scales the byte counters of a --pmc run
         nb = args.calib_copy << 20
@@ -170,7 +186,8 @@ def main():
         ach = gu_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic_b, "kernel": "gate/up grouped GEMM",
-                "per_launch": {"bytes": gu_bytes, "ms": round(gu_ms, 4)}}
+                "per_launch": {"bytes": gu_bytes, "ms": round(gu_ms, 4)},
+                "frac_of_read_ceiling": round(ach / ceiling, 4) if ceiling else None}
 
     out = {
         "metric": METRIC,
@@ -198,6 +215,7 @@ def main():
         "timed_entry_ms_per_step": round(timed_ms, 4),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
+        "hbm_read_ceiling_GBps": ceiling,
         "cpu_baseline": None,
     }
 

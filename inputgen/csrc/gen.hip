@@ -203,9 +203,34 @@ __global__ void __launch_bounds__(256) copy16_kernel(const uint4* __restrict__ s
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// A plain streaming read (16 bytes per lane, non-temporal, each byte once): the achievable HBM
+// read rate that kernel bandwidths are compared with.
+typedef __attribute__((ext_vector_type(4))) unsigned v4u;
+__global__ void __launch_bounds__(256) stream_read_kernel(const v4u* __restrict__ src, long long n16,
+                                                          unsigned* __restrict__ sink) {
+  const long long stride = (long long)gridDim.x * 256 * 8;
+  unsigned acc = 0;
+  for (long long i = (long long)blockIdx.x * 256 * 8 + threadIdx.x; i < n16; i += stride) {
+    v4u v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = i + u * 256 < n16 ? __builtin_nontemporal_load(src + i + u * 256) : v4u{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never stores
+}
+
 }  // namespace
 
 extern "C" {
+
+// Reads src[0, bytes) once (bytes a multiple of 16); sink: one writable uint32.
+int gen_stream_read(const void* src, long long bytes, void* sink, hipStream_t st) {
+  if (bytes % 16 || (uintptr_t)src % 16) return -1;
+  if (!bytes) return 0;
+  stream_read_kernel<<<4096, 256, 0, st>>>((const v4u*)src, bytes / 16, (unsigned*)sink);
+  return (int)hipGetLastError();
+}
 
 // dst[0, bytes) <- src[0, bytes); bytes a multiple of 16, both pointers 16-byte aligned.
 int gen_copy(const void* src, void* dst, long long bytes, hipStream_t st) {

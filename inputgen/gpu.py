@@ -43,6 +43,7 @@ def lib():
         _lib.gen_fill_fp8.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_fill_mxfp4.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_copy.argtypes = [p, p, i64, p]
+        _lib.gen_stream_read.argtypes = [p, i64, p, p]
     return _lib
 
 
@@ -70,6 +71,13 @@ def copy(src, dst):
     n = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() >= n
     _chk(lib().gen_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, _stream()), "copy")
+
+
+def stream_read(src, sink):
+    """One plain streaming read of all of src (the achievable HBM read rate)."""
+    n = src.numel() * src.element_size()
+    _chk(lib().gen_stream_read(ctypes.c_void_p(src.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()), _stream()),
+         "stream_read")
 
 
 def fill_dense(out, fmt: str, seed: int, tid: int, stream0: int, count: int, n: int, start: int = 0,
