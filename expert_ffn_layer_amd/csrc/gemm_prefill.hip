@@ -443,6 +443,38 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     ldo = a.ldo;
     rowoff = 0;
   }
+  if constexpr (EPI == EPI_PLAIN) {
+    // The plain epilogue writes 64 columns x 128 rows of bf16 per wave: through LDS, 64 rows at
+    // a time (rows of EPS bytes, padded so the 16 lanes of a write phase hit distinct banks),
+    // then out as 16 bytes per lane, one 128-byte line per row, instead of 8-byte pieces.
+    constexpr int EPS = 136;
+    static_assert(8 * 64 * EPS <= D * STAGE_B, "epilogue staging exceeds the LDS ring");
+    __syncthreads();  // every wave is done with the ring
+    uint8_t* ep = lds + wave * 64 * EPS;
+    const int col0 = ftile[0] * 16;  // this wave's 64 consecutive output columns
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int f = 0; f < WF; ++f) {
+          const f32x4 v = acc[f][4 * hh + j];
+          *(u32x2*)(ep + (j * 16 + j16) * EPS + (f * 16 + 4 * g4) * 2) =
+              u32x2{pack_bf16x2(v[0] * mcur[0], v[1] * mcur[0]), pack_bf16x2(v[2] * mcur[0], v[3] * mcur[0])};
+        }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = k * 8 + (lane >> 3);
+        const int rr = wrow * 128 + hh * 64 + r;
+        const u32x4 v = *(const u32x4*)(ep + r * EPS + (lane & 7) * 16);
+        if (rr < nr) {
+          const size_t row = (size_t)((long long)row0 + rr + rowoff);
+          *(u32x4*)(out + (row * ldo + col0) * 2 + (lane & 7) * 16) = v;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int rr = wrow * 128 + j * 16 + j16;
