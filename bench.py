@@ -27,8 +27,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 # kernel of known size that --calib-copy appends. Keyed by workload; an entry holds only while
 # the kernel sources it was measured on are unchanged (sha256 of those files).
 TRAFFIC = {
-    "c2": {"sha": "9bd53d272c2b8ba1", "bytes": 3177000000},  # gate/up decode kernel
-    "c5": {"sha": "0d982f50a73d8e88", "bytes": 16323000000},  # gate/up prefill kernel
+    "c2": {"sha": "d19114cde11b4a36", "bytes": 3176825079},  # gate/up decode kernel
+    "c5": {"sha": "1b2179f3108af01c", "bytes": 16404419934},  # gate/up prefill kernel
 }
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
@@ -74,7 +74,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard "
-              "by experts across GPUs; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "by experts across GPUs, each GPU running this same path on its share). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
