@@ -380,7 +380,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       sc[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), ((kstep0 + step) * PBK) >> 7));
       if constexpr (RESCALE) {
         const float mn = scale_mantissa(sc[m]);
-        rs[m] = mcur[m] / mn;
+        rs[m] = mcur[m] * __builtin_amdgcn_rcpf(mn);  // m ratio in (0.5, 2), about 1 ulp
         mcur[m] = mn;
       }
     }
