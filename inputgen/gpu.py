@@ -91,6 +91,7 @@ def fill_dense(out, fmt: str, seed: int, tid: int, stream0: int, count: int, n: 
 
 def alloc_matrices(fmt: str, count: int, K: int, N: int, device):
     """Stored-format device tensors for `count` K x N matrices: (codes, scales or None)."""
+    fmt = "mxfp4" if fmt == "mxfp4a8" else fmt  # W4A8 stores MXFP4 weights
     import torch
     if fmt == "f32":
         return torch.empty((count, K, N), dtype=torch.float32, device=device), None
@@ -106,6 +107,7 @@ def alloc_matrices(fmt: str, count: int, K: int, N: int, device):
 
 
 def fill_matrices(codes, scales, fmt: str, seed: int, tid: int, stream0: int, K: int, N: int, fan_in: int):
+    fmt = "mxfp4" if fmt == "mxfp4a8" else fmt  # W4A8 stores MXFP4 weights
     count = codes.shape[0]
     T, TT = _tabs(codes.device)
     s = L.sigma(fan_in)

@@ -20,6 +20,8 @@ Stored formats (logical row-major, the layout in which the pages write the matri
 * ``fp8``  : uint8[K, N] OCP E4M3FN codes + float32[K/128, N/128] scales (w = code * s)
 * ``mxfp4``: uint8[K, N/2] e2m1 codes (even column in the low nibble) + uint8[K/32, N] e8m0
   exponents (w = e2m1 * 2^(E-127), one exponent per 32 consecutive K of a column)
+* ``mxfp4a8``: stored as ``mxfp4``; the layer quantises the routed experts' activations to MXFP8
+  for their products (W4A8)
 
 with (K, N) = (H, I) for gate and up and (I, H) for down.
 
@@ -44,7 +46,7 @@ TID_ROUTED = {"gate": 16, "up": 17, "down": 18}
 TID_SHARED = {"gate": 24, "up": 25, "down": 26}
 
 ACT_DTYPES = ("f32", "bf16")
-W_DTYPES = ("f32", "bf16", "fp8", "mxfp4")
+W_DTYPES = ("f32", "bf16", "fp8", "mxfp4", "mxfp4a8")
 
 
 @dataclass(frozen=True)
@@ -125,7 +127,7 @@ def store_matrix(w: np.ndarray, fmt: str) -> dict:
     if fmt == "fp8":
         c, s = px.quantize_fp8_block128(w)
         return {"w": c, "scale": s}
-    if fmt == "mxfp4":
+    if fmt in ("mxfp4", "mxfp4a8"):
         c, s = px.quantize_mxfp4_k32(w)
         return {"w": c, "scale": s}
     raise ValueError(fmt)

@@ -12,6 +12,8 @@
  *   fp8   uint8[K][N] OCP E4M3FN + float[K/128][N/128]   (w = e4m3(code) * s)
  *   mxfp4 uint8[K][N/2] e2m1, even n in the low nibble + uint8[K/32][N] e8m0
  *                                                        (w = e2m1(code) * 2^(E-127))
+ *   mxfp4a8  stored as mxfp4; the routed experts' activations are quantised to MXFP8 before
+ *            each of their products (W4A8, see oracle_mxfp8_quantize)
  *
  * What it computes, step by step (sources: "AI infra book, ch. 6 Supernodes" (bojieli.github.io
  * ai-infra-book ch. 6) = [ch6]; "DeepSeek-V4-Pro on NVIDIA H200" report = [V4]):
@@ -31,7 +33,10 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_MXFP4_A8 = 4 };
+
+/* storage format of a weight format (W4A8 stores its weights as MXFP4) */
+static int stored(int fmt) { return fmt == OR_MXFP4_A8 ? OR_MXFP4 : fmt; }
 
 /* ---------------------------------------------------------------------------------------- */
 /* decoders                                                                                  */
@@ -76,7 +81,7 @@ static double act_at(const void* p, int act, size_t i) {
 /* Element W[k][n] of a stored K x N matrix. */
 static double w_at(const void* w, const void* scale, int fmt, int K, int N, int k, int n) {
   size_t i = (size_t)k * N + n;
-  switch (fmt) {
+  switch (stored(fmt)) {
     case OR_F32: return (double)((const float*)w)[i];
     case OR_BF16: return oracle_decode_bf16(((const uint16_t*)w)[i]);
     case OR_FP8: {
@@ -95,7 +100,7 @@ static double w_at(const void* w, const void* scale, int fmt, int K, int N, int 
 
 /* Bytes of one stored K x N matrix and of its scales. */
 static size_t w_bytes(int fmt, int K, int N) {
-  switch (fmt) {
+  switch (stored(fmt)) {
     case OR_F32: return (size_t)K * N * 4;
     case OR_BF16: return (size_t)K * N * 2;
     case OR_FP8: return (size_t)K * N;
@@ -104,7 +109,7 @@ static size_t w_bytes(int fmt, int K, int N) {
   return 0;
 }
 static size_t s_bytes(int fmt, int K, int N) {
-  switch (fmt) {
+  switch (stored(fmt)) {
     case OR_FP8: return (size_t)(K / 128) * (N / 128) * 4;
     case OR_MXFP4: return (size_t)(K / 32) * N;
   }
@@ -218,24 +223,98 @@ int oracle_permute(int T, int k, int E, const int32_t* topk_idx, int32_t* expert
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* ---------------------------------------------------------------------------------------- */
+/* W4A8: activations quantised to MXFP8 for the routed experts' products                     */
+/*                                                                                          */
+/* [CANN] "CANN DeepSeek-V4推理优化", quantisation strategy: the routed experts' linear layers */
+/* run W4A8, 4-bit weights times 8-bit activations. The 8-bit activation format read here is */
+/* OCP MXFP8 (OCP Microscaling Formats v1.0): each run of 32 consecutive reduction elements   */
+/* shares an e8m0 exponent X = floor(log2 max|v|) - 8 (8 is the largest E4M3 exponent),      */
+/* clamped to [-127, 127] and -127 for an all-zero run; each element is stored as           */
+/* E4M3FN(v / 2^X), rounded to nearest even and saturated at +-448.                         */
+/* ---------------------------------------------------------------------------------------- */
+
+/* E4M3FN code of v, round to nearest even, saturating (the sign of v, zero included, kept). */
+static uint8_t e4m3_encode(double v) {
+  const uint8_t s = signbit(v) ? 0x80 : 0;
+  const double a = fabs(v);
+  if (!(a < 448.0)) return s | 0x7E;
+  if (a < ldexp(1.0, -6)) return s | (uint8_t)nearbyint(ldexp(a, 9)); /* grid 2^-9; 8 -> 0x08 */
+  int e = ilogb(a);                                                    /* -6 .. 8 */
+  double m = nearbyint((ldexp(a, -e) - 1.0) * 8.0);                    /* 0 .. 8 */
+  if (m == 8.0) {
+    e += 1;
+    m = 0.0;
+  }
+  int code = ((e + 7) << 3) | (int)m;
+  if (code > 0x7E) code = 0x7E; /* 464 <= a < 480 would round to the NaN pattern */
+  return s | (uint8_t)code;
+}
+
+/* K values (K a multiple of 32) -> K E4M3FN codes and K/32 e8m0 exponents. */
+int oracle_mxfp8_quantize(int K, const double* v, uint8_t* codes, uint8_t* scales) {
+  if (K % 32) return 1;
+  for (int b = 0; b < K / 32; ++b) {
+    double amax = 0.0;
+    for (int j = 0; j < 32; ++j) amax = fmax(amax, fabs(v[32 * b + j]));
+    int X = amax > 0.0 ? ilogb(amax) - 8 : -127;
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+    scales[b] = (uint8_t)(X + 127);
+    for (int j = 0; j < 32; ++j) codes[32 * b + j] = e4m3_encode(ldexp(v[32 * b + j], -X));
+  }
+  return 0;
+}
+
+/* v -> the value its MXFP8 encoding stands for (quantise, then decode), in place. */
+static int mxfp8_roundtrip(int K, double* v) {
+  uint8_t* c = (uint8_t*)malloc(K);
+  uint8_t* e = (uint8_t*)malloc(K / 32 + 1);
+  int rc = (!c || !e) ? 2 : oracle_mxfp8_quantize(K, v, c, e);
+  for (int i = 0; i < K && !rc; ++i) v[i] = oracle_decode_e4m3fn(c[i]) * oracle_decode_e8m0(e[i / 32]);
+  free(c);
+  free(e);
+  return rc;
+}
+
+/* v rounded to the nearest bfloat16 (8 significant bits), ties to even. */
+static double bf16_round(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e = ilogb(v);
+  if (e < -126) e = -126;
+  return ldexp(nearbyint(ldexp(v, 7 - e)), e - 7);
+}
+
+/* W4A8 (fmt mxfp4a8): the row is quantised to MXFP8 before gate/up; h = SiLU(g) * v is rounded
+ * to bf16, the type the layer keeps it in between the two products, then quantised to MXFP8
+ * before down. Other formats multiply the rows as given. */
 int oracle_expert_ffn(int H, int I, int M, int fmt, const void* wg, const void* sg,
                       const void* wu, const void* su, const void* wd, const void* sd,
                       const double* u, double* y) {
   int bad = 0;
+  const int a8 = fmt == OR_MXFP4_A8;
 #pragma omp parallel for schedule(dynamic, 1) if (M > 1)
   for (int m = 0; m < M; ++m) {
     double* g = (double*)malloc(sizeof(double) * I);
     double* v = (double*)malloc(sizeof(double) * I);
-    if (!g || !v) {
+    double* uq = (double*)malloc(sizeof(double) * H);
+    if (!g || !v || !uq) {
       bad = 1;
     } else {
-      oracle_row_matmul(H, I, fmt, wg, sg, u + (size_t)m * H, g);
-      oracle_row_matmul(H, I, fmt, wu, su, u + (size_t)m * H, v);
+      memcpy(uq, u + (size_t)m * H, sizeof(double) * H);
+      if (a8 && mxfp8_roundtrip(H, uq)) bad = 1;
+      oracle_row_matmul(H, I, fmt, wg, sg, uq, g);
+      oracle_row_matmul(H, I, fmt, wu, su, uq, v);
       for (int i = 0; i < I; ++i) g[i] = silu(g[i]) * v[i];
+      if (a8) {
+        for (int i = 0; i < I; ++i) g[i] = bf16_round(g[i]);
+        if (mxfp8_roundtrip(I, g)) bad = 1;
+      }
       oracle_row_matmul(I, H, fmt, wd, sd, g, y + (size_t)m * H);
     }
     free(g);
     free(v);
+    free(uq);
   }
   return bad ? 2 : 0;
 }

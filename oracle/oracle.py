@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "moe_oracle.c")
 LIB = os.path.join(HERE, "libmoe_oracle.so")
 
-FMT = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3}
+FMT = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "mxfp4a8": 4}
 
 _lib = None
 
@@ -44,6 +44,7 @@ def lib() -> ctypes.CDLL:
             getattr(_lib, name).restype = d
             getattr(_lib, name).argtypes = [ctypes.c_uint8]
         _lib.oracle_decode_matrix.argtypes = [i, i, i, p, p, p]
+        _lib.oracle_mxfp8_quantize.argtypes = [i, p, p, p]
         _lib.oracle_row_matmul.argtypes = [i, i, i, p, p, p, p]
         _lib.oracle_route.argtypes = [i, i, i, i, i, p, p, p, p, p, p]
         _lib.oracle_permute.argtypes = [i, i, i, p, p, p, p]
@@ -67,17 +68,30 @@ def _check(rc, what):
 
 
 def _wdtype(fmt):
-    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "mxfp4": np.uint8}[fmt]
+    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "mxfp4": np.uint8,
+            "mxfp4a8": np.uint8}[fmt]
 
 
 def _sdtype(fmt):
-    return {"fp8": np.float32, "mxfp4": np.uint8}.get(fmt)
+    return {"fp8": np.float32, "mxfp4": np.uint8, "mxfp4a8": np.uint8}.get(fmt)
 
 
 def decode_scalar(fmt: str, code: int) -> float:
     f = {"bf16": "oracle_decode_bf16", "e4m3fn": "oracle_decode_e4m3fn",
          "e2m1": "oracle_decode_e2m1", "e8m0": "oracle_decode_e8m0"}[fmt]
     return getattr(lib(), f)(code)
+
+
+def mxfp8_quantize(v):
+    """v[..., K] (K a multiple of 32) -> (E4M3FN codes uint8[..., K], e8m0 uint8[..., K/32])."""
+    v = _c(v, np.float64)
+    K = v.shape[-1]
+    rows = v.reshape(-1, K)
+    codes = np.empty(rows.shape, np.uint8)
+    scales = np.empty((rows.shape[0], K // 32), np.uint8)
+    for r in range(rows.shape[0]):
+        _check(lib().oracle_mxfp8_quantize(K, _ptr(rows[r]), _ptr(codes[r]), _ptr(scales[r])), "mxfp8")
+    return codes.reshape(v.shape), scales.reshape(v.shape[:-1] + (K // 32,))
 
 
 def decode_matrix(fmt: str, K: int, N: int, w, scale=None) -> np.ndarray:
@@ -92,7 +106,7 @@ def row_matmul(u, w, fmt: str = "f32", scale=None) -> np.ndarray:
     u = _c(u, np.float64)
     K = u.shape[0]
     w = _c(w, _wdtype(fmt))
-    N = w.shape[1] * (2 if fmt == "mxfp4" else 1)
+    N = w.shape[1] * (2 if fmt in ("mxfp4", "mxfp4a8") else 1)
     out = np.empty(N, np.float64)
     scale = _c(scale, _sdtype(fmt)) if _sdtype(fmt) else None
     _check(lib().oracle_row_matmul(K, N, FMT[fmt], _ptr(w), _ptr(scale), _ptr(u), _ptr(out)),
@@ -130,7 +144,7 @@ def expert_ffn(u, wts: dict, fmt: str) -> np.ndarray:
     u = _c(u, np.float64)
     M, H = u.shape
     g = _c(wts["gate"], _wdtype(fmt))
-    I = g.shape[1] * (2 if fmt == "mxfp4" else 1)
+    I = g.shape[1] * (2 if fmt in ("mxfp4", "mxfp4a8") else 1)
     sd = _sdtype(fmt)
     keep = [_c(wts[n], _wdtype(fmt)) for n in ("gate", "up", "down")]
     keep += [_c(wts[n + "_scale"], sd) if sd else None for n in ("gate", "up", "down")]

@@ -353,3 +353,135 @@ def test_layer_matches_its_own_steps():
                                                  for kk, v in routed.items()}, "f32")[0]
                        for e in idx[t]])
         assert np.allclose(O.combine_token(w[t], yk), out["y"][t], rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------------ W4A8: MXFP8 activations
+#
+# The routed experts' linear layers run W4A8 ('CANN DeepSeek-V4推理优化', quantisation
+# strategy). The activation side is OCP MXFP8 (OCP Microscaling Formats v1.0): an e8m0 exponent
+# X = floor(log2 max|v|) - 8 per 32 elements, elements E4M3FN(v / 2^X), round to nearest even,
+# saturated at 448.
+
+def _e4m3_values():
+    """All finite non-negative E4M3FN values, from torch's own decoder (code -> value)."""
+    codes = torch.arange(0, 0x7F, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("X", [-30, -1, 0, 7])
+def test_mxfp8_representable_values_round_trip(X):
+    """Every E4M3FN value times 2^X, in a block whose maximum is 448 * 2^X (so the shared
+    exponent is X), is encoded exactly: code and exponent are both fixed by the spec."""
+    vals = _e4m3_values()
+    for start in range(0, len(vals), 31):
+        chunk = vals[start:start + 31]
+        v = np.zeros(32)
+        v[0] = 448.0 * 2.0 ** X
+        v[1:1 + len(chunk)] = chunk * 2.0 ** X
+        c, e = O.mxfp8_quantize(v)
+        assert e[0] == X + 127
+        assert np.array_equal(c[1:1 + len(chunk)], np.arange(start, start + len(chunk)))
+        assert c[0] == 0x7E
+
+
+def test_mxfp8_negative_values_and_sign_of_zero():
+    v = np.zeros(32)
+    v[0], v[1], v[2], v[3] = -448.0, -1.0, -0.0, -2.0 ** -9
+    c, e = O.mxfp8_quantize(v)
+    assert e[0] == 127 and list(c[:4]) == [0xFE, 0xB8, 0x80, 0x81]
+
+
+def test_mxfp8_ties_round_to_even():
+    """Midpoints between neighbouring E4M3FN values go to the code with the even mantissa."""
+    vals = _e4m3_values()
+    for i in range(1, 0x7D):
+        mid = 0.5 * (vals[i] + vals[i + 1])
+        v = np.zeros(32)
+        v[0], v[1] = 448.0, mid
+        c, _ = O.mxfp8_quantize(v)
+        want = i if i % 2 == 0 else i + 1  # the mantissa is the low 3 bits of the code
+        assert c[1] == want, (i, mid)
+
+
+def test_mxfp8_saturates_and_picks_the_exponent_of_the_maximum():
+    """max|v| in [2^(X+8), 2^(X+9)) gives exponent X; scaled values past 448 saturate."""
+    for X, top in [(0, 511.0), (0, 470.0), (3, 500.0 * 8), (-5, 256.0 / 32)]:
+        v = np.zeros(32)
+        v[0] = top
+        v[1] = 460.0 * 2.0 ** X  # rounds to 448 (nearer than 480)
+        c, e = O.mxfp8_quantize(v)
+        assert e[0] == X + 127
+        assert c[0] == (0x7E if top / 2.0 ** X >= 464 else c[0])
+        assert c[1] == 0x7E
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((64, 32)) * np.exp(rng.uniform(-20, 20, (64, 1)))
+    _, e = O.mxfp8_quantize(v)
+    want = np.floor(np.log2(np.abs(v).max(axis=1))).astype(int) - 8 + 127
+    assert np.array_equal(e[:, 0], want)
+
+
+def test_mxfp8_zero_block_and_error_bound():
+    c, e = O.mxfp8_quantize(np.zeros(64))
+    assert np.all(c == 0) and np.all(e == 0)
+    rng = np.random.default_rng(4)
+    v = rng.standard_normal(32 * 200)
+    c, e = O.mxfp8_quantize(v)
+    dec = np.array([O.decode_scalar("e4m3fn", int(x)) for x in c]) * np.repeat(2.0 ** (e.astype(int) - 127), 32)
+    X = np.repeat(e.astype(int) - 127, 32)
+    # half a step: 2^-4 relative for normals, 2^(X-10) absolute on the subnormal grid; values
+    # scaled past 448 (the block maximum can reach 2^9 before saturation) clamp to 448 * 2^X
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** (X - 10))
+    bound = np.maximum(bound, np.abs(v) - 448.0 * 2.0 ** X)
+    assert np.all(np.abs(dec - v) <= bound * (1 + 1e-12))
+    assert np.any(np.abs(v) > 448.0 * 2.0 ** X)  # the saturating case occurs in this sample
+
+
+def _bf16_round(v):
+    """Round-to-nearest-even to 8 significant bits (bfloat16), written independently of the
+    oracle with numpy frexp."""
+    m, ex = np.frexp(v)  # v = m * 2^ex, |m| in [0.5, 1)
+    q = np.round(np.ldexp(m, 8))  # numpy rounds half to even
+    return np.ldexp(q, ex - 8)
+
+
+def _mxfp8_roundtrip(v):
+    c, e = O.mxfp8_quantize(v)
+    dec = np.vectorize(lambda x: O.decode_scalar("e4m3fn", int(x)))(c)
+    return dec * np.repeat(2.0 ** (e.astype(np.float64) - 127), 32, axis=-1)
+
+
+def test_expert_ffn_w4a8_is_quantised_swiglu():
+    """W4A8 FFN = down(Q(bf16(SiLU(Q(u) Wg) * (Q(u) Wu)))) with Q the MXFP8 round trip (pinned
+    above), the products by the pinned row_matmul on the MXFP4 weights, and torch's SiLU."""
+    H, I, M = 256, 128, 4
+    s = L.LayerSpec("f", T=M, H=H, E=1, k=1, I=I, w_routed="mxfp4a8")
+    wts = L.expert_weights(s, "routed", 0)
+    u = L.act_to_f64(L.store_act(px.normal_f32(3, 6, 0, 0, M * H).reshape(M, H), "bf16"), "bf16")
+    y = O.expert_ffn(u, wts, "mxfp4a8")
+    g = O.decode_matrix("mxfp4", H, I, wts["gate"], wts["gate_scale"])
+    v = O.decode_matrix("mxfp4", H, I, wts["up"], wts["up_scale"])
+    d = O.decode_matrix("mxfp4", I, H, wts["down"], wts["down_scale"])
+    uq = _mxfp8_roundtrip(u)
+    assert not np.array_equal(uq, u)  # the quantisation really acts
+    h = torch.nn.functional.silu(torch.from_numpy(uq @ g)).numpy() * (uq @ v)
+    ref = _mxfp8_roundtrip(_bf16_round(h)) @ d
+    assert np.allclose(y, ref, rtol=1e-9, atol=1e-11)
+    # and it stays near the bf16-activation MXFP4 FFN: two E4M3 roundings (2^-4 relative half
+    # step, up to 12.5% where a block maximum saturates) in each product give about 6%
+    y4 = O.expert_ffn(u, wts, "mxfp4")
+    rel = np.linalg.norm(y - y4) / np.linalg.norm(y4)
+    assert 1e-2 < rel < 8e-2
+
+
+def test_layer_w4a8_routes_like_mxfp4():
+    """W4A8 changes only the routed experts' products: routing and permutation equal the MXFP4
+    layer's, and the output stays within the MX activation error of it."""
+    s = L.LayerSpec("a8", T=8, H=128, E=4, k=2, I=128, act="bf16", w_routed="mxfp4a8", seed=9)
+    r = L.router_inputs(s)
+    routed = L.stack_experts(s)
+    a8 = O.layer(s, r["x"], r["Wr"], r["bias"], routed, None)
+    m4 = O.layer(s.replace(w_routed="mxfp4"), r["x"], r["Wr"], r["bias"], routed, None)
+    assert np.array_equal(a8["topk_idx"], m4["topk_idx"])
+    assert np.array_equal(a8["slot_token"], m4["slot_token"])
+    rel = np.linalg.norm(a8["y"] - m4["y"]) / np.linalg.norm(m4["y"])
+    assert 1e-2 < rel < 8e-2
