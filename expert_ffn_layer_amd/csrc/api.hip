@@ -37,11 +37,14 @@ int act_bytes(moe_dtype a) { return a == MOE_F32 ? 4 : 2; }
 int pad64(int n) { return (n + 63) / 64 * 64; }
 constexpr int ROW_BLOCK = 64;
 
-bool valid_fmt(int f) { return f >= MOE_F32 && f <= MOE_MXFP4_B32; }
+bool valid_fmt(int f) { return f >= MOE_F32 && f <= MOE_MXFP4_B32_A8; }
+// storage format: W4A8 weights are stored and packed as MXFP4
+moe_dtype stored_fmt(moe_dtype f) { return f == MOE_MXFP4_B32_A8 ? MOE_MXFP4_B32 : f; }
 
 // Bytes of `count` packed K x N matrices and of their packed scales.
 moe_status packed_sizes(moe_dtype fmt, int count, int K, int N, size_t* bytes, size_t* sbytes) {
   if (!valid_fmt(fmt)) return fail(MOE_ERR_INVALID_ARG, "unknown weight format %d", (int)fmt);
+  fmt = stored_fmt(fmt);
   if (count < 0 || K < 1 || N < 1) return fail(MOE_ERR_INVALID_ARG, "bad matrix size count=%d K=%d N=%d", count, K, N);
   const int KP = kp_of(fmt);
   if (K % KP) return fail(MOE_ERR_INVALID_ARG, "K=%d is not a multiple of %d for format %d", K, KP, (int)fmt);
@@ -77,6 +80,15 @@ moe_status check_shape(const moe_shape* s) {
   auto ok = [&](moe_dtype w) { return f32 ? w == MOE_F32 : w != MOE_F32; };
   if (!ok(s->w_routed) || (s->I_shared && !ok(s->w_shared)))
     return fail(MOE_ERR_UNSUPPORTED, "weights must be F32 with F32 activations and BF16/FP8/MXFP4 with BF16 ones");
+  if (s->I_shared && s->w_shared == MOE_MXFP4_B32_A8)
+    return fail(MOE_ERR_UNSUPPORTED, "W4A8 (MOE_MXFP4_B32_A8) applies to the routed experts only");
+  if (s->w_routed == MOE_MXFP4_B32_A8 &&
+      (s->path == MOE_PATH_DECODE ||
+       !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
+       !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->I, s->I, s->H)))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "W4A8 routed experts run on the prefill path only: BF16 activations, I a multiple of 256, "
+                "H a multiple of 512");
   if (s->path == MOE_PATH_PREFILL &&
       (!prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
        !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->I, s->I, s->H)))
@@ -119,7 +131,7 @@ RouterPlan router_plan(const moe_shape& s) {
 
 struct Ws {
   size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, zero, h, y_perm,
-      y_shared, total;
+      y_shared, xq, xs, hq, hs, total;
 };
 
 Ws ws_layout(const moe_shape& s) {
@@ -146,6 +158,14 @@ Ws ws_layout(const moe_shape& s) {
   w.y_perm = take(P * s.H * ab);
   w.y_shared = take(S * s.T * s.H * ab);
   w.zero = take((size_t)std::max(s.H, s.I) * ab);  // zero activations for prefill padding rows
+  if (s.w_routed == MOE_MXFP4_B32_A8) {
+    // W4A8: MXFP8 codes of x (gathered) and of h, in permuted row order, and their exponents
+    const size_t PR = mxfp8_padded_rows((int)P, s.E);
+    w.xq = take(P * s.H);
+    w.xs = take(PR * (s.H / 32));
+    w.hq = take(P * s.I);
+    w.hs = take(PR * (s.I / 32));
+  }
   w.total = o;
   return w;
 }
@@ -167,7 +187,8 @@ T* at(void* ws, size_t off) {
 moe_status check_weights(const moe_weights* w, moe_dtype fmt, const char* what) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "%s weights are NULL", what);
   if (!w->gate || !w->up || !w->down) return fail(MOE_ERR_INVALID_ARG, "%s weight pointer is NULL", what);
-  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP4_B32) && (!w->gate_scale || !w->up_scale || !w->down_scale))
+  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP4_B32 || fmt == MOE_MXFP4_B32_A8) &&
+      (!w->gate_scale || !w->up_scale || !w->down_scale))
     return fail(MOE_ERR_INVALID_ARG, "%s scales are NULL", what);
   return MOE_OK;
 }
@@ -209,7 +230,7 @@ bool use_prefill(const moe_shape& s) {
   const int cs = s.I_shared ? s.w_shared : s.w_routed;
   if (!prefill_supported(s.act, s.w_routed, cs, s.H, s.I, s.H) || !prefill_supported(s.act, s.w_routed, cs, s.I, s.I, s.H))
     return false;
-  if (s.path == MOE_PATH_PREFILL) return true;
+  if (s.path == MOE_PATH_PREFILL || s.w_routed == MOE_MXFP4_B32_A8) return true;
   if (s.path == MOE_PATH_DECODE) return false;
   return (long long)s.T * s.k >= 64LL * s.E;
 }
@@ -289,8 +310,33 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.ldo = s.I;
   a.out_s = nullptr;
   const int cs = S ? s.w_shared : s.w_routed;
-  e = prefill ? launch_grouped_prefill(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st)
-              : launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
+  const bool a8 = s.w_routed == MOE_MXFP4_B32_A8;
+  const int PR = a8 ? (int)mxfp8_padded_rows(P, s.E) : 0;
+  // W4A8: the routed groups read MXFP8 codes of their gathered rows (quantised here, in permuted
+  // row order, no gather in the GEMM); the shared expert keeps its own launch on the bf16 rows.
+  auto launch_a8 = [&](int epi, const GroupedArgs& base, const void* codes, const void* scales, int K) {
+    GroupedArgs ra = base, sa = base;
+    ra.gather = nullptr;
+    ra.act = codes;
+    ra.lda = K;
+    ra.act_rows = P;
+    ra.act_scale = scales;
+    ra.g_begin = 0;
+    ra.g_end = s.E;
+    hipError_t r = launch_grouped_prefill(s.act, epi, MOE_MXFP4_B32_A8, MOE_MXFP4_B32_A8, ra, max_rb, st);
+    if (r != hipSuccess || !S) return r;
+    sa.g_begin = s.E;
+    sa.g_end = s.E + 1;
+    return launch_grouped_prefill(s.act, epi, cs, cs, sa, max_rb, st);
+  };
+  if (a8) {
+    e = launch_quant_mxfp8(x, s.H, slot_token, gr, cb, s.E, s.H, PR, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), st);
+    if (e != hipSuccess) return hip_status(e, "MXFP8 quantisation of x");
+    e = launch_a8(EPI_SWIGLU, a, at<void>(ws, L.xq), at<void>(ws, L.xs), s.H);
+  } else {
+    e = prefill ? launch_grouped_prefill(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st)
+                : launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
+  }
   if (e != hipSuccess) return hip_status(e, "gate/up grouped GEMM");
   if (ev && (rs = record(ev[1], st)) != MOE_OK) return rs;
   // down: y = h Wd
@@ -316,8 +362,15 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.ldo = s.H;
   a.out_s = S ? y_shared : nullptr;
   a.ldo_s = s.H;
-  e = prefill ? launch_grouped_prefill(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st)
-              : launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);
+  if (a8) {
+    e = launch_quant_mxfp8(at<void>(ws, L.h), s.I, nullptr, gr, cb, s.E, s.I, PR, at<uint8_t>(ws, L.hq),
+                           at<uint8_t>(ws, L.hs), st);
+    if (e != hipSuccess) return hip_status(e, "MXFP8 quantisation of h");
+    e = launch_a8(EPI_PLAIN, a, at<void>(ws, L.hq), at<void>(ws, L.hs), s.I);
+  } else {
+    e = prefill ? launch_grouped_prefill(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st)
+                : launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);
+  }
   if (e != hipSuccess) return hip_status(e, "down grouped GEMM");
   return ev ? record(ev[2], st) : MOE_OK;
 }
@@ -389,7 +442,8 @@ moe_status moe_pack(moe_dtype fmt, int32_t count, int32_t K, int32_t N, const vo
   if (count == 0) return MOE_OK;
   if (!w || !packed) return fail(MOE_ERR_INVALID_ARG, "NULL matrix pointer");
   if (sb && (!scale || !packed_scale)) return fail(MOE_ERR_INVALID_ARG, "NULL scale pointer");
-  return hip_status(moe_launch_pack(fmt, count, K, N, w, scale, packed, packed_scale, (hipStream_t)stream), "pack");
+  return hip_status(moe_launch_pack(stored_fmt(fmt), count, K, N, w, scale, packed, packed_scale, (hipStream_t)stream),
+                    "pack");
 }
 
 moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {

@@ -48,6 +48,9 @@ struct PCodec<MOE_BF16> {
   static constexpr int PK = 1;       // packets per 16-column tile per pipeline step
   static constexpr bool HALF_ONLY = false;  // every item 128 rows x 512 columns
   static constexpr bool SCALE_DMA = false;  // per-packet scales reach LDS with the weights
+  static constexpr int ACT_BYTES = 2;       // bytes per activation element
+  static constexpr int NSC = 0;             // scale DMA loads per wave per step
+  static constexpr int SC_KIB = 0;          // LDS of those scales per stage
   // Activation layout of one 16-row tile per step (H KiB of LDS): DMA unit u, lane l reads
   // 16 bytes of row dma_row(l, u) at byte dma_off(l, u) of the row's step slice and lands them
   // at u * 1024 + 16 * l; the B fragment of MFMA half h is the 16 bytes at read_off(l, h).
@@ -88,6 +91,7 @@ struct PCodec<MOE_FP8_E4M3_B128> {
   static constexpr int PK = 1;
   static constexpr bool HALF_ONLY = false;
   static constexpr bool SCALE_DMA = false;
+  static constexpr int ACT_BYTES = 2, NSC = 0, SC_KIB = 0;
   // Lane group g of a packet holds reduction elements 16g .. 16g + 15 and MFMA half h takes the
   // h-th run of 8 of them, so the B fragment of half h for lane (g, row j) is the 16-byte chunk
   // c = 2g + h of row j's 128-byte step slice. DMA unit u moves rows 8u .. 8u + 7 as whole
@@ -133,6 +137,7 @@ struct PCodec<MOE_MXFP4_B32> {
   static constexpr int PK = 1;
   static constexpr bool HALF_ONLY = true;
   static constexpr bool SCALE_DMA = true;
+  static constexpr int ACT_BYTES = 2, NSC = 1, SC_KIB = 8;
   __device__ static int dma_row(int l, int u) { return 4 * u + (l >> 4); }
   __device__ static int dma_off(int l, int u) { return 16 * ((l & 15) ^ (4 * u + (l >> 4))); }
   __device__ static int read_off(int l, int h) {
@@ -143,6 +148,41 @@ struct PCodec<MOE_MXFP4_B32> {
 #pragma unroll
     for (int h = 0; h < H; ++h) a[h] = p_fp4x8(w[0][h], s);
   }
+};
+
+// W4A8: MXFP4 weight packets times MXFP8 activations, both handed to
+// v_mfma_scale_f32_16x16x128_f8f6f4 as stored (no conversion, no rescale: the e8m0 exponents go to
+// the instruction's scale operands). One step is one packet deep (128). The operand layouts of that
+// instruction (fp4 A, fp8 B, measured on the hardware):
+//   A, fp4: lane (f, g) = (l % 16, l / 16) holds 32 codes of feature f. Its pairing with B makes
+//           them reduction elements 32g .. 32g + 31 -- exactly a packet lane -- and the lane's own
+//           scale byte applies to all 32: the packet's e8m0 byte of that lane.
+//   B, fp8: lane (j, g) holds token j: bytes 0..15 are elements 16g .. 16g + 15, bytes 16..31 are
+//           elements 64 + 16g .. 64 + 16g + 15, i.e. 16-byte chunks g and 4 + g of the token's
+//           128-byte step slice; the exponent of (token j, block b) is taken from lane j + 16b.
+// Activations move as whole 128-byte row lines, 8 rows per DMA unit, with the same XOR swizzle as
+// the fp8 codec's bf16 lines, so the two chunk reads of a lane are conflict-free. Per stage the LDS
+// also holds each wave's 4 tiles x 64 packet exponents (one 4-byte DMA per wave) and the 16 row
+// tiles x 64 activation exponents of the item (one 16-byte DMA, issued by every wave with the same
+// bytes to the same place).
+template <>
+struct PCodec<MOE_MXFP4_B32_A8> {
+  static constexpr int KP = 128;
+  static constexpr int PBK = 128;
+  static constexpr int H = 2;  // 1 KiB activation DMA units per 16-row tile per step
+  static constexpr int PK = 1;
+  static constexpr bool HALF_ONLY = false;
+  static constexpr bool SCALE_DMA = false;
+  static constexpr int ACT_BYTES = 1, NSC = 2, SC_KIB = 3;
+  __device__ static int dma_row(int l, int u) { return 8 * u + (l >> 3); }
+  __device__ static int dma_off(int l, int u) { return 16 * ((l & 7) ^ (l >> 3) ^ u); }
+  // chunk 4h + g of token row j = l % 16
+  __device__ static int read_off(int l, int h) {
+    const int j = l & 15, g = l >> 4;
+    return (j >> 3) * 1024 + (j & 7) * 128 + 16 * ((4 * h + g) ^ (j & 7) ^ (j >> 3));
+  }
+  // the bf16-operand step is compiled but never reached for this codec (its step returns first)
+  __device__ static void frags(const u32x4 (&)[PK], float, bf16x8 (&)[H]) {}
 };
 
 template <int EPI>
@@ -161,7 +201,7 @@ struct PLayout {
   // 1 KiB of packet scales; in KiB
   static constexpr int FULL_ACT = 16 * H, HALF_ACT = 8 * H;
   static constexpr int FULL_W = 16 * PK, HALF_W = 32 * PK;
-  static constexpr int SC_KIB = Cd::SCALE_DMA ? 8 : 0;
+  static constexpr int SC_KIB = Cd::SC_KIB;
   static constexpr int ITEM_KIB = (!Cd::HALF_ONLY && FULL_ACT + FULL_W > HALF_ACT + HALF_W) ? FULL_ACT + FULL_W
                                                                                          : HALF_ACT + HALF_W;
   static constexpr int SC_OFF = ITEM_KIB * 1024;
@@ -170,7 +210,7 @@ struct PLayout {
   // DMA instructions per wave per stage; the shorter kind is padded with repeats of its last
   // load so both kinds issue the same count (the wait counts are compile-time)
   static constexpr int LF = Cd::HALF_ONLY ? 0 : 2 * H + 2 * PK, LH = H + 4 * PK;
-  static constexpr int L = (LF > LH ? LF : LH) + (Cd::SCALE_DMA ? 1 : 0);
+  static constexpr int L = (LF > LH ? LF : LH) + Cd::NSC;
   static_assert(STAGES * STAGE_KIB <= 160, "LDS");
 };
 
@@ -303,12 +343,31 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   int qdst[L], qstride[L];
   const int wts_off = (half ? Ly::HALF_ACT : Ly::FULL_ACT) * 1024;
   constexpr int LSC = Cd::SCALE_DMA ? 1 : 0;  // the last load moves the packet scales
+  constexpr bool A8 = C == MOE_MXFP4_B32_A8;   // the last two loads move the exponents
+  // W4A8: the activation exponents are indexed by 16-row tiles of the padded row space in which
+  // group g starts at row 128 * cum_blocks[g]
+  const int prow0 = planned ? PRB * a.cum_blocks[g] + (row0 - rbeg) : row0;
 #pragma unroll
   for (int q = 0; q < L; ++q) {
     const int nact = half ? H : 2 * H;
     const int nw = half ? 4 * PK : 2 * PK;
     const int qq = q < nact + nw ? q : nact + nw - 1;
-    if (LSC && q == L - 1) {
+    if (A8 && q == L - 2) {
+      // this wave's 4 column tiles' packet exponents, 64 bytes per tile: a 4-byte DMA, lane l
+      // moving bytes 4 (l % 16) .. + 4 of tile l / 16
+      const int t = lane >> 4;
+      const uint8_t* sp = t / WF == 0 ? ws0 : ws1;
+      qsrc[q] = sp + ((size_t)(gw * WF + t % WF) * KT) * 64 + (size_t)(lane & 15) * 4;
+      qdst[q] = Ly::SC_OFF + wave * 256;
+      qstride[q] = 64;
+    } else if (A8 && q == L - 1) {
+      // the item's 16 row tiles x 4 blocks x 16 tokens of activation exponents of the step:
+      // lane l moves chunk l % 4 of row tile l / 4
+      qsrc[q] = (const uint8_t*)a.act_scale + ((size_t)(prow0 / 16 + (lane >> 2)) * (a.K / 32)) * 16 +
+                (size_t)(lane & 3) * 16;
+      qdst[q] = Ly::SC_OFF + 2048;
+      qstride[q] = 64;
+    } else if (LSC && q == L - 1) {
       // this wave's 4 column tiles' e8m0 bytes of the step's packets (64 per tile): lane l
       // fetches 16 bytes of tile (l % 16) / 4; lanes 16..63 repeat lanes 0..15
       const int t = (lane & 15) >> 2;
@@ -326,10 +385,10 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       // rows past the group's end feed zeros when a zero row is given (their results are
       // discarded either way; zero operands keep the padding MFMAs cheap in power)
       const uint8_t* rowp = (rr >= nr && a.zero_row) ? (const uint8_t*)a.zero_row
-                                                      : (const uint8_t*)a.act + (size_t)src * a.lda * 2;
+                                                      : (const uint8_t*)a.act + (size_t)src * a.lda * Cd::ACT_BYTES;
       qsrc[q] = rowp + Cd::dma_off(lane, h);
       qdst[q] = (rt * H + h) * 1024;
-      qstride[q] = PBK * 2;
+      qstride[q] = PBK * Cd::ACT_BYTES;
     } else {
       const int i = (qq - nact) / PK, p = (qq - nact) % PK;
       const int t = half ? i : 2 * wrow + i;
@@ -340,8 +399,12 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   }
   auto dma_one = [&](int q, int step) {
     const int st = kstep0 + min(step, nsteps - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(qsrc[q] + (size_t)st * qstride[q]),
-                                     (lds_void*)(lds + (step % D) * STAGE_B + qdst[q]), 16, 0, 0);
+    if (A8 && q == L - 2)
+      __builtin_amdgcn_global_load_lds((const void*)(qsrc[q] + (size_t)st * qstride[q]),
+                                       (lds_void*)(lds + (step % D) * STAGE_B + qdst[q]), 4, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((const void*)(qsrc[q] + (size_t)st * qstride[q]),
+                                       (lds_void*)(lds + (step % D) * STAGE_B + qdst[q]), 16, 0, 0);
   };
 
   f32x4 acc[NT][8];
@@ -383,6 +446,42 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
         rs[m] = mcur[m] * __builtin_amdgcn_rcpf(mn);  // m ratio in (0.5, 2), about 1 ulp
         mcur[m] = mn;
       }
+    }
+    if constexpr (A8) {
+      // one block-scaled fp4 x fp8 MFMA per (row tile, column tile): the packet as stored (fp4
+      // codes in operand dwords 0-3) with its e8m0 byte, the two 16-byte activation chunks of the
+      // lane with the row tile's exponent byte
+      i32x8 af8[NT];
+      int sa[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x4 pk = *(const u32x4*)(base + wbase + t * 1024);
+        af8[t] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+        sa[t] = base[Ly::SC_OFF + wave * 256 + t * 64 + lane];
+      }
+      const uint8_t* sbp = base + Ly::SC_OFF + 2048 + wrow * 8 * 64 + lane;
+      u32x4 b0n = *(const u32x4*)(base + aoff[0]), b1n = *(const u32x4*)(base + aoff[1]);
+      int sbn = sbp[0];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 b0 = b0n, b1 = b1n;
+        const int sb = sbn;
+        if (j + 1 < 8) {
+          b0n = *(const u32x4*)(base + aoff[0] + (j + 1) * H * 1024);
+          b1n = *(const u32x4*)(base + aoff[1] + (j + 1) * H * 1024);
+          sbn = sbp[(j + 1) * 64];
+        }
+        const i32x8 bf = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                               (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af8[t], bf, acc[t][j], 4, 0, 0, sa[t], 0, sb);
+#pragma unroll
+        for (int u = 0; u < QJ; ++u)
+          if (j * QJ + u < L) dma_one(j * QJ + u, step + D - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
     }
     bf16x8 af[NT][H];
 #pragma unroll
@@ -519,6 +618,7 @@ static hipError_t launch_codec(int c, const GroupedArgs& a, int max_units, hipSt
   if (c == MOE_BF16) return launch_p<MOE_BF16, EPI>(a, max_units, st);
   if (c == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI>(a, max_units, st);
   if (c == MOE_MXFP4_B32) return launch_p<MOE_MXFP4_B32, EPI>(a, max_units, st);
+  if (c == MOE_MXFP4_B32_A8) return launch_p<MOE_MXFP4_B32_A8, EPI>(a, max_units, st);
   return hipErrorInvalidValue;
 }
 
@@ -547,6 +647,7 @@ static bool prefill_codec_ok(int c, int K) {
   if (c == MOE_BF16) pbk = PCodec<MOE_BF16>::PBK;
   else if (c == MOE_FP8_E4M3_B128) pbk = PCodec<MOE_FP8_E4M3_B128>::PBK;
   else if (c == MOE_MXFP4_B32) pbk = PCodec<MOE_MXFP4_B32>::PBK;
+  else if (c == MOE_MXFP4_B32_A8) pbk = PCodec<MOE_MXFP4_B32_A8>::PBK;
   else return false;
   return K % pbk == 0 && K % 128 == 0 && K <= 64 * 128;
 }

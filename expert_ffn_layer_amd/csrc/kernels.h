@@ -43,6 +43,7 @@ struct GroupedArgs {
   int ksplit;  // > 1: fp32 output only; workgroup y sums K part y into out + y * M * ldo
   const void* zero_row;  // prefill: K zero activations that rows past a group's end read, or null
   int g_begin, g_end;    // prefill: groups of this launch (g_end <= g_begin: all groups)
+  const void* act_scale; // W4A8: e8m0 exponents of the MXFP8 activations (launch_quant_mxfp8 layout)
 };
 
 // Output features (in units of 16) per decode work item, chosen from the instantiated set so an
@@ -81,6 +82,11 @@ hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int sha
                                 int32_t* slot_token, int32_t* pair_slot, int32_t* group_range, int32_t* cum_blocks,
                                 hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t st);
+// W4A8: bf16 rows -> MXFP8 codes (permuted row order) + exponents (padded 16-row-tile layout).
+size_t mxfp8_padded_rows(int P, int E);
+hipError_t launch_quant_mxfp8(const void* src, int lds_, const int32_t* gather, const int32_t* group_range,
+                              const int32_t* cum_blocks, int G, int K, int padded_rows, uint8_t* codes,
+                              uint8_t* scales, hipStream_t st);
 hipError_t launch_combine(int act, const void* y_perm, const int32_t* pair_slot, const float* w,
                           const void* y_shared, void* y, int T, int H, int k, hipStream_t st);
 

@@ -54,7 +54,15 @@ typedef enum {
   MOE_F32 = 0,            /* float32 */
   MOE_BF16 = 1,           /* bfloat16 */
   MOE_FP8_E4M3_B128 = 2,  /* OCP E4M3FN codes + one fp32 scale per 128 x 128 block */
-  MOE_MXFP4_B32 = 3       /* OCP e2m1 codes + one e8m0 exponent per 32 reduction elements */
+  MOE_MXFP4_B32 = 3,      /* OCP e2m1 codes + one e8m0 exponent per 32 reduction elements */
+  MOE_MXFP4_B32_A8 = 4    /* W4A8 routed experts ('CANN DeepSeek-V4推理优化', quantisation
+                             strategy: the routed experts' linear layers run W4A8). Weights are
+                             stored, packed and sized exactly as MOE_MXFP4_B32; the activations of
+                             both products (x before gate/up, h before down) are quantised to OCP
+                             MXFP8 (E4M3FN codes, round to nearest even, saturating at 448, with
+                             one e8m0 exponent floor(log2 max|v|) - 8 per 32 reduction elements)
+                             and multiplied by the block-scaled fp4 x fp8 matrix instruction.
+                             Only as w_routed, with BF16 activations, on the prefill path. */
 } moe_dtype;
 
 typedef enum {
@@ -62,8 +70,9 @@ typedef enum {
                              shape, else decode */
   MOE_PATH_DECODE = 1,    /* weight-streaming grouped GEMM (few rows per expert) */
   MOE_PATH_PREFILL = 2    /* LDS-tiled MFMA grouped GEMM (many rows per expert): BF16
-                             activations, BF16 / FP8 / MXFP4 weights, I a multiple of 256, H a
-                             multiple of 512; MOE_ERR_UNSUPPORTED otherwise */
+                             activations, BF16 / FP8 / MXFP4 / W4A8 weights, I a multiple of 256,
+                             H a multiple of 512; MOE_ERR_UNSUPPORTED otherwise. W4A8 routed
+                             experts always take this path (AUTO included). */
 } moe_path;
 
 typedef struct {
@@ -74,8 +83,9 @@ typedef struct {
   int32_t I;          /* expert intermediate size, multiple of 128 */
   int32_t I_shared;   /* shared expert intermediate size: 0 = no shared expert, else == I */
   moe_dtype act;      /* MOE_F32 or MOE_BF16: x, Wr, y and the intermediates */
-  moe_dtype w_routed; /* MOE_F32 (with act MOE_F32) or BF16 / FP8 / MXFP4 (with act BF16) */
-  moe_dtype w_shared; /* same rule */
+  moe_dtype w_routed; /* MOE_F32 (with act MOE_F32) or BF16 / FP8 / MXFP4 / MXFP4_B32_A8 (with
+                         act BF16) */
+  moe_dtype w_shared; /* same rule, without MXFP4_B32_A8 */
   moe_path path;
 } moe_shape;
 
@@ -104,7 +114,7 @@ const char* moe_last_error(void);
  *   MOE_F32   float[K][N]                MOE_BF16  uint16[K][N] (bf16 bits)
  *   MOE_FP8_E4M3_B128  uint8[K][N] codes + float[K/128][N/128] scales (w = e4m3(c) * s)
  *   MOE_MXFP4_B32      uint8[K][N/2] codes, even n in the low nibble + uint8[K/32][N] e8m0
- *                      exponents (w = e2m1(c) * 2^(E-127))
+ *                      exponents (w = e2m1(c) * 2^(E-127)); MOE_MXFP4_B32_A8 the same
  * Packed layout: 1 KiB packets of 16 features x KP reduction elements (KP = 16, 32, 64, 128 for
  * F32, BF16, FP8, MXFP4), packet (nt, kt) at byte (nt*(K/KP) + kt)*1024, lane l of a packet
  * holding feature nt*16 + l%16 and reduction run kt*KP + (l/16)*KP/4 + [0, KP/4). FP8 scales

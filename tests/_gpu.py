@@ -14,7 +14,9 @@ from inputgen import gpu as G
 from inputgen import layers as L
 from oracle import oracle as O
 
-TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 4e-2, "mxfp4": 4e-2}
+# W4A8 is held to the bf16 bar: its oracle performs the same MXFP8 quantisation, so only
+# accumulation order and rounding of h / y differ
+TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 4e-2, "mxfp4": 4e-2, "mxfp4a8": 1e-2}
 
 
 def say(*a):

@@ -47,11 +47,22 @@ def _shape(**kw):
     (dict(T=-1), 1), (dict(H=100), 1), (dict(I=64), 1), (dict(E=0), 1), (dict(E=2000), 1),
     (dict(k=0), 1), (dict(k=9), 1), (dict(E=32, k=17), 1), (dict(I_shared=256), 2),
     (dict(act="fp8"), 1), (dict(act="f32"), 2), (dict(w_routed="f32"), 2),
+    # W4A8: routed experts only, prefill only (bf16 activations, I % 256, H % 512)
+    (dict(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="mxfp4a8"), 2),
+    (dict(H=512, I=256, w_routed="mxfp4a8", path="decode"), 2),
+    (dict(H=512, I=128, w_routed="mxfp4a8"), 2), (dict(H=256, I=256, w_routed="mxfp4a8"), 2),
 ])
 def test_shape_validation(kw, status):
     with pytest.raises(N.MoeError) as e:
         N.moe_workspace_size(_shape(**kw))
     assert e.value.status == status
+
+
+def test_w4a8_shape_is_accepted_and_adds_quantised_activations():
+    base = N.moe_workspace_size(_shape(H=512, I=256, w_routed="mxfp4"))
+    a8 = N.moe_workspace_size(_shape(H=512, I=256, w_routed="mxfp4a8"))
+    assert a8 > base
+    assert N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="bf16")) > a8
 
 
 def test_workspace_grows_with_tokens_and_shared_expert():
@@ -67,6 +78,8 @@ def test_pack_sizes():
     assert N.moe_pack_size("f32", 1, 256, 128) == (256 * 128 * 4, 0)
     assert N.moe_pack_size("fp8", 2, 7168, 2048) == (2 * 7168 * 2048, 2 * 56 * 16 * 4)
     assert N.moe_pack_size("mxfp4", 1, 7168, 3072) == (7168 * 3072 // 2, 7168 * 3072 // 32)
+    # W4A8 weights are stored and packed exactly as MXFP4
+    assert N.moe_pack_size("mxfp4a8", 2, 7168, 3072) == N.moe_pack_size("mxfp4", 2, 7168, 3072)
     # the router's E is padded to 64 features
     assert N.moe_pack_size("bf16", 1, 256, 8) == (256 * 64 * 2, 0)
     for fmt, K, Nn in (("fp8", 7168, 100), ("fp8", 100, 128), ("bf16", 48, 64), ("mxfp4", 128, 3)):

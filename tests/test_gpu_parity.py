@@ -123,12 +123,18 @@ SMALL = [
                                   w_shared="mxfp4", seed=42)),
     ("fp8-bf16-prefill", L.LayerSpec("s13", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="fp8",
                                      w_shared="bf16", seed=43)),
+    # W4A8 routed experts (MXFP4 weights x MXFP8 activations on the block-scaled MFMA): ragged
+    # groups with a bf16 shared expert, and many small groups (half items) without one
+    ("w4a8-bf16-shared", L.LayerSpec("s14", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="mxfp4a8",
+                                     w_shared="bf16", router="zipf", zipf_alpha=1.0, calib_tokens=512,
+                                     seed=44)),
+    ("w4a8-small-groups", L.LayerSpec("s15", T=96, H=1024, E=24, k=4, I=512, w_routed="mxfp4a8", seed=45)),
 ]
 
 
 def _prefill_ok(spec):
     fmts = ("bf16", "fp8", "mxfp4")
-    return (spec.act == "bf16" and spec.w_routed in fmts and (not spec.shared or spec.w_shared in fmts)
+    return (spec.act == "bf16" and spec.w_routed in fmts + ("mxfp4a8",) and (not spec.shared or spec.w_shared in fmts)
             and spec.I % 256 == 0 and spec.H % 512 == 0)
 
 
@@ -137,6 +143,8 @@ def _prefill_ok(spec):
 def test_layer_small(name, spec, path):
     if path == "prefill" and not _prefill_ok(spec):
         pytest.skip("the prefill kernel takes bf16 activations, I % 256 == 0 and H % 512 == 0")
+    if path == "decode" and spec.w_routed == "mxfp4a8":
+        pytest.skip("W4A8 routed experts run on the prefill path only (the decode path is refused)")
     say("layer", name, path, spec)
     lay, pl = build(spec, DEV, path)
     y, idx, w = run(spec, lay, pl)
@@ -182,6 +190,8 @@ STAGE_SPECS = [
                              w_shared="fp8", seed=48)),
     ("mxfp4+fp8", L.LayerSpec("st49", T=20, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4",
                               w_shared="fp8", seed=49)),
+    ("w4a8+bf16", L.LayerSpec("st50", T=40, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
+                              w_shared="bf16", seed=50)),
 ]
 
 
@@ -241,10 +251,13 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
 
 # ------------------------------------------------------------------ full-size layers
 
-FULL = ["c2", "c3", "c4", "c5", "v4pro-prefill"]
+FULL = ["c2", "c3", "c4", "c5", "v4pro-prefill", "v4pro-prefill-w4a8"]
 # the DeepSeek-V4-Pro-shaped layer at a prefill batch: MXFP4 routed experts in the prefill
-# kernel, the bf16 shared expert in a launch of its own
-EXTRA = {"v4pro-prefill": L.CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096)}
+# kernel, the bf16 shared expert in a launch of its own; and the same layer with W4A8 routed
+# experts (MXFP8 activations on the block-scaled MFMA)
+EXTRA = {"v4pro-prefill": L.CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096),
+         "v4pro-prefill-w4a8": L.CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-w4a8", T=4096,
+                                                       w_routed="mxfp4a8")}
 
 
 @pytest.mark.slow
