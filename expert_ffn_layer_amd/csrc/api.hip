@@ -159,12 +159,11 @@ Ws ws_layout(const moe_shape& s) {
   w.y_shared = take(S * s.T * s.H * ab);
   w.zero = take((size_t)std::max(s.H, s.I) * ab);  // zero activations for prefill padding rows
   if (s.w_routed == MOE_MXFP4_B32_A8) {
-    // W4A8: MXFP8 codes of x (gathered) and of h, in permuted row order, and their exponents
-    const size_t PR = mxfp8_padded_rows((int)P, s.E);
-    w.xq = take(P * s.H);
-    w.xs = take(PR * (s.H / 32));
+    // W4A8: MXFP8 codes and exponents of x (token rows) and of the routed rows of h
+    w.xq = take((size_t)s.T * s.H);
+    w.xs = take((size_t)s.T * (s.H / 32));
     w.hq = take(P * s.I);
-    w.hs = take(PR * (s.I / 32));
+    w.hs = take(P * (s.I / 32));
   }
   w.total = o;
   return w;
@@ -311,28 +310,34 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.out_s = nullptr;
   const int cs = S ? s.w_shared : s.w_routed;
   const bool a8 = s.w_routed == MOE_MXFP4_B32_A8;
-  const int PR = a8 ? (int)mxfp8_padded_rows(P, s.E) : 0;
-  // W4A8: the routed groups read MXFP8 codes of their gathered rows (quantised here, in permuted
-  // row order, no gather in the GEMM); the shared expert keeps its own launch on the bf16 rows.
-  auto launch_a8 = [&](int epi, const GroupedArgs& base, const void* codes, const void* scales, int K) {
+  // W4A8: the routed groups multiply MXFP8 codes of x (quantised once per token, gathered like x)
+  // and write h as MXFP8 for their down product; the shared expert keeps its own launch on the
+  // bf16 rows.
+  auto launch_a8 = [&](int epi, const GroupedArgs& base, const void* codes, const void* scales, int K,
+                       int rows, const int32_t* gather) {
     GroupedArgs ra = base, sa = base;
-    ra.gather = nullptr;
+    ra.gather = gather;
     ra.act = codes;
     ra.lda = K;
-    ra.act_rows = P;
+    ra.act_rows = rows;
     ra.act_scale = scales;
     ra.g_begin = 0;
     ra.g_end = s.E;
-    hipError_t r = launch_grouped_prefill(s.act, epi, MOE_MXFP4_B32_A8, MOE_MXFP4_B32_A8, ra, max_rb, st);
+    if (epi == EPI_SWIGLU) {
+      ra.out = at<void>(ws, L.hq);
+      ra.ldo = s.I;
+      ra.out_scale = at<void>(ws, L.hs);
+    }
+    hipError_t r = launch_w4a8_prefill(epi == EPI_SWIGLU ? EPI_SWIGLU_Q8 : epi, ra, max_rb, st);
     if (r != hipSuccess || !S) return r;
     sa.g_begin = s.E;
     sa.g_end = s.E + 1;
     return launch_grouped_prefill(s.act, epi, cs, cs, sa, max_rb, st);
   };
   if (a8) {
-    e = launch_quant_mxfp8(x, s.H, slot_token, gr, cb, s.E, s.H, PR, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), st);
+    e = launch_quant_mxfp8(x, s.T, s.H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), st);
     if (e != hipSuccess) return hip_status(e, "MXFP8 quantisation of x");
-    e = launch_a8(EPI_SWIGLU, a, at<void>(ws, L.xq), at<void>(ws, L.xs), s.H);
+    e = launch_a8(EPI_SWIGLU, a, at<void>(ws, L.xq), at<void>(ws, L.xs), s.H, s.T, slot_token);
   } else {
     e = prefill ? launch_grouped_prefill(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st)
                 : launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
@@ -363,10 +368,7 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.out_s = S ? y_shared : nullptr;
   a.ldo_s = s.H;
   if (a8) {
-    e = launch_quant_mxfp8(at<void>(ws, L.h), s.I, nullptr, gr, cb, s.E, s.I, PR, at<uint8_t>(ws, L.hq),
-                           at<uint8_t>(ws, L.hs), st);
-    if (e != hipSuccess) return hip_status(e, "MXFP8 quantisation of h");
-    e = launch_a8(EPI_PLAIN, a, at<void>(ws, L.hq), at<void>(ws, L.hs), s.I);
+    e = launch_a8(EPI_PLAIN, a, at<void>(ws, L.hq), at<void>(ws, L.hs), s.I, P, nullptr);
   } else {
     e = prefill ? launch_grouped_prefill(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st)
                 : launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);

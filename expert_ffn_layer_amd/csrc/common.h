@@ -57,6 +57,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // division sequence; e^-z -> inf for very negative z gives z * 0 = -0, the right limit.
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
+// fp32 -> OCP E4M3FN code, round to nearest even, saturating at +-448 (the sign of y, zero
+// included, is kept); y finite.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = __builtin_fabsf(y);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);  // below 2^-6: grid 2^-9
+  const uint32_t ab = __float_as_uint(a);
+  int e = (int)(ab >> 23) - 127;  // -6 .. 8
+  uint32_t m = (ab >> 20) & 7u;   // top 3 mantissa bits
+  const uint32_t rest = ab & 0xFFFFFu, half = 0x80000u;
+  if (rest > half || (rest == half && (m & 1u))) ++m;
+  if (m == 8u) {
+    m = 0;
+    ++e;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | m;  // a < 448 keeps this at or below 0x7E
+}
+
+// Shared e8m0 exponent of an OCP MXFP8 block with maximum magnitude amax:
+// floor(log2 amax) - 8 (8 = the largest E4M3 exponent), clamped to [-127, 127], -127 for zero.
+__device__ __forceinline__ int mxfp8_exponent(float amax) {
+  int X = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 9 : -127;
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) {
   return __builtin_nontemporal_load(p);

@@ -162,9 +162,10 @@ struct PCodec<MOE_MXFP4_B32> {
 //           128-byte step slice; the exponent of (token j, block b) is taken from lane j + 16b.
 // Activations move as whole 128-byte row lines, 8 rows per DMA unit, with the same XOR swizzle as
 // the fp8 codec's bf16 lines, so the two chunk reads of a lane are conflict-free. Per stage the LDS
-// also holds each wave's 4 tiles x 64 packet exponents (one 4-byte DMA per wave) and the 16 row
-// tiles x 64 activation exponents of the item (one 16-byte DMA, issued by every wave with the same
-// bytes to the same place).
+// also holds each wave's 4 tiles x 64 packet exponents and the item's activation exponents, 4
+// bytes (the step's 4 blocks) per row, gathered like the rows: both by 4-byte DMAs, one per wave,
+// the second covering 4 row tiles from the wave's first (neighbouring waves write the same bytes
+// to the overlap).
 template <>
 struct PCodec<MOE_MXFP4_B32_A8> {
   static constexpr int KP = 128;
@@ -173,7 +174,7 @@ struct PCodec<MOE_MXFP4_B32_A8> {
   static constexpr int PK = 1;
   static constexpr bool HALF_ONLY = false;
   static constexpr bool SCALE_DMA = false;
-  static constexpr int ACT_BYTES = 1, NSC = 2, SC_KIB = 3;
+  static constexpr int ACT_BYTES = 1, NSC = 2, SC_KIB = 4;
   __device__ static int dma_row(int l, int u) { return 8 * u + (l >> 3); }
   __device__ static int dma_off(int l, int u) { return 16 * ((l & 7) ^ (l >> 3) ^ u); }
   // chunk 4h + g of token row j = l % 16
@@ -187,7 +188,7 @@ struct PCodec<MOE_MXFP4_B32_A8> {
 
 template <int EPI>
 struct PEpi {
-  static constexpr int NMAT = EPI == EPI_SWIGLU ? 2 : 1;
+  static constexpr int NMAT = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) ? 2 : 1;
   static constexpr int WF = PWC / 16 / NMAT;   // 16-feature tiles per matrix per wave
   static constexpr int FULL_F = 4 * WF * 16;   // output features of a full item
 };
@@ -344,9 +345,6 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   const int wts_off = (half ? Ly::HALF_ACT : Ly::FULL_ACT) * 1024;
   constexpr int LSC = Cd::SCALE_DMA ? 1 : 0;  // the last load moves the packet scales
   constexpr bool A8 = C == MOE_MXFP4_B32_A8;   // the last two loads move the exponents
-  // W4A8: the activation exponents are indexed by 16-row tiles of the padded row space in which
-  // group g starts at row 128 * cum_blocks[g]
-  const int prow0 = planned ? PRB * a.cum_blocks[g] + (row0 - rbeg) : row0;
 #pragma unroll
   for (int q = 0; q < L; ++q) {
     const int nact = half ? H : 2 * H;
@@ -361,12 +359,18 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       qdst[q] = Ly::SC_OFF + wave * 256;
       qstride[q] = 64;
     } else if (A8 && q == L - 1) {
-      // the item's 16 row tiles x 4 blocks x 16 tokens of activation exponents of the step:
-      // lane l moves chunk l % 4 of row tile l / 4
-      qsrc[q] = (const uint8_t*)a.act_scale + ((size_t)(prow0 / 16 + (lane >> 2)) * (a.K / 32)) * 16 +
-                (size_t)(lane & 3) * 16;
-      qdst[q] = Ly::SC_OFF + 2048;
-      qstride[q] = 64;
+      // activation exponents of the step (4 bytes per row) for 4 row tiles from this wave's first:
+      // lane l moves row rt0 * 16 + l, gathered like the activation rows; rows past the group's
+      // end read the zero row (exponent byte 0 with zero codes)
+      const int rt0 = half ? wave : 2 * wave;
+      const int rr = rt0 * 16 + lane;
+      const int r = row0 + (rr < nr ? rr : 0);
+      int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
+      if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
+      qsrc[q] = (rr >= nr && a.zero_row) ? (const uint8_t*)a.zero_row
+                                         : (const uint8_t*)a.act_scale + (size_t)src * (a.K / 32);
+      qdst[q] = Ly::SC_OFF + 2048 + rt0 * 64;
+      qstride[q] = 4;
     } else if (LSC && q == L - 1) {
       // this wave's 4 column tiles' e8m0 bytes of the step's packets (64 per tile): lane l
       // fetches 16 bytes of tile (l % 16) / 4; lanes 16..63 repeat lanes 0..15
@@ -399,7 +403,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   }
   auto dma_one = [&](int q, int step) {
     const int st = kstep0 + min(step, nsteps - 1);
-    if (A8 && q == L - 2)
+    if (A8 && q >= L - 2)
       __builtin_amdgcn_global_load_lds((const void*)(qsrc[q] + (size_t)st * qstride[q]),
                                        (lds_void*)(lds + (step % D) * STAGE_B + qdst[q]), 4, 0, 0);
     else
@@ -459,7 +463,8 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
         af8[t] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
         sa[t] = base[Ly::SC_OFF + wave * 256 + t * 64 + lane];
       }
-      const uint8_t* sbp = base + Ly::SC_OFF + 2048 + wrow * 8 * 64 + lane;
+      // exponent of (token l % 16, block l / 16) of row tile rt: byte rt * 64 + 4 (l % 16) + l / 16
+      const uint8_t* sbp = base + Ly::SC_OFF + 2048 + wrow * 8 * 64 + 4 * j16 + (lane >> 4);
       u32x4 b0n = *(const u32x4*)(base + aoff[0]), b1n = *(const u32x4*)(base + aoff[1]);
       int sbn = sbp[0];
 #pragma unroll
@@ -574,6 +579,43 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     }
     return;
   }
+  if constexpr (EPI == EPI_SWIGLU_Q8) {
+    // h = SiLU(g) * u, rounded to bf16 (the type the layer keeps h in), then OCP MXFP8 for the W4A8
+    // down product. This wave's 32 h columns of a row (2 tiles x 16) are exactly one 32-block: the
+    // lane's 8 values and those of the lanes 16 and 32 apart (same row) make it, so the block
+    // maximum takes two xor shuffles. Codes go to out ([row][ldo] bytes), exponents to out_scale
+    // ([row][ldo / 32]).
+    static_assert(WF == 2, "one MX block per wave and row");
+    const int hc0 = ftile[0] * 16;  // this wave's first h column
+    uint8_t* osc = (uint8_t*)a.out_scale;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rr = wrow * 128 + j * 16 + j16;
+      float v[2][4];
+      float amax = 0.f;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[f][i] = (float)(__bf16)(silu(acc[f][j][i] * mcur[0]) * (acc[WF + f][j][i] * mcur[1]));
+          amax = __builtin_fmaxf(amax, __builtin_fabsf(v[f][i]));
+        }
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+      const int X = mxfp8_exponent(amax);
+      if (rr >= nr) continue;
+      const size_t row = (size_t)((long long)row0 + rr + rowoff);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w |= e4m3_rne_sat(__builtin_amdgcn_ldexpf(v[f][i], -X)) << (8 * i);
+        *(uint32_t*)(out + row * ldo + hc0 + 16 * f + 4 * g4) = w;
+      }
+      if (g4 == 0) osc[row * (ldo / 32) + hc0 / 32] = (uint8_t)(X + 127);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int rr = wrow * 128 + j * 16 + j16;
@@ -618,7 +660,6 @@ static hipError_t launch_codec(int c, const GroupedArgs& a, int max_units, hipSt
   if (c == MOE_BF16) return launch_p<MOE_BF16, EPI>(a, max_units, st);
   if (c == MOE_FP8_E4M3_B128) return launch_p<MOE_FP8_E4M3_B128, EPI>(a, max_units, st);
   if (c == MOE_MXFP4_B32) return launch_p<MOE_MXFP4_B32, EPI>(a, max_units, st);
-  if (c == MOE_MXFP4_B32_A8) return launch_p<MOE_MXFP4_B32_A8, EPI>(a, max_units, st);
   return hipErrorInvalidValue;
 }
 
@@ -655,6 +696,20 @@ static bool prefill_codec_ok(int c, int K) {
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down) {
   return act == MOE_BF16 && prefill_codec_ok(cr, K) && prefill_codec_ok(cs, K) &&
          N_gateup % (2 * PEpi<EPI_SWIGLU>::FULL_F) == 0 && N_down % (2 * PEpi<EPI_PLAIN>::FULL_F) == 0;
+}
+
+// W4A8 routed groups [g_begin, g_end): gate/up with the MXFP8-writing SwiGLU epilogue, or down.
+hipError_t launch_w4a8_prefill(int epi, const GroupedArgs& a, int max_units, hipStream_t st) {
+  if (!prefill_codec_ok(MOE_MXFP4_B32_A8, a.K) || !a.act_scale) return hipErrorInvalidValue;
+  if (epi == EPI_SWIGLU_Q8) {
+    if (a.N % (2 * PEpi<EPI_SWIGLU_Q8>::FULL_F) || !a.out_scale) return hipErrorInvalidValue;
+    return launch_p<MOE_MXFP4_B32_A8, EPI_SWIGLU_Q8>(a, max_units, st);
+  }
+  if (epi == EPI_PLAIN) {
+    if (a.N % (2 * PEpi<EPI_PLAIN>::FULL_F)) return hipErrorInvalidValue;
+    return launch_p<MOE_MXFP4_B32_A8, EPI_PLAIN>(a, max_units, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 // One launch over all groups when routed and shared experts share a format; else one launch

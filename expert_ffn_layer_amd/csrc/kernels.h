@@ -5,7 +5,9 @@
 
 namespace moe {
 
-enum { EPI_SWIGLU = 0, EPI_PLAIN = 1, EPI_F32 = 2 };
+// EPI_SWIGLU_Q8: SiLU(g) * u rounded to bf16, then written as MXFP8 (codes to out, one e8m0
+// exponent per 32 columns to out_scale) for a W4A8 down product
+enum { EPI_SWIGLU = 0, EPI_PLAIN = 1, EPI_F32 = 2, EPI_SWIGLU_Q8 = 3 };
 
 // Arguments of a grouped GEMM over a "row space": group g owns rows
 // [group_range[2g], group_range[2g+1]). Row r reads activation row
@@ -43,7 +45,8 @@ struct GroupedArgs {
   int ksplit;  // > 1: fp32 output only; workgroup y sums K part y into out + y * M * ldo
   const void* zero_row;  // prefill: K zero activations that rows past a group's end read, or null
   int g_begin, g_end;    // prefill: groups of this launch (g_end <= g_begin: all groups)
-  const void* act_scale; // W4A8: e8m0 exponents of the MXFP8 activations (launch_quant_mxfp8 layout)
+  const void* act_scale; // W4A8: e8m0 exponents of the MXFP8 activations, [row][K/32], gathered as act
+  void* out_scale;       // EPI_SWIGLU_Q8: e8m0 exponents of the output, [row][N/64] (N = 2 I)
 };
 
 // Output features (in units of 16) per decode work item, chosen from the instantiated set so an
@@ -65,6 +68,7 @@ hipError_t launch_grouped_decode(int act, int epi, int cr, int cs, const Grouped
                                  int max_row_blocks, hipStream_t st);
 hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const GroupedArgs& a, int max_tiles,
                                   hipStream_t st);
+hipError_t launch_w4a8_prefill(int epi, const GroupedArgs& a, int max_units, hipStream_t st);
 int prefill_row_tile();
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down);
 bool prefill_scores_supported(int act, int K, int N);
@@ -82,11 +86,8 @@ hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int sha
                                 int32_t* slot_token, int32_t* pair_slot, int32_t* group_range, int32_t* cum_blocks,
                                 hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t st);
-// W4A8: bf16 rows -> MXFP8 codes (permuted row order) + exponents (padded 16-row-tile layout).
-size_t mxfp8_padded_rows(int P, int E);
-hipError_t launch_quant_mxfp8(const void* src, int lds_, const int32_t* gather, const int32_t* group_range,
-                              const int32_t* cum_blocks, int G, int K, int padded_rows, uint8_t* codes,
-                              uint8_t* scales, hipStream_t st);
+// W4A8: bf16 rows [rows][K] -> MXFP8 codes uint8[rows][K] + e8m0 exponents uint8[rows][K/32].
+hipError_t launch_quant_mxfp8(const void* src, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t launch_combine(int act, const void* y_perm, const int32_t* pair_slot, const float* w,
                           const void* y_shared, void* y, int T, int H, int k, hipStream_t st);
 
