@@ -35,6 +35,7 @@ constexpr size_t ALIGN = 256;
 size_t up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 int act_bytes(moe_dtype a) { return a == MOE_F32 ? 4 : 2; }
 int pad64(int n) { return (n + 63) / 64 * 64; }
+int pad256(int n) { return (n + 255) / 256 * 256; }
 constexpr int ROW_BLOCK = 64;
 
 bool valid_fmt(int f) { return f >= MOE_F32 && f <= MOE_MXFP4_B32_A8; }
@@ -51,7 +52,7 @@ moe_status packed_sizes(moe_dtype fmt, int count, int K, int N, size_t* bytes, s
   if (fmt == MOE_FP8_E4M3_B128 && (K % 128 || N % 128))
     return fail(MOE_ERR_INVALID_ARG, "fp8 block-128 scales need K, N multiples of 128 (K=%d N=%d)", K, N);
   if (fmt == MOE_MXFP4_B32 && N % 2) return fail(MOE_ERR_INVALID_ARG, "MXFP4 packs N=%d in pairs", N);
-  const size_t NT = pad64(N) / 16, KT = K / KP;
+  const size_t NT = pad256(N) / 16, KT = K / KP;
   *bytes = (size_t)count * NT * KT * PACKET_BYTES;
   if (fmt == MOE_FP8_E4M3_B128)
     *sbytes = (size_t)count * (K / 128) * (N / 128) * 4;
@@ -119,7 +120,7 @@ struct RouterPlan {
 };
 
 RouterPlan router_plan(const moe_shape& s) {
-  const int Ep = pad64(s.E);
+  const int Ep = pad256(s.E);  // the packed router has its features padded to a multiple of 256
   if (s.T >= 2048 && prefill_scores_supported(s.act, s.H, Ep)) {
     const int items = (s.T + 255) / 256 * (Ep / 256);
     int ks = (256 + items - 1) / items;
@@ -144,7 +145,7 @@ Ws ws_layout(const moe_shape& s) {
     o += up(bytes ? bytes : 1);
     return at;
   };
-  w.logits = take((size_t)router_plan(s).ksplit * s.T * pad64(s.E) * 4);
+  w.logits = take((size_t)router_plan(s).ksplit * s.T * pad256(s.E) * 4);
   w.idx = take(P * 4);
   w.w = take(P * 4);
   w.offsets = take(((size_t)s.E + 1) * 4);
@@ -196,7 +197,9 @@ moe_status check_weights(const moe_weights* w, moe_dtype fmt, const char* what) 
 moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const float* bias, int32_t* idx,
                     float* w, void* ws, const Ws& L, hipStream_t st) {
   if (s.T == 0) return MOE_OK;
-  const int Ep = pad64(s.E);
+  const RouterPlan rp = router_plan(s);
+  // scores of the padded experts: 256-wide MFMA tiles on the prefill kernel, 64 on the decode one
+  const int Ep = rp.prefill ? pad256(s.E) : pad64(s.E);
   GroupedArgs a{};
   a.group_range = nullptr;
   a.cum_blocks = nullptr;
@@ -214,7 +217,6 @@ moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const flo
   a.N = Ep;
   a.out = at<float>(ws, L.logits);
   a.ldo = Ep;
-  const RouterPlan rp = router_plan(s);
   a.ksplit = rp.ksplit;
   hipError_t e = rp.prefill ? launch_prefill_scores(a, st)
                             : launch_grouped_decode(s.act, EPI_F32, s.act, s.act, a, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);

@@ -70,7 +70,7 @@ using namespace moe;
 extern "C" __attribute__((visibility("hidden"))) hipError_t moe_launch_pack(int fmt, int count, int K, int N, const void* w,
                                       const void* scale, void* packed, void* packed_scale,
                                       hipStream_t stream) {
-  const int NT = (N + 63) / 64 * 4;  // features padded to a multiple of 64 with zeros
+  const int NT = (N + 255) / 256 * 16;  // features padded to a multiple of 256 with zeros
   const int KT = K / kp_of(fmt);
   long long total = (long long)count * NT * KT * 64;
   dim3 grid((unsigned)((total + 255) / 256)), block(256);

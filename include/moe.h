@@ -119,7 +119,7 @@ const char* moe_last_error(void);
  * F32, BF16, FP8, MXFP4), packet (nt, kt) at byte (nt*(K/KP) + kt)*1024, lane l of a packet
  * holding feature nt*16 + l%16 and reduction run kt*KP + (l/16)*KP/4 + [0, KP/4). FP8 scales
  * are copied unchanged; MXFP4 scales are regrouped one byte per lane per packet.
- * N is padded up to a multiple of 64 with zero features (only the router, N = E, needs it).
+ * N is padded up to a multiple of 256 with zero features (only the router, N = E, needs it).
  * Requirements: K a multiple of KP (and of 128 for FP8), N a multiple of 16 (128 for FP8, 2
  * for MXFP4) before padding. `packed_scale` may be NULL for F32 / BF16.
  * Router: pack Wr[H][E] as one K = H, N = E matrix in the `act` format.

@@ -75,13 +75,14 @@ def test_workspace_grows_with_tokens_and_shared_expert():
 
 def test_pack_sizes():
     assert N.moe_pack_size("bf16", 3, 4096, 1536) == (3 * 4096 * 1536 * 2, 0)
-    assert N.moe_pack_size("f32", 1, 256, 128) == (256 * 128 * 4, 0)
+    assert N.moe_pack_size("f32", 1, 256, 128) == (256 * 256 * 4, 0)  # 128 features pad to 256
     assert N.moe_pack_size("fp8", 2, 7168, 2048) == (2 * 7168 * 2048, 2 * 56 * 16 * 4)
     assert N.moe_pack_size("mxfp4", 1, 7168, 3072) == (7168 * 3072 // 2, 7168 * 3072 // 32)
     # W4A8 weights are stored and packed exactly as MXFP4
     assert N.moe_pack_size("mxfp4a8", 2, 7168, 3072) == N.moe_pack_size("mxfp4", 2, 7168, 3072)
-    # the router's E is padded to 64 features
-    assert N.moe_pack_size("bf16", 1, 256, 8) == (256 * 64 * 2, 0)
+    # the router's E is padded to 256 features (the width of one MFMA item)
+    assert N.moe_pack_size("bf16", 1, 256, 8) == (256 * 256 * 2, 0)
+    assert N.moe_pack_size("bf16", 1, 7168, 384) == (7168 * 512 * 2, 0)
     for fmt, K, Nn in (("fp8", 7168, 100), ("fp8", 100, 128), ("bf16", 48, 64), ("mxfp4", 128, 3)):
         with pytest.raises(N.MoeError):
             N.moe_pack_size(fmt, 1, K, Nn)
