@@ -52,7 +52,7 @@ def measured_traffic(config: str, path: str):
 
 
 # bounded CPU-oracle samples (tokens): about 10-30 s of oracle work per config
-CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4}
+CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4, "v4p": 6, "v4p-w4a8": 6}
 
 
 def log(*a):
@@ -64,7 +64,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8"],
+                    help="c1-c5: the layer configurations; v4p, v4p-w4a8: the V4-Pro-shaped layer at a "
+                         "prefill batch with MXFP4 / W4A8 routed experts")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=None)
@@ -88,7 +90,7 @@ def main():
 
     N.load()
     dev = torch.device("cuda:0")
-    spec = L.CONFIGS[args.config]
+    spec = L.workload(args.config)
     log("bench: generating %s on the device" % spec.name)
     lay = G.layer_on_device(spec, dev)
     pl = PackedLayer(spec, lay["Wr"], lay["routed"], lay["shared"], path=args.path)
@@ -174,9 +176,23 @@ def main():
                 + T * H * ab + R * I * ab)
     gu_flops = 4 * H * I * R
     gu_ms = stage_ms[names.index("gate_up")]
-    prefill = (T * k) / spec.E >= 64
+    a8 = spec.w_routed == "mxfp4a8"
+    prefill = a8 or (T * k) / spec.E >= 64
     traffic_b = measured_traffic(args.config, "prefill" if prefill else "decode")
-    if prefill:
+    if a8:
+        # W4A8: the gate/up stage is the x quantisation, the routed fp4 x fp8 GEMM (fp8 peak) and
+        # the shared expert's bf16 GEMM (bf16 peak); its peak is the FLOP-weighted blend, i.e.
+        # the stage's FLOPs over the time both GEMMs would take at their own peaks
+        fr, fs = 4 * H * I * T * k, 4 * H * I * (T if spec.shared else 0)
+        t_peak = fr / (MFMA_PEAK_TFLOPS["fp8"] * 1e12) + fs / (MFMA_PEAK_TFLOPS["bf16"] * 1e12)
+        peak = round(gu_flops / t_peak / 1e12, 1)
+        ach = gu_flops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": traffic_b,
+                "kernel": "gate/up stage: x to MXFP8, W4A8 routed GEMM (fp8 peak 5000), bf16 shared GEMM "
+                          "(bf16 peak 2500)",
+                "per_launch": {"flops": gu_flops, "routed_flops": fr, "shared_flops": fs, "ms": round(gu_ms, 4)}}
+    elif prefill:
         peak = MFMA_PEAK_TFLOPS["bf16" if spec.act == "bf16" else "f32"]
         ach = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",

@@ -434,8 +434,9 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   for (int m = 0; m < NMAT; ++m)
     mcur[m] = scale_mantissa(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), (kstep0 * PBK) >> 7)));
 
-  auto step_body = [&](int step, auto first_of_block) {
+  auto step_body = [&](int step, auto first_of_block, auto row_tiles) {
     constexpr bool RESCALE = SCALED && decltype(first_of_block)::value;
+    constexpr int MTA = decltype(row_tiles)::value;  // row tiles of this wave that hold group rows
     // this wave's loads of `step` have landed; after the barrier, every wave's have, and no
     // wave still reads the slot the next DMA overwrites (that of step - 1)
     MOE_WAIT_VMCNT((D - 2) * L);
@@ -467,11 +468,12 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       const uint8_t* sbp = base + Ly::SC_OFF + 2048 + wrow * 8 * 64 + 4 * j16 + (lane >> 4);
       u32x4 b0n = *(const u32x4*)(base + aoff[0]), b1n = *(const u32x4*)(base + aoff[1]);
       int sbn = sbp[0];
+      constexpr int QA = (L + MTA - 1) / MTA;  // DMA loads per row tile
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < MTA; ++j) {
         const u32x4 b0 = b0n, b1 = b1n;
         const int sb = sbn;
-        if (j + 1 < 8) {
+        if (j + 1 < MTA) {
           b0n = *(const u32x4*)(base + aoff[0] + (j + 1) * H * 1024);
           b1n = *(const u32x4*)(base + aoff[1] + (j + 1) * H * 1024);
           sbn = sbp[(j + 1) * 64];
@@ -482,8 +484,8 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
         for (int t = 0; t < NT; ++t)
           acc[t][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af8[t], bf, acc[t][j], 4, 0, 0, sa[t], 0, sb);
 #pragma unroll
-        for (int u = 0; u < QJ; ++u)
-          if (j * QJ + u < L) dma_one(j * QJ + u, step + D - 1);
+        for (int u = 0; u < QA; ++u)
+          if (j * QA + u < L) dma_one(j * QA + u, step + D - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       return;
@@ -527,10 +529,25 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int step = 0; step < nsteps; step += SPB) {
-    step_body(step, std::true_type{});
+  auto run_steps = [&](auto row_tiles) {
+    for (int step = 0; step < nsteps; step += SPB) {
+      step_body(step, std::true_type{}, row_tiles);
 #pragma unroll
-    for (int u = 1; u < SPB; ++u) step_body(step + u, std::false_type{});
+      for (int u = 1; u < SPB; ++u) step_body(step + u, std::false_type{}, row_tiles);
+    }
+  };
+  if constexpr (A8) {
+    // W4A8 leaves the row tiles past the group's end out of the MFMA stream, 32 rows at a time:
+    // each wave runs the loop compiled for 2, 4, 6 or 8 row tiles, chosen once per item, so the
+    // stream has no branches. Their accumulators stay zero and are never stored. (Padding MFMAs
+    // of the bf16-operand codecs read zero rows and cost little; fp8 MFMAs cost twice the issue.)
+    const int wave_rows = nr - wrow * PRB;  // group rows in this wave's 128-row half
+    if (wave_rows > 96) run_steps(std::integral_constant<int, 8>{});
+    else if (wave_rows > 64) run_steps(std::integral_constant<int, 6>{});
+    else if (wave_rows > 32) run_steps(std::integral_constant<int, 4>{});
+    else run_steps(std::integral_constant<int, 2>{});
+  } else {
+    run_steps(std::integral_constant<int, 8>{});
   }
   MOE_WAIT_VMCNT(0);  // the clamped tail DMAs must land before the workgroup's LDS is released
 

@@ -88,6 +88,18 @@ CONFIGS = {
                     seed=5),
 }
 
+# Further workloads measured beside the configurations above: the DeepSeek-V4-Pro-shaped layer at a
+# prefill batch (T * k = 64 E, where the path switches to the MFMA kernel), with MXFP4 routed
+# experts and bf16 activations, and with W4A8 routed experts (activations quantised to MXFP8).
+EXTRA = {
+    "v4p": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096),
+    "v4p-w4a8": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-w4a8", T=4096, w_routed="mxfp4a8"),
+}
+
+
+def workload(name: str) -> LayerSpec:
+    return CONFIGS[name] if name in CONFIGS else EXTRA[name]
+
 
 # ----------------------------------------------------------------------------------------------
 # dense draws and stored formats

@@ -254,13 +254,10 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
 
 # ------------------------------------------------------------------ full-size layers
 
-FULL = ["c2", "c3", "c4", "c5", "v4pro-prefill", "v4pro-prefill-w4a8"]
 # the DeepSeek-V4-Pro-shaped layer at a prefill batch: MXFP4 routed experts in the prefill
 # kernel, the bf16 shared expert in a launch of its own; and the same layer with W4A8 routed
 # experts (MXFP8 activations on the block-scaled MFMA)
-EXTRA = {"v4pro-prefill": L.CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096),
-         "v4pro-prefill-w4a8": L.CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-w4a8", T=4096,
-                                                       w_routed="mxfp4a8")}
+FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8"]
 
 
 @pytest.mark.slow
@@ -268,7 +265,7 @@ EXTRA = {"v4pro-prefill": L.CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-pref
 def test_full_size_layer(cfg):
     """The bench's launch configuration at full size: routing and permutation identical for
     every token, outputs against the oracle on sampled tokens."""
-    spec = L.CONFIGS[cfg] if cfg in L.CONFIGS else EXTRA[cfg]
+    spec = L.workload(cfg)
     say("full-size", cfg, spec)
     lay, pl = build(spec, DEV)
     y, idx, w = run(spec, lay, pl)
