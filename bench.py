@@ -29,10 +29,13 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 TRAFFIC = {
     "c2": {"sha": "d19114cde11b4a36", "bytes": 3176825079},  # gate/up decode kernel
     "c5": {"sha": "1b2179f3108af01c", "bytes": 16404419934},  # gate/up prefill kernel
+    # the W4A8 gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared bf16 GEMM
+    "v4p-w4a8": {"sha": "92298b6e2cc2d506", "bytes": 10134626545},
 }
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
-                  "prefill": ("gemm_prefill.hip", "common.h", "kernels.h")}
+                  "prefill": ("gemm_prefill.hip", "common.h", "kernels.h"),
+                  "w4a8": ("gemm_prefill.hip", "quant.hip", "common.h", "kernels.h")}
 
 
 def kernel_sha(path: str) -> str:
@@ -178,7 +181,7 @@ def main():
     gu_ms = stage_ms[names.index("gate_up")]
     a8 = spec.w_routed == "mxfp4a8"
     prefill = a8 or (T * k) / spec.E >= 64
-    traffic_b = measured_traffic(args.config, "prefill" if prefill else "decode")
+    traffic_b = measured_traffic(args.config, "w4a8" if a8 else "prefill" if prefill else "decode")
     if a8:
         # W4A8: the gate/up stage is the x quantisation, the routed fp4 x fp8 GEMM (fp8 peak) and
         # the shared expert's bf16 GEMM (bf16 peak); its peak is the FLOP-weighted blend, i.e.
