@@ -73,7 +73,7 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=None)
-    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read HBM ceiling")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the measured ceilings (streaming HBM read, sustained MFMA rate)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
                     help="end with one plain copy kernel of this size (byte-counter calibration)")
     args = ap.parse_args()
@@ -162,6 +162,23 @@ def main():
         ceiling = round(5 * buf.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
         del buf
 
+    mfma_ceiling = None
+    a8 = spec.w_routed == "mxfp4a8"
+    if not args.no_ceiling and (a8 or (spec.T * spec.k) / spec.E >= 64):
+        # the matrix-core rates this GPU sustains with GEMM-like (changing, random) operands:
+        # register-only MFMA bursts of the GEMMs' instruction kinds, 2 waves per SIMD
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        mfma_ceiling = {}
+        for kind, name in ((0, "bf16 16x16x32"), (1, "fp4 x fp8 16x16x128")) if a8 else ((0, "bf16 16x16x32"),):
+            iters = 2048 if kind else 8192
+            G.mfma_burst(kind, iters, 512, sink)
+            m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            m0.record()
+            fl = sum(G.mfma_burst(kind, iters, 512, sink) for _ in range(5))
+            m1.record()
+            torch.cuda.synchronize()
+            mfma_ceiling[name] = round(fl / (m0.elapsed_time(m1) * 1e-3) / 1e12, 1)
+
     if args.calib_copy:
         # one plain copy of known size, the reference that scales the byte counters of a --pmc run
         nb = args.calib_copy << 20
@@ -179,7 +196,6 @@ def main():
                 + T * H * ab + R * I * ab)
     gu_flops = 4 * H * I * R
     gu_ms = stage_ms[names.index("gate_up")]
-    a8 = spec.w_routed == "mxfp4a8"
     prefill = a8 or (T * k) / spec.E >= 64
     traffic_b = measured_traffic(args.config, "w4a8" if a8 else "prefill" if prefill else "decode")
     if a8:
@@ -195,12 +211,18 @@ def main():
                 "kernel": "gate/up stage: x to MXFP8, W4A8 routed GEMM (fp8 peak 5000), bf16 shared GEMM "
                           "(bf16 peak 2500)",
                 "per_launch": {"flops": gu_flops, "routed_flops": fr, "shared_flops": fs, "ms": round(gu_ms, 4)}}
+        if mfma_ceiling:
+            # the time both GEMMs would take at the measured sustained rates, over the stage time
+            t_meas = fr / (mfma_ceiling["fp4 x fp8 16x16x128"] * 1e12) + fs / (mfma_ceiling["bf16 16x16x32"] * 1e12)
+            roof["frac_of_measured_mfma"] = round(t_meas / (gu_ms * 1e-3), 4)
     elif prefill:
         peak = MFMA_PEAK_TFLOPS["bf16" if spec.act == "bf16" else "f32"]
         ach = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "traffic": traffic_b, "kernel": "gate/up grouped GEMM",
                 "per_launch": {"flops": gu_flops, "ms": round(gu_ms, 4)}}
+        if mfma_ceiling:
+            roof["frac_of_measured_mfma"] = round(ach / mfma_ceiling["bf16 16x16x32"], 4)
     else:
         ach = gu_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -235,6 +257,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "hbm_read_ceiling_GBps": ceiling,
+        "mfma_sustained_TFLOPs": mfma_ceiling,
         "cpu_baseline": None,
     }
 

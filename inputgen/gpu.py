@@ -44,6 +44,7 @@ def lib():
         _lib.gen_fill_mxfp4.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_copy.argtypes = [p, p, i64, p]
         _lib.gen_stream_read.argtypes = [p, i64, p, p]
+        _lib.gen_mfma_burst.argtypes = [i32, i32, i32, p, p]
     return _lib
 
 
@@ -71,6 +72,12 @@ def copy(src, dst):
     n = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() >= n
     _chk(lib().gen_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, _stream()), "copy")
+
+
+def mfma_burst(kind: int, iters: int, blocks: int, sink) -> float:
+    """One MFMA burst (kind 0: bf16 16x16x32, kind 1: fp4 x fp8 16x16x128); returns its FLOPs."""
+    _chk(lib().gen_mfma_burst(kind, iters, blocks, ctypes.c_void_p(sink.data_ptr()), _stream()), "mfma_burst")
+    return float(blocks) * 8 * iters * 16 * (16384 if kind == 0 else 65536)
 
 
 def stream_read(src, sink):
