@@ -131,8 +131,8 @@ RouterPlan router_plan(const moe_shape& s) {
 }
 
 struct Ws {
-  size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, zero, h, y_perm,
-      y_shared, xq, xs, hq, hs, total;
+  size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, block_group, zero, h,
+      y_perm, y_shared, xq, xs, hq, hs, total;
 };
 
 Ws ws_layout(const moe_shape& s) {
@@ -155,6 +155,9 @@ Ws ws_layout(const moe_shape& s) {
   w.hist = take((size_t)permute_blocks((int)P) * s.E * 4);
   w.group_range = take(((size_t)s.E + 1) * 8);
   w.cum_blocks = take(((size_t)s.E + 2) * 4);
+  // one entry per row block: at most one partial block per group plus the full ones (64-row
+  // blocks at decode, 128 at prefill)
+  w.block_group = take(((size_t)s.E + 2 + (R + ROW_BLOCK - 1) / ROW_BLOCK) * 4);
   w.h = take(R * s.I * ab);
   w.y_perm = take(P * s.H * ab);
   w.y_shared = take(S * s.T * s.H * ab);
@@ -244,7 +247,8 @@ moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int3
   hipError_t e;
   if (permute_small_ok(s.T * s.k, s.E)) {
     e = launch_permute_small(idx, s.T, s.k, s.E, s.I_shared ? 1 : 0, ROW_BLOCK, off, st_, ps,
-                             with_plan ? at<int32_t>(ws, L.group_range) : nullptr, at<int32_t>(ws, L.cum_blocks), st);
+                             with_plan ? at<int32_t>(ws, L.group_range) : nullptr, at<int32_t>(ws, L.cum_blocks),
+                             at<int32_t>(ws, L.block_group), st);
     if (planned) *planned = with_plan;
   } else {
     e = launch_permute(idx, s.T, s.k, s.E, off, st_, ps, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.hist), st);
@@ -274,7 +278,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   hipError_t e = hipSuccess;
   uint32_t* zero = prefill ? at<uint32_t>(ws, L.zero) : nullptr;
   const int zero_words = (int)((size_t)std::max(s.H, s.I) * act_bytes(s.act) / 4);
-  if (!plan_ready || prefill) e = launch_plan(off, s.E, P, s.T, S, rb, gr, cb, zero, zero_words, st);
+  int32_t* bg = at<int32_t>(ws, L.block_group);
+  if (!plan_ready || prefill) e = launch_plan(off, s.E, P, s.T, S, rb, gr, cb, bg, zero, zero_words, st);
   if (e != hipSuccess) return hip_status(e, "plan");
   moe_status rs;
   if (ev && (rs = record(ev[0], st)) != MOE_OK) return rs;
@@ -284,6 +289,7 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.zero_row = zero;
   a.group_range = gr;
   a.cum_blocks = cb;
+  a.block_group = bg;
   a.G = G;
   a.shared_group = S ? s.E : -1;
   a.P = P;

@@ -377,13 +377,20 @@ __global__ void __launch_bounds__(256) grouped_decode_kernel(GroupedArgs a) {
   int g = 0, blk = rbi;
   if (a.cum_blocks) {
     if (rbi >= a.cum_blocks[a.G]) return;
-    int lo = 0, hi = a.G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.cum_blocks[mid] <= rbi) lo = mid; else hi = mid - 1;
+    if (a.block_group) {
+      // one load: group and block within it
+      const int gb = a.block_group[rbi];
+      g = gb >> 16;
+      blk = gb & 0xFFFF;
+    } else {
+      int lo = 0, hi = a.G - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.cum_blocks[mid] <= rbi) lo = mid; else hi = mid - 1;
+      }
+      g = lo;
+      blk = rbi - a.cum_blocks[g];
     }
-    g = lo;
-    blk = rbi - a.cum_blocks[g];
   } else if (rbi * RB >= a.M) {
     return;
   }

@@ -267,16 +267,26 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   bool half = false;
   if (planned) {
     const int gi = item + ibase;
-    int lo = gb, hi = ge - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.cum_blocks[mid] * (ntn >> 1) <= gi) lo = mid; else hi = mid - 1;
+    // 128-row block gi / (ntn / 2) of the row space: its group and place from the plan's table
+    // (one load), else a search over cum_blocks
+    int bin;
+    if (a.block_group) {
+      const int gbk = a.block_group[gi / (ntn >> 1)];
+      g = gbk >> 16;
+      bin = gbk & 0xFFFF;
+    } else {
+      int lo = gb, hi = ge - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.cum_blocks[mid] * (ntn >> 1) <= gi) lo = mid; else hi = mid - 1;
+      }
+      g = lo;
+      bin = gi / (ntn >> 1) - a.cum_blocks[g];
     }
-    g = lo;
     rbeg = a.group_range[2 * g];
     rend = a.group_range[2 * g + 1];
-    const int mt = a.cum_blocks[g + 1] - a.cum_blocks[g];  // 128-row blocks of the group
-    const int li = gi - a.cum_blocks[g] * (ntn >> 1);
+    const int mt = (rend - rbeg + PRB - 1) / PRB;  // 128-row blocks of the group
+    const int li = bin * (ntn >> 1) + gi % (ntn >> 1);
     if constexpr (Cd::HALF_ONLY) {
       int blk;
       item_tiles(li, mt, ntn >> 1, blk, ntile);

@@ -18,6 +18,7 @@ enum { EPI_SWIGLU = 0, EPI_PLAIN = 1, EPI_F32 = 2, EPI_SWIGLU_Q8 = 3 };
 struct GroupedArgs {
   const int32_t* group_range;
   const int32_t* cum_blocks;  // prefix count of row blocks per group (block = RB rows)
+  const int32_t* block_group; // per row block b: (group << 16) | (b - cum_blocks[group]), or null
   int G;
   int shared_group;  // group index of the shared expert, or -1
   int P;
@@ -74,7 +75,8 @@ bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down)
 bool prefill_scores_supported(int act, int K, int N);
 hipError_t launch_prefill_scores(const GroupedArgs& a, hipStream_t st);
 hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
-                       int32_t* group_range, int32_t* cum_blocks, uint32_t* zero, int zero_words, hipStream_t st);
+                       int32_t* group_range, int32_t* cum_blocks, int32_t* block_group, uint32_t* zero, int zero_words,
+                       hipStream_t st);
 hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
                        int32_t* idx, float* w, hipStream_t st);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
@@ -84,7 +86,7 @@ int permute_blocks(int P);
 bool permute_small_ok(int P, int E);
 hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int shared, int rb, int32_t* offsets,
                                 int32_t* slot_token, int32_t* pair_slot, int32_t* group_range, int32_t* cum_blocks,
-                                hipStream_t st);
+                                int32_t* block_group, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t st);
 // W4A8: bf16 rows [rows][K] -> MXFP8 codes uint8[rows][K] + e8m0 exponents uint8[rows][K/32].
 hipError_t launch_quant_mxfp8(const void* src, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t st);

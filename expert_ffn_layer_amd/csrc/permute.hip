@@ -146,10 +146,18 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 // cannot produce rows outside the buffers. It also clears `zero` (zero_words words): the zero
 // activations the prefill GEMM feeds to the padding rows of a group's last tile.
 // ------------------------------------------------------------------------------------------
+// block_group[b] = (g << 16) | (b - cum_blocks[g]) for every row block b of group g: the GEMM
+// kernels find an item's group and its place in it with one load (no search over cum_blocks).
+__device__ __forceinline__ void write_block_group(const int32_t* cum, int G, int32_t* block_group, int tid,
+                                                  int nthreads) {
+  for (int g = tid; g < G; g += nthreads)
+    for (int b = cum[g]; b < cum[g + 1]; ++b) block_group[b] = (g << 16) | (b - cum[g]);
+}
+
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ off, int E, int P, int T,
                                                      int shared, int rb, int32_t* __restrict__ group_range,
-                                                     int32_t* __restrict__ cum_blocks, uint32_t* __restrict__ zero,
-                                                     int zero_words) {
+                                                     int32_t* __restrict__ cum_blocks, int32_t* __restrict__ block_group,
+                                                     uint32_t* __restrict__ zero, int zero_words) {
   __shared__ int32_t blk[2048], tmp[2048];
   for (int i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
   const int G = E + (shared ? 1 : 0);
@@ -169,13 +177,19 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   __syncthreads();
   const int total = block_exclusive_scan(blk, tmp, G);
   for (int g = threadIdx.x; g < G; g += blockDim.x) cum_blocks[g] = blk[g];
-  if (threadIdx.x == 0) cum_blocks[G] = total;
+  if (threadIdx.x == 0) {
+    cum_blocks[G] = total;
+    blk[G] = total;
+  }
+  __syncthreads();
+  write_block_group(blk, G, block_group, threadIdx.x, blockDim.x);
 }
 
 hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
-                       int32_t* group_range, int32_t* cum_blocks, uint32_t* zero, int zero_words, hipStream_t st) {
+                       int32_t* group_range, int32_t* cum_blocks, int32_t* block_group, uint32_t* zero, int zero_words,
+                       hipStream_t st) {
   if (E + 1 > 2048) return hipErrorInvalidValue;
-  plan_kernel<<<1, 1024, 0, st>>>(expert_offsets, E, P, T, shared, rb, group_range, cum_blocks, zero,
+  plan_kernel<<<1, 1024, 0, st>>>(expert_offsets, E, P, T, shared, rb, group_range, cum_blocks, block_group, zero,
                                   zero ? zero_words : 0);
   return hipGetLastError();
 }
@@ -192,7 +206,7 @@ constexpr int SMALL_P = SMALL_THR * SMALL_CHUNKS;
 __global__ void __launch_bounds__(SMALL_THR) permute_small_kernel(
     const int32_t* __restrict__ idx, int P, int k, int E, int T, int shared, int rb,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot_token, int32_t* __restrict__ pair_slot,
-    int32_t* __restrict__ group_range, int32_t* __restrict__ cum_blocks) {
+    int32_t* __restrict__ group_range, int32_t* __restrict__ cum_blocks, int32_t* __restrict__ block_group) {
   __shared__ int32_t wcnt[16 * SMALL_E];
   __shared__ int32_t run[2048], tmp[2048];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -271,18 +285,23 @@ __global__ void __launch_bounds__(SMALL_THR) permute_small_kernel(
   __syncthreads();
   const int nblk = block_exclusive_scan(tmp, run, G);
   for (int g = tid; g < G; g += SMALL_THR) cum_blocks[g] = tmp[g];
-  if (tid == 0) cum_blocks[G] = nblk;
+  if (tid == 0) {
+    cum_blocks[G] = nblk;
+    tmp[G] = nblk;
+  }
+  __syncthreads();
+  write_block_group(tmp, G, block_group, tid, SMALL_THR);
 }
 
 bool permute_small_ok(int P, int E) { return P <= SMALL_P && E <= SMALL_E; }
 
 hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int shared, int rb, int32_t* offsets,
                                 int32_t* slot_token, int32_t* pair_slot, int32_t* group_range, int32_t* cum_blocks,
-                                hipStream_t st) {
+                                int32_t* block_group, hipStream_t st) {
   const int P = T * k;
   if (!permute_small_ok(P, E)) return hipErrorInvalidValue;
   permute_small_kernel<<<1, SMALL_THR, 0, st>>>(idx, P, k, E, T, shared, rb, offsets, slot_token, pair_slot,
-                                                group_range, cum_blocks);
+                                                group_range, cum_blocks, block_group);
   return hipGetLastError();
 }
 
