@@ -292,3 +292,58 @@ def test_full_size_layer(cfg):
     err = rel_fro(to_f64(y)[tokens], ref)
     say("  rel. Frobenius error on sampled tokens %.3e (bound %.0e)" % (err, tol_of(spec)))
     assert err <= tol_of(spec)
+
+
+# ------------------------------------------------------------------ seeded sweep of random small layers
+
+def _sweep_specs(n=24, seed=2024):
+    """Random small layers over the supported combinations: formats, shared expert or not,
+    Zipf or uniform routing, k up to 8, group sizes from empty to several 128-row blocks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        act = "f32" if i % 8 == 0 else "bf16"
+        if act == "f32":
+            wr = ws = "f32"
+        else:
+            wr = str(rng.choice(["bf16", "fp8", "mxfp4", "mxfp4a8"]))
+            ws = str(rng.choice(["bf16", "fp8", "mxfp4"]))
+        prefill_shape = wr == "mxfp4a8" or rng.random() < 0.5
+        H = int(rng.choice([512, 1024])) if prefill_shape else int(rng.choice([256, 384, 512]))
+        I = int(rng.choice([256, 512])) if prefill_shape else int(rng.choice([128, 256, 384]))
+        E = int(rng.choice([4, 8, 16, 40]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 7, 33, 150, 420]))
+        zipf = bool(rng.random() < 0.5) and E >= 8
+        out.append(L.LayerSpec("sw%d" % i, T=T, H=H, E=E, k=k, I=I, shared=bool(rng.random() < 0.5), act=act,
+                               w_routed=wr, w_shared=ws, router="zipf" if zipf else "uniform",
+                               zipf_alpha=1.1 if zipf else 0.0, calib_tokens=256, seed=100 + i))
+    return out
+
+
+SWEEP = _sweep_specs()
+
+
+@pytest.mark.parametrize("spec", SWEEP, ids=[s.name for s in SWEEP])
+def test_layer_random_sweep(spec):
+    """Every random layer on the automatic path, and on both explicit paths where the shape allows
+    them: routing identical to the oracle's, outputs within the format's bound."""
+    paths = ["auto"]
+    if spec.w_routed != "mxfp4a8":
+        paths.append("decode")
+    if _prefill_ok(spec) and spec.w_routed != "mxfp4a8":
+        paths.append("prefill")
+    if spec.w_routed == "mxfp4a8" and not _prefill_ok(spec):
+        pytest.skip("W4A8 needs the prefill shape constraints")
+    say("sweep", spec)
+    ref = None
+    for path in paths:
+        lay, pl = build(spec, DEV, path)
+        y, idx, w = run(spec, lay, pl)
+        if ref is None:
+            ref = oracle_full(spec, lay)
+        assert np.array_equal(idx.cpu().numpy(), ref["topk_idx"])
+        assert np.max(np.abs(w.cpu().numpy() - ref["topk_w"])) <= 1e-5
+        err = rel_fro(to_f64(y), ref["y"])
+        say("  %s: rel. Frobenius error %.3e (bound %.0e)" % (path, err, tol_of(spec)))
+        assert err <= tol_of(spec)
