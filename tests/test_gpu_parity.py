@@ -347,3 +347,49 @@ def test_layer_random_sweep(spec):
         err = rel_fro(to_f64(y), ref["y"])
         say("  %s: rel. Frobenius error %.3e (bound %.0e)" % (path, err, tol_of(spec)))
         assert err <= tol_of(spec)
+
+
+# ------------------------------------------------------------------ graph capture
+
+GRAPH_SPECS = [
+    ("decode-bf16-shared", L.LayerSpec("g1", T=45, H=512, E=12, k=3, I=256, shared=True, router="zipf",
+                                       zipf_alpha=1.0, calib_tokens=512, seed=61)),
+    ("prefill-fp8", L.LayerSpec("g2", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="fp8",
+                                w_shared="fp8", seed=62)),
+    ("w4a8", L.LayerSpec("g3", T=200, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
+                         w_shared="bf16", seed=63)),
+]
+
+
+@pytest.mark.parametrize("name,spec", GRAPH_SPECS, ids=[g[0] for g in GRAPH_SPECS])
+def test_layer_forward_captures_into_a_graph(name, spec):
+    """Every entry point only enqueues on its stream (no host synchronisation, no allocation, no
+    memset), so a whole layer forward can be captured in a HIP graph. The graph is replayed several
+    times, with eager work and synchronisations between the replays, and every replay must equal
+    the eager forward bit for bit (the plan and the zero row are rewritten by kernels each call)."""
+    say("graph", name, spec)
+    lay, pl = build(spec, DEV)
+    y_ref, idx_ref, w_ref = run(spec, lay, pl)
+    x = lay["x"].view(torch.bfloat16)
+    y = torch.empty_like(y_ref)
+    idx = torch.empty_like(idx_ref)
+    w = torch.empty_like(w_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pl.forward(x, lay["bias"], y, idx, w)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pl.forward(x, lay["bias"], y, idx, w)
+    for rep in range(4):
+        y.fill_(0)
+        idx.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx_ref), rep
+        assert torch.equal(w, w_ref), rep
+        assert torch.equal(y, y_ref), rep
+        # eager work between the replays, on the same workspace
+        run(spec, lay, pl)
