@@ -128,6 +128,32 @@ def main():
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / args.steps
 
+    # The same forward captured once in a HIP graph and replayed K times: one host launch per layer
+    # instead of one per kernel (the plan lives on the device, so nothing is read back).
+    graph_ms = None
+    try:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            step()
+        torch.cuda.current_stream().wait_stream(gs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = round(g0.elapsed_time(g1) / args.steps, 4)
+        del graph
+    except RuntimeError as e:  # reported, not fatal: the eager loop above is the measurement
+        log("bench: graph capture failed: %s" % e)
+
     # Per-kernel durations, live: the same K steps again through the timed entry point, which
     # records HIP events on the launch stream between the kernels of each forward (one event
     # set per step, no synchronisation inside the region).
@@ -254,6 +280,7 @@ def main():
         "algorithmic": {"bytes": traffic["bytes"], "flops": traffic["flops"]},
         "stages_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
         "timed_entry_ms_per_step": round(timed_ms, 4),
+        "graph_replay_ms_per_step": graph_ms,
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "hbm_read_ceiling_GBps": ceiling,
