@@ -5,7 +5,8 @@
 //   * normal value = integer-interpolated inverse CDF table (Q20), exact in fp32;
 //   * N(0, s^2) = z * s (one fp32 multiply, round to nearest even);
 //   * stored formats: bf16 (round to nearest even), fp8 e4m3fn with one fp32 scale
-//     amax/448 per 128 x 128 block, MXFP4 e2m1 with one e8m0 exponent per 32 K of a column.
+//     amax/448 per 128 x 128 block, MXFP4 e2m1 and MXFP8 e4m3fn with one e8m0 exponent per 32 K
+//     of a column.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -196,6 +197,46 @@ __global__ void fill_mxfp4_kernel(uint8_t* codes, uint8_t* scales, uint32_t k0, 
   *(uint32_t*)(scales + (size_t)m * (K / 32) * N + (size_t)kb * N + c0) = E[0] | (E[1] << 8) | (E[2] << 16) | (E[3] << 24);
 }
 
+// MXFP8: one thread per (4 consecutive columns, 32-row block) of one K x N matrix; the exponent
+// is floor(log2 amax) - 8 (the largest E4M3 exponent), so codes saturate at 448.
+__global__ void fill_mxfp8_kernel(uint8_t* codes, uint8_t* scales, uint32_t k0, uint32_t k1, uint32_t stream0,
+                                  int count, int K, int N, float sigma, const int32_t* T, const int32_t* TT) {
+  const long long per = (long long)(N / 4) * (K / 32);
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= per * count) return;
+  const int m = (int)(gid / per);
+  const int kb = (int)((gid % per) / (N / 4));
+  const int c0 = 4 * (int)(gid % (N / 4));
+  float v[32][4];
+  float amax[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < 32; ++r) {
+    uint32_t w[4];
+    block_words(((uint64_t)(kb * 32 + r) * N + c0) / 4, stream0 + (uint32_t)m, k0, k1, w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[r][i] = __fmul_rn(normal_of(w[i], T, TT), sigma);
+      amax[i] = fmaxf(amax[i], fabsf(v[r][i]));
+    }
+  }
+  uint32_t E[4];
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = (int)((__float_as_uint(amax[i]) >> 23) & 0xFF) - 8;
+    e = e < 1 ? 1 : (e > 254 ? 254 : e);
+    E[i] = amax[i] > 0.0f ? (uint32_t)e : 127u;
+    inv[i] = __uint_as_float((254u - E[i]) << 23);
+  }
+  uint8_t* cm = codes + (size_t)m * K * N;
+  for (int r = 0; r < 32; ++r) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) word |= e4m3_code(__fmul_rn(v[r][i], inv[i])) << (8 * i);
+    *(uint32_t*)(cm + (size_t)(kb * 32 + r) * N + c0) = word;
+  }
+  *(uint32_t*)(scales + (size_t)m * (K / 32) * N + (size_t)kb * N + c0) = E[0] | (E[1] << 8) | (E[2] << 16) | (E[3] << 24);
+}
+
 // A plain 16-byte-per-lane copy: the known-size reference for hardware byte counters.
 __global__ void __launch_bounds__(256) copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                      long long n16) {
@@ -337,6 +378,16 @@ int gen_fill_mxfp4(uint8_t* codes, uint8_t* scales, uint32_t k0, uint32_t k1, ui
   const long long threads = (long long)count * (N / 4) * (K / 32);
   if (!threads) return 0;
   fill_mxfp4_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(codes, scales, k0, k1, stream0, count, K, N,
+                                                                       sigma, T, TT);
+  return (int)hipGetLastError();
+}
+
+int gen_fill_mxfp8(uint8_t* codes, uint8_t* scales, uint32_t k0, uint32_t k1, uint32_t stream0, int count, int K,
+                   int N, float sigma, const int32_t* T, const int32_t* TT, hipStream_t st) {
+  if (K % 32 || N % 4) return -1;
+  const long long threads = (long long)count * (N / 4) * (K / 32);
+  if (!threads) return 0;
+  fill_mxfp8_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(codes, scales, k0, k1, stream0, count, K, N,
                                                                        sigma, T, TT);
   return (int)hipGetLastError();
 }

@@ -22,6 +22,9 @@ Stored formats (logical row-major, the layout in which the pages write the matri
   exponents (w = e2m1 * 2^(E-127), one exponent per 32 consecutive K of a column)
 * ``mxfp4a8``: stored as ``mxfp4``; the layer quantises the routed experts' activations to MXFP8
   for their products (W4A8)
+* ``mxfp8a8``: uint8[K, N] E4M3FN codes + uint8[K/32, N] e8m0 exponents (w = e4m3 * 2^(E-127),
+  one exponent per 32 consecutive K of a column); the layer quantises the expert's activations to
+  MXFP8 for its products (W8A8 MXFP8, the shared expert of the hybrid MXFP8-MXFP4 layer)
 
 with (K, N) = (H, I) for gate and up and (I, H) for down.
 
@@ -46,7 +49,7 @@ TID_ROUTED = {"gate": 16, "up": 17, "down": 18}
 TID_SHARED = {"gate": 24, "up": 25, "down": 26}
 
 ACT_DTYPES = ("f32", "bf16")
-W_DTYPES = ("f32", "bf16", "fp8", "mxfp4", "mxfp4a8")
+W_DTYPES = ("f32", "bf16", "fp8", "mxfp4", "mxfp4a8", "mxfp8a8")
 
 
 @dataclass(frozen=True)
@@ -90,10 +93,13 @@ CONFIGS = {
 
 # Further workloads measured beside the configurations above: the DeepSeek-V4-Pro-shaped layer at a
 # prefill batch (T * k = 64 E, where the path switches to the MFMA kernel), with MXFP4 routed
-# experts and bf16 activations, and with W4A8 routed experts (activations quantised to MXFP8).
+# experts and bf16 activations, with W4A8 routed experts (activations quantised to MXFP8), and in
+# the hybrid MXFP8-MXFP4 scheme: W4A8 routed experts and a W8A8 MXFP8 shared expert.
 EXTRA = {
     "v4p": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096),
     "v4p-w4a8": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-w4a8", T=4096, w_routed="mxfp4a8"),
+    "v4p-mx": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-hybrid-mxfp8-mxfp4", T=4096,
+                                    w_routed="mxfp4a8", w_shared="mxfp8a8"),
 }
 
 
@@ -141,6 +147,9 @@ def store_matrix(w: np.ndarray, fmt: str) -> dict:
         return {"w": c, "scale": s}
     if fmt in ("mxfp4", "mxfp4a8"):
         c, s = px.quantize_mxfp4_k32(w)
+        return {"w": c, "scale": s}
+    if fmt == "mxfp8a8":
+        c, s = px.quantize_mxfp8_k32(w)
         return {"w": c, "scale": s}
     raise ValueError(fmt)
 

@@ -175,6 +175,24 @@ def quantize_fp8_block128(w: np.ndarray):
     return f32_to_e4m3fn(v).reshape(K, N), s
 
 
+def quantize_mxfp8_k32(w: np.ndarray):
+    """W[K, N] fp32 -> (E4M3FN codes uint8[K, N], e8m0 scales uint8[K/32, N]).
+
+    A block is 32 consecutive K elements of one column. E = floor(log2(amax)) - 8 + 127 (8 is the
+    largest E4M3 exponent, so the largest magnitude maps into [256, 512) and saturates at 448),
+    clamped to [1, 254]; an all-zero block gets E = 127. Codes = e4m3fn(w * 2^-(E-127)).
+    """
+    K, N = w.shape
+    assert K % 32 == 0
+    wb = w.reshape(K // 32, 32, N)
+    amax = np.abs(wb).max(axis=1).astype(np.float32)
+    ebits = (amax.view(np.uint32) >> 23).astype(np.int64) & 0xFF
+    E = np.where(amax > 0, np.clip(ebits - 8, 1, 254), 127).astype(np.int64)
+    inv = ((254 - E).astype(np.uint32) << 23).view(np.float32)  # 2^-(E-127), exact
+    v = (wb * inv[:, None, :]).astype(np.float32).reshape(K, N)
+    return f32_to_e4m3fn(v), E.astype(np.uint8)
+
+
 def quantize_mxfp4_k32(w: np.ndarray):
     """W[K, N] fp32 -> (packed codes uint8[K, N/2], e8m0 scales uint8[K/32, N]).
 

@@ -14,6 +14,9 @@
  *                                                        (w = e2m1(code) * 2^(E-127))
  *   mxfp4a8  stored as mxfp4; the routed experts' activations are quantised to MXFP8 before
  *            each of their products (W4A8, see oracle_mxfp8_quantize)
+ *   mxfp8a8  uint8[K][N] OCP E4M3FN + uint8[K/32][N] e8m0     (w = e4m3(code) * 2^(E-127));
+ *            the expert's activations are quantised to MXFP8 before each of its products
+ *            (W8A8 MXFP8, the shared expert of the hybrid MXFP8-MXFP4 scheme)
  *
  * What it computes, step by step (sources: "AI infra book, ch. 6 Supernodes" (bojieli.github.io
  * ai-infra-book ch. 6) = [ch6]; "DeepSeek-V4-Pro on NVIDIA H200" report = [V4]):
@@ -33,7 +36,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_MXFP4_A8 = 4 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_MXFP4_A8 = 4, OR_MXFP8_A8 = 5 };
 
 /* storage format of a weight format (W4A8 stores its weights as MXFP4) */
 static int stored(int fmt) { return fmt == OR_MXFP4_A8 ? OR_MXFP4 : fmt; }
@@ -94,6 +97,10 @@ static double w_at(const void* w, const void* scale, int fmt, int K, int N, int 
       uint8_t E = ((const uint8_t*)scale)[(size_t)(k / 32) * N + n];
       return oracle_decode_e2m1(code) * oracle_decode_e8m0(E);
     }
+    case OR_MXFP8_A8: {
+      uint8_t E = ((const uint8_t*)scale)[(size_t)(k / 32) * N + n];
+      return oracle_decode_e4m3fn(((const uint8_t*)w)[i]) * oracle_decode_e8m0(E);
+    }
   }
   return NAN;
 }
@@ -105,13 +112,15 @@ static size_t w_bytes(int fmt, int K, int N) {
     case OR_BF16: return (size_t)K * N * 2;
     case OR_FP8: return (size_t)K * N;
     case OR_MXFP4: return (size_t)K * N / 2;
+    case OR_MXFP8_A8: return (size_t)K * N;
   }
   return 0;
 }
 static size_t s_bytes(int fmt, int K, int N) {
   switch (stored(fmt)) {
     case OR_FP8: return (size_t)(K / 128) * (N / 128) * 4;
-    case OR_MXFP4: return (size_t)(K / 32) * N;
+    case OR_MXFP4:
+    case OR_MXFP8_A8: return (size_t)(K / 32) * N;
   }
   return 0;
 }
@@ -285,14 +294,14 @@ static double bf16_round(double v) {
   return ldexp(nearbyint(ldexp(v, 7 - e)), e - 7);
 }
 
-/* W4A8 (fmt mxfp4a8): the row is quantised to MXFP8 before gate/up; h = SiLU(g) * v is rounded
- * to bf16, the type the layer keeps it in between the two products, then quantised to MXFP8
- * before down. Other formats multiply the rows as given. */
+/* W4A8 (fmt mxfp4a8) and W8A8 MXFP8 (fmt mxfp8a8): the row is quantised to MXFP8 before gate/up;
+ * h = SiLU(g) * v is rounded to bf16, the type the layer keeps it in between the two products,
+ * then quantised to MXFP8 before down. Other formats multiply the rows as given. */
 int oracle_expert_ffn(int H, int I, int M, int fmt, const void* wg, const void* sg,
                       const void* wu, const void* su, const void* wd, const void* sd,
                       const double* u, double* y) {
   int bad = 0;
-  const int a8 = fmt == OR_MXFP4_A8;
+  const int a8 = fmt == OR_MXFP4_A8 || fmt == OR_MXFP8_A8;
 #pragma omp parallel for schedule(dynamic, 1) if (M > 1)
   for (int m = 0; m < M; ++m) {
     double* g = (double*)malloc(sizeof(double) * I);

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "moe_oracle.c")
 LIB = os.path.join(HERE, "libmoe_oracle.so")
 
-FMT = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "mxfp4a8": 4}
+FMT = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "mxfp4a8": 4, "mxfp8a8": 5}
 
 _lib = None
 
@@ -69,11 +69,11 @@ def _check(rc, what):
 
 def _wdtype(fmt):
     return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "mxfp4": np.uint8,
-            "mxfp4a8": np.uint8}[fmt]
+            "mxfp4a8": np.uint8, "mxfp8a8": np.uint8}[fmt]
 
 
 def _sdtype(fmt):
-    return {"fp8": np.float32, "mxfp4": np.uint8, "mxfp4a8": np.uint8}.get(fmt)
+    return {"fp8": np.float32, "mxfp4": np.uint8, "mxfp4a8": np.uint8, "mxfp8a8": np.uint8}.get(fmt)
 
 
 def decode_scalar(fmt: str, code: int) -> float:

@@ -80,6 +80,25 @@ def test_mxfp4_scale_puts_block_max_in_4_to_8():
     assert np.all((r >= 4) & (r < 8))
 
 
+def test_mxfp8_scale_puts_block_max_in_256_to_512_saturating_at_448():
+    """OCP MXFP8 weights: E = floor(log2 amax) - 8, so the scaled block maximum lies in [256, 512)
+    and codes above 448 saturate; every other element is the nearest E4M3 value."""
+    w = px.normal_f32(2, 3, 0, 0, 64 * 32).reshape(64, 32) * np.float32(0.02)
+    codes, E = px.quantize_mxfp8_k32(w)
+    amax = np.abs(w.reshape(2, 32, 32)).max(axis=1)
+    scale = np.ldexp(1.0, E.astype(np.int64) - 127)
+    r = amax / scale
+    assert np.all((r >= 256) & (r < 512))
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    scaled = w.astype(np.float64) / np.repeat(scale, 32, axis=0)
+    assert np.all(np.abs(dec) <= 448)
+    inside = np.abs(scaled) <= 448
+    # nearest: at most half a step of the E4M3 grid (2^(e-3) for |v| in [2^e, 2^(e+1)), 2^-9 below 2^-6)
+    e = np.floor(np.log2(np.maximum(np.abs(scaled), 2.0 ** -6)))
+    assert np.all(np.abs(dec - scaled)[inside] <= (2.0 ** (e - 4))[inside] + 1e-12)
+    assert np.all(dec[~inside] == np.sign(scaled[~inside]) * 448)
+
+
 def test_generation_is_deterministic_and_seeded():
     s = L.CONFIGS["c1"]
     a, b = L.router_inputs(s), L.router_inputs(s)

@@ -51,7 +51,7 @@ def test_bf16_matches_torch():
     assert np.array_equal(got, ref.astype(np.float64))
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8"])
 def test_decode_matrix_layout(fmt):
     """The matrix decoder against an independent numpy/torch decode of the stored layout."""
     K, N = 256, 256
@@ -65,6 +65,9 @@ def test_decode_matrix_layout(fmt):
     elif fmt == "fp8":
         v = torch.from_numpy(st["w"]).view(torch.float8_e4m3fn).double().numpy()
         ref = v * np.kron(st["scale"].astype(np.float64), np.ones((128, 128)))
+    elif fmt == "mxfp8a8":
+        v = torch.from_numpy(st["w"]).view(torch.float8_e4m3fn).double().numpy()
+        ref = v * np.repeat(np.ldexp(1.0, st["scale"].astype(np.int64) - 127), 32, axis=0)
     else:
         lo, hi = st["w"] & 15, st["w"] >> 4
         codes = np.empty((K, N), np.uint8)
@@ -74,8 +77,8 @@ def test_decode_matrix_layout(fmt):
         ref = table[codes] * np.repeat(scale, 32, axis=0)
     assert np.array_equal(got, ref)
     # the stored value is the nearest representable one: relative error bound of the format
-    rel = {"f32": 0, "bf16": 2 ** -8, "fp8": 2 ** -3, "mxfp4": 0.5}[fmt]
-    if fmt != "mxfp4":
+    rel = {"f32": 0, "bf16": 2 ** -8, "fp8": 2 ** -3, "mxfp4": 0.5, "mxfp8a8": 2 ** -3}[fmt]
+    if fmt not in ("mxfp4", "mxfp8a8"):
         assert np.all(np.abs(got - w) <= rel * np.abs(w) + 2 ** -9 * 1e-1)
 
 
@@ -471,6 +474,65 @@ def test_expert_ffn_w4a8_is_quantised_swiglu():
     y4 = O.expert_ffn(u, wts, "mxfp4")
     rel = np.linalg.norm(y - y4) / np.linalg.norm(y4)
     assert 1e-2 < rel < 8e-2
+
+
+def test_mxfp8_weights_decode_hand_values():
+    """MXFP8 weights (OCP Microscaling v1.0: E4M3FN element times the e8m0 block scale of 32
+    consecutive K of a column) on hand-decoded codes: 0x38 = 1.0, 0xC4 = -3.0, 0x01 = 2^-9
+    (the smallest subnormal), 0x7E = 448."""
+    K, N = 64, 2
+    codes = np.zeros((K, N), np.uint8)
+    scales = np.array([[130, 125], [127, 120]], np.uint8)  # [K/32][N]
+    codes[0, 0], codes[31, 0], codes[32, 0] = 0x38, 0xC4, 0x7E
+    codes[5, 1], codes[40, 1] = 0x01, 0xB8
+    d = O.decode_matrix("mxfp8a8", K, N, codes, scales)
+    assert d[0, 0] == 8.0 and d[31, 0] == -24.0 and d[32, 0] == 448.0
+    assert d[5, 1] == 2.0 ** -9 * 2.0 ** -2 and d[40, 1] == -1.0 * 2.0 ** -7
+    assert np.count_nonzero(d) == 5
+
+
+def test_expert_ffn_w8a8_mxfp8_is_quantised_swiglu():
+    """W8A8 MXFP8 FFN (the shared expert of the hybrid MXFP8-MXFP4 scheme, 'CANN DeepSeek-V4推理
+    优化' quantisation strategy) = down(Q(bf16(SiLU(Q(u) Wg) * (Q(u) Wu)))) on the MXFP8 weights,
+    like the W4A8 composition above; near the FFN of the unquantised weights."""
+    H, I, M = 256, 128, 4
+    s = L.LayerSpec("f", T=M, H=H, E=1, k=1, I=I, shared=True, w_shared="mxfp8a8")
+    wts = L.expert_weights(s, "shared", 0)
+    u = L.act_to_f64(L.store_act(px.normal_f32(3, 6, 0, 0, M * H).reshape(M, H), "bf16"), "bf16")
+    y = O.expert_ffn(u, wts, "mxfp8a8")
+    g = O.decode_matrix("mxfp8a8", H, I, wts["gate"], wts["gate_scale"])
+    v = O.decode_matrix("mxfp8a8", H, I, wts["up"], wts["up_scale"])
+    d = O.decode_matrix("mxfp8a8", I, H, wts["down"], wts["down_scale"])
+    uq = _mxfp8_roundtrip(u)
+    h = torch.nn.functional.silu(torch.from_numpy(uq @ g)).numpy() * (uq @ v)
+    ref = _mxfp8_roundtrip(_bf16_round(h)) @ d
+    assert np.allclose(y, ref, rtol=1e-9, atol=1e-11)
+    f = {n: L.draw_f32(s.seed, L.TID_SHARED[n], 0, shp, fan).astype(np.float32)
+         for n, shp, fan in (("gate", (H, I), H), ("up", (H, I), H), ("down", (I, H), I))}
+    y32 = O.expert_ffn(u, {"gate": f["gate"], "up": f["up"], "down": f["down"],
+                           "gate_scale": None, "up_scale": None, "down_scale": None}, "f32")
+    rel = np.linalg.norm(y - y32) / np.linalg.norm(y32)
+    assert 1e-2 < rel < 8e-2
+
+
+def test_layer_hybrid_mxfp8_shared_changes_only_the_shared_expert():
+    """Hybrid MXFP8-MXFP4 layer (W4A8 routed, W8A8 MXFP8 shared): routing and permutation equal
+    those of the layer with a bf16 shared expert, and y differs from it by the shared expert's
+    output difference alone (the combine adds y_sh with weight 1)."""
+    s = L.LayerSpec("hy", T=8, H=128, E=4, k=2, I=128, act="bf16", shared=True, w_routed="mxfp4a8",
+                    w_shared="mxfp8a8", seed=10)
+    r = L.router_inputs(s)
+    routed = L.stack_experts(s)
+    sh8 = L.expert_weights(s, "shared", 0)
+    sb = s.replace(w_shared="bf16")
+    sh16 = L.expert_weights(sb, "shared", 0)
+    a = O.layer(s, r["x"], r["Wr"], r["bias"], routed, sh8)
+    b = O.layer(sb, r["x"], r["Wr"], r["bias"], routed, sh16)
+    assert np.array_equal(a["topk_idx"], b["topk_idx"]) and np.array_equal(a["pair_slot"], b["pair_slot"])
+    xf = L.act_to_f64(r["x"], "bf16")
+    dy = O.expert_ffn(xf, sh8, "mxfp8a8") - O.expert_ffn(xf, sh16, "bf16")
+    assert np.allclose(a["y"] - b["y"], dy, rtol=1e-9, atol=1e-12)
+    assert np.abs(dy).max() > 0
 
 
 def test_layer_w4a8_routes_like_mxfp4():
