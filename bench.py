@@ -55,7 +55,7 @@ def measured_traffic(config: str, path: str):
 
 
 # bounded CPU-oracle samples (tokens): about 10-30 s of oracle work per config
-CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4, "v4p": 6, "v4p-w4a8": 6}
+CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4, "v4p": 6, "v4p-w4a8": 6, "v4p-mx": 6}
 
 
 def log(*a):
@@ -67,9 +67,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8"],
-                    help="c1-c5: the layer configurations; v4p, v4p-w4a8: the V4-Pro-shaped layer at a "
-                         "prefill batch with MXFP4 / W4A8 routed experts")
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx"],
+                    help="c1-c5: the layer configurations; v4p, v4p-w4a8, v4p-mx: the V4-Pro-shaped layer at a "
+                         "prefill batch with MXFP4 / W4A8 routed experts, and in the hybrid MXFP8-MXFP4 scheme "
+                         "(W4A8 routed, W8A8 MXFP8 shared)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=None)
@@ -195,7 +196,9 @@ def main():
         # register-only MFMA bursts of the GEMMs' instruction kinds, 2 waves per SIMD
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         mfma_ceiling = {}
-        for kind, name in ((0, "bf16 16x16x32"), (1, "fp4 x fp8 16x16x128")) if a8 else ((0, "bf16 16x16x32"),):
+        kinds = ((0, "bf16 16x16x32"), (1, "fp4 x fp8 16x16x128"), (2, "fp8 x fp8 16x16x128")) if a8 else \
+            ((0, "bf16 16x16x32"),)
+        for kind, name in kinds:
             iters = 2048 if kind else 8192
             G.mfma_burst(kind, iters, 512, sink)
             m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -213,48 +216,65 @@ def main():
         torch.cuda.synchronize()
         log("bench: calibration copy of %d bytes" % nb)
 
-    # roofline of the dominant kernel (the gate/up grouped GEMM)
+    # roofline of the dominant kernel (the gate/up grouped GEMM, or the W4A8 gate/up stage), against
+    # the roof that binds it: its algorithmic FLOPs at the MFMA peak of its instruction kinds, or its
+    # algorithmic bytes at the HBM peak, whichever takes longer
     H, I, T, k = spec.H, spec.I, spec.T, spec.k
     R = T * k + (T if spec.shared else 0)
     ab = 4 if spec.act == "f32" else 2
-    gu_bytes = (traffic["active_experts"] * 2 * pm.matrix_bytes(H, I, spec.w_routed)
-                + (2 * pm.matrix_bytes(H, I, spec.w_shared) if spec.shared else 0)
-                + T * H * ab + R * I * ab)
+    mx = a8 and spec.shared and spec.w_shared == "mxfp8a8"
+    w_bytes = (traffic["active_experts"] * 2 * pm.matrix_bytes(H, I, spec.w_routed)
+               + (2 * pm.matrix_bytes(H, I, spec.w_shared) if spec.shared else 0))
+    if a8:
+        q = 1 + 1 / 32  # MXFP8 bytes per element (E4M3 code + an e8m0 byte per 32)
+        # x read once as bf16, its MXFP8 form written and read once; h written as MXFP8 (routed rows,
+        # and the shared rows in the hybrid scheme) or bf16 (a bf16 shared expert)
+        gu_bytes = int(w_bytes + T * H * ab + 2 * T * H * q + T * k * I * q
+                       + (T * I * (q if mx else ab) if spec.shared else 0))
+    else:
+        gu_bytes = w_bytes + T * H * ab + R * I * ab
     gu_flops = 4 * H * I * R
     gu_ms = stage_ms[names.index("gate_up")]
     prefill = a8 or (T * k) / spec.E >= 64
     traffic_b = measured_traffic(args.config, "w4a8" if a8 else "prefill" if prefill else "decode")
+    hbm_ach = gu_bytes / (gu_ms * 1e-3) / 1e9
+    hbm_roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(hbm_ach / HBM_PEAK_GBPS, 4),
+                "frac_of_read_ceiling": round(hbm_ach / ceiling, 4) if ceiling else None}
     if a8:
         # W4A8: the gate/up stage is the x quantisation, the routed fp4 x fp8 GEMM (fp8 peak) and
-        # the shared expert's bf16 GEMM (bf16 peak); its peak is the FLOP-weighted blend, i.e.
-        # the stage's FLOPs over the time both GEMMs would take at their own peaks
+        # the shared expert's GEMM: bf16 (bf16 peak), or W8A8 MXFP8 in the hybrid scheme (fp8 peak);
+        # the stage's MFMA peak is the FLOP-weighted blend, i.e. its FLOPs over the time both GEMMs
+        # would take at their own peaks
         fr, fs = 4 * H * I * T * k, 4 * H * I * (T if spec.shared else 0)
-        t_peak = fr / (MFMA_PEAK_TFLOPS["fp8"] * 1e12) + fs / (MFMA_PEAK_TFLOPS["bf16"] * 1e12)
+        t_peak = fr / (MFMA_PEAK_TFLOPS["fp8"] * 1e12) + fs / (MFMA_PEAK_TFLOPS["fp8" if mx else "bf16"] * 1e12)
         peak = round(gu_flops / t_peak / 1e12, 1)
-        ach = gu_flops / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": traffic_b,
-                "kernel": "gate/up stage: x to MXFP8, W4A8 routed GEMM (fp8 peak 5000), bf16 shared GEMM "
-                          "(bf16 peak 2500)",
-                "per_launch": {"flops": gu_flops, "routed_flops": fr, "shared_flops": fs, "ms": round(gu_ms, 4)}}
-        if mfma_ceiling:
-            # the time both GEMMs would take at the measured sustained rates, over the stage time
-            t_meas = fr / (mfma_ceiling["fp4 x fp8 16x16x128"] * 1e12) + fs / (mfma_ceiling["bf16 16x16x32"] * 1e12)
-            roof["frac_of_measured_mfma"] = round(t_meas / (gu_ms * 1e-3), 4)
-    elif prefill:
-        peak = MFMA_PEAK_TFLOPS["bf16" if spec.act == "bf16" else "f32"]
-        ach = gu_flops / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": traffic_b, "kernel": "gate/up grouped GEMM",
-                "per_launch": {"flops": gu_flops, "ms": round(gu_ms, 4)}}
-        if mfma_ceiling:
-            roof["frac_of_measured_mfma"] = round(ach / mfma_ceiling["bf16 16x16x32"], 4)
+        kernel = ("gate/up stage: x to MXFP8, W4A8 routed GEMM and W8A8 MXFP8 shared GEMM (fp8 peak 5000)"
+                  if mx else "gate/up stage: x to MXFP8, W4A8 routed GEMM (fp8 peak 5000), bf16 shared GEMM "
+                             "(bf16 peak 2500)")
+        per_launch = {"flops": gu_flops, "routed_flops": fr, "shared_flops": fs, "bytes": gu_bytes,
+                      "ms": round(gu_ms, 4)}
     else:
-        ach = gu_bytes / (gu_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic_b, "kernel": "gate/up grouped GEMM",
-                "per_launch": {"bytes": gu_bytes, "ms": round(gu_ms, 4)},
-                "frac_of_read_ceiling": round(ach / ceiling, 4) if ceiling else None}
+        peak = MFMA_PEAK_TFLOPS["bf16" if spec.act == "bf16" else "f32"]
+        kernel = "gate/up grouped GEMM"
+        per_launch = {"flops": gu_flops, "bytes": gu_bytes, "ms": round(gu_ms, 4)}
+    mfma_ach = gu_flops / (gu_ms * 1e-3) / 1e12
+    mfma_roof = {"bound": "mfma", "achieved": round(mfma_ach, 1), "peak": peak, "unit": "TFLOP/s",
+                 "frac": round(mfma_ach / peak, 4)}
+    if mfma_ceiling and prefill:
+        if a8:
+            # the time both GEMMs would take at the measured sustained rates, over the stage time
+            rs = mfma_ceiling["fp8 x fp8 16x16x128" if mx else "bf16 16x16x32"]
+            t_meas = fr / (mfma_ceiling["fp4 x fp8 16x16x128"] * 1e12) + fs / (rs * 1e12)
+            mfma_roof["frac_of_measured_mfma"] = round(t_meas / (gu_ms * 1e-3), 4)
+        else:
+            mfma_roof["frac_of_measured_mfma"] = round(mfma_ach / mfma_ceiling["bf16 16x16x32"], 4)
+    t_hbm = gu_bytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = gu_flops / (peak * 1e12)
+    binding, other = (mfma_roof, hbm_roof) if prefill and t_mfma >= t_hbm else (hbm_roof, mfma_roof)
+    roof = dict(binding)
+    roof.update({"traffic": traffic_b, "kernel": kernel, "per_launch": per_launch,
+                 "roof_ms": {"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4)}, "other_roof": other})
 
     out = {
         "metric": METRIC,

@@ -38,7 +38,7 @@ int pad64(int n) { return (n + 63) / 64 * 64; }
 int pad256(int n) { return (n + 255) / 256 * 256; }
 constexpr int ROW_BLOCK = 64;
 
-bool valid_fmt(int f) { return f >= MOE_F32 && f <= MOE_MXFP4_B32_A8; }
+bool valid_fmt(int f) { return f >= MOE_F32 && f <= MOE_MXFP8_B32_A8; }
 // storage format: W4A8 weights are stored and packed as MXFP4
 moe_dtype stored_fmt(moe_dtype f) { return f == MOE_MXFP4_B32_A8 ? MOE_MXFP4_B32 : f; }
 
@@ -52,12 +52,16 @@ moe_status packed_sizes(moe_dtype fmt, int count, int K, int N, size_t* bytes, s
   if (fmt == MOE_FP8_E4M3_B128 && (K % 128 || N % 128))
     return fail(MOE_ERR_INVALID_ARG, "fp8 block-128 scales need K, N multiples of 128 (K=%d N=%d)", K, N);
   if (fmt == MOE_MXFP4_B32 && N % 2) return fail(MOE_ERR_INVALID_ARG, "MXFP4 packs N=%d in pairs", N);
+  if (fmt == MOE_MXFP8_B32_A8 && K % 128)
+    return fail(MOE_ERR_INVALID_ARG, "MXFP8 scales are packed per 128 reduction elements (K=%d)", K);
   const size_t NT = pad256(N) / 16, KT = K / KP;
   *bytes = (size_t)count * NT * KT * PACKET_BYTES;
   if (fmt == MOE_FP8_E4M3_B128)
     *sbytes = (size_t)count * (K / 128) * (N / 128) * 4;
   else if (fmt == MOE_MXFP4_B32)
     *sbytes = (size_t)count * NT * KT * 64;
+  else if (fmt == MOE_MXFP8_B32_A8)
+    *sbytes = (size_t)count * NT * (K / 128) * 64;
   else
     *sbytes = 0;
   return MOE_OK;
@@ -83,6 +87,10 @@ moe_status check_shape(const moe_shape* s) {
     return fail(MOE_ERR_UNSUPPORTED, "weights must be F32 with F32 activations and BF16/FP8/MXFP4 with BF16 ones");
   if (s->I_shared && s->w_shared == MOE_MXFP4_B32_A8)
     return fail(MOE_ERR_UNSUPPORTED, "W4A8 (MOE_MXFP4_B32_A8) applies to the routed experts only");
+  if (s->w_routed == MOE_MXFP8_B32_A8)
+    return fail(MOE_ERR_UNSUPPORTED, "W8A8 MXFP8 (MOE_MXFP8_B32_A8) applies to the shared expert only");
+  if (s->I_shared && s->w_shared == MOE_MXFP8_B32_A8 && s->w_routed != MOE_MXFP4_B32_A8)
+    return fail(MOE_ERR_UNSUPPORTED, "a W8A8 MXFP8 shared expert needs W4A8 routed experts (MOE_MXFP4_B32_A8)");
   if (s->w_routed == MOE_MXFP4_B32_A8 &&
       (s->path == MOE_PATH_DECODE ||
        !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
@@ -163,11 +171,13 @@ Ws ws_layout(const moe_shape& s) {
   w.y_shared = take(S * s.T * s.H * ab);
   w.zero = take((size_t)std::max(s.H, s.I) * ab);  // zero activations for prefill padding rows
   if (s.w_routed == MOE_MXFP4_B32_A8) {
-    // W4A8: MXFP8 codes and exponents of x (token rows) and of the routed rows of h
+    // W4A8: MXFP8 codes and exponents of x (token rows) and of the rows of h that the W4A8 and
+    // W8A8 products read (the routed rows, then the shared expert's with a W8A8 shared expert)
+    const size_t QR = P + (S && s.w_shared == MOE_MXFP8_B32_A8 ? (size_t)s.T : 0);
     w.xq = take((size_t)s.T * s.H);
     w.xs = take((size_t)s.T * (s.H / 32));
-    w.hq = take(P * s.I);
-    w.hs = take(P * (s.I / 32));
+    w.hq = take(QR * s.I);
+    w.hs = take(QR * (s.I / 32));
   }
   w.total = o;
   return w;
@@ -190,7 +200,7 @@ T* at(void* ws, size_t off) {
 moe_status check_weights(const moe_weights* w, moe_dtype fmt, const char* what) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "%s weights are NULL", what);
   if (!w->gate || !w->up || !w->down) return fail(MOE_ERR_INVALID_ARG, "%s weight pointer is NULL", what);
-  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP4_B32 || fmt == MOE_MXFP4_B32_A8) &&
+  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP4_B32 || fmt == MOE_MXFP4_B32_A8 || fmt == MOE_MXFP8_B32_A8) &&
       (!w->gate_scale || !w->up_scale || !w->down_scale))
     return fail(MOE_ERR_INVALID_ARG, "%s scales are NULL", what);
   return MOE_OK;
@@ -340,7 +350,23 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
     if (r != hipSuccess || !S) return r;
     sa.g_begin = s.E;
     sa.g_end = s.E + 1;
-    return launch_grouped_prefill(s.act, epi, cs, cs, sa, max_rb, st);
+    if (cs != MOE_MXFP8_B32_A8) return launch_grouped_prefill(s.act, epi, cs, cs, sa, max_rb, st);
+    // W8A8 MXFP8 shared expert: the same MXFP8 rows of x (token t is row P + t of the group)
+    // and of h, whose shared rows follow the routed ones
+    sa.act = codes;
+    sa.lda = K;
+    sa.act_scale = scales;
+    if (epi == EPI_SWIGLU) {
+      sa.gather = gather;
+      sa.act_rows = rows;
+      sa.out = at<void>(ws, L.hq);
+      sa.ldo = s.I;
+      sa.out_scale = at<void>(ws, L.hs);
+    } else {
+      sa.gather = nullptr;
+      sa.act_rows = P + s.T;
+    }
+    return launch_w8a8_shared(epi == EPI_SWIGLU ? EPI_SWIGLU_Q8 : epi, sa, s.T, st);
   };
   if (a8) {
     e = launch_quant_mxfp8(x, s.T, s.H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), st);

@@ -37,7 +37,7 @@ constexpr int WAVE = 64;
 constexpr int PACKET_BYTES = 1024;
 
 __host__ __device__ constexpr int kp_of(int fmt) {
-  return fmt == MOE_F32 ? 16 : fmt == MOE_BF16 ? 32 : fmt == MOE_FP8_E4M3_B128 ? 64 : 128;
+  return fmt == MOE_F32 ? 16 : fmt == MOE_BF16 ? 32 : (fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP8_B32_A8) ? 64 : 128;
 }
 
 // bf16 bit helpers (raw uint16 storage)

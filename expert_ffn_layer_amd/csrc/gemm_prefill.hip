@@ -47,6 +47,7 @@ struct PCodec<MOE_BF16> {
   static constexpr int H = 1;        // 32-deep MFMA steps per pipeline step
   static constexpr int PK = 1;       // packets per 16-column tile per pipeline step
   static constexpr bool HALF_ONLY = false;  // every item 128 rows x 512 columns
+  static constexpr bool FULL_ONLY = false;  // every item 256 rows x 256 columns (one group per launch)
   static constexpr bool SCALE_DMA = false;  // per-packet scales reach LDS with the weights
   static constexpr int ACT_BYTES = 2;       // bytes per activation element
   static constexpr int NSC = 0;             // scale DMA loads per wave per step
@@ -89,7 +90,7 @@ struct PCodec<MOE_FP8_E4M3_B128> {
   static constexpr int PBK = 64;
   static constexpr int H = 2;
   static constexpr int PK = 1;
-  static constexpr bool HALF_ONLY = false;
+  static constexpr bool HALF_ONLY = false, FULL_ONLY = false;
   static constexpr bool SCALE_DMA = false;
   static constexpr int ACT_BYTES = 2, NSC = 0, SC_KIB = 0;
   // Lane group g of a packet holds reduction elements 16g .. 16g + 15 and MFMA half h takes the
@@ -135,7 +136,7 @@ struct PCodec<MOE_MXFP4_B32> {
   static constexpr int PBK = 128;
   static constexpr int H = 4;
   static constexpr int PK = 1;
-  static constexpr bool HALF_ONLY = true;
+  static constexpr bool HALF_ONLY = true, FULL_ONLY = false;
   static constexpr bool SCALE_DMA = true;
   static constexpr int ACT_BYTES = 2, NSC = 1, SC_KIB = 8;
   __device__ static int dma_row(int l, int u) { return 4 * u + (l >> 4); }
@@ -172,7 +173,7 @@ struct PCodec<MOE_MXFP4_B32_A8> {
   static constexpr int PBK = 128;
   static constexpr int H = 2;  // 1 KiB activation DMA units per 16-row tile per step
   static constexpr int PK = 1;
-  static constexpr bool HALF_ONLY = false;
+  static constexpr bool HALF_ONLY = false, FULL_ONLY = false;
   static constexpr bool SCALE_DMA = false;
   static constexpr int ACT_BYTES = 1, NSC = 2, SC_KIB = 4;
   __device__ static int dma_row(int l, int u) { return 8 * u + (l >> 3); }
@@ -183,6 +184,31 @@ struct PCodec<MOE_MXFP4_B32_A8> {
     return (j >> 3) * 1024 + (j & 7) * 128 + 16 * ((4 * h + g) ^ (j & 7) ^ (j >> 3));
   }
   // the bf16-operand step is compiled but never reached for this codec (its step returns first)
+  __device__ static void frags(const u32x4 (&)[PK], float, bf16x8 (&)[H]) {}
+};
+
+// W8A8 MXFP8 (the shared expert of the hybrid MXFP8-MXFP4 scheme): fp8 weight packets times
+// MXFP8 activations on the same block-scaled instruction, fp8 x fp8. Measured on the hardware, the
+// fp8 A operand has the fp8 B layout: lane (f, g) holds elements 16g .. 16g + 15 in bytes 0..15 and
+// 64 + 16g .. + 15 in bytes 16..31, and the exponent of (feature f, block b) comes from lane
+// f + 16b. The two packets of a column tile in one step (elements 0..63 and 64..127, lane l holding
+// run 16 (l / 16) of each) are therefore the operand as stored, and the packed exponents (one byte
+// per lane per pair of packets) its scales. A step takes 2 KiB of weights per column tile, so a
+// 128-row x 512-column half item would need 80 KiB per stage: every item is a full one (64 KiB of
+// codes and 4 KiB of exponents per stage, two stages), the waves of a row half without rows skip
+// the MFMAs, and a launch covers one group. Activations as in the W4A8 codec.
+template <>
+struct PCodec<MOE_MXFP8_B32_A8> {
+  static constexpr int KP = 64;
+  static constexpr int PBK = 128;
+  static constexpr int H = 2;
+  static constexpr int PK = 2;
+  static constexpr bool HALF_ONLY = false, FULL_ONLY = true;
+  static constexpr bool SCALE_DMA = false;
+  static constexpr int ACT_BYTES = 1, NSC = 2, SC_KIB = 4;
+  __device__ static int dma_row(int l, int u) { return PCodec<MOE_MXFP4_B32_A8>::dma_row(l, u); }
+  __device__ static int dma_off(int l, int u) { return PCodec<MOE_MXFP4_B32_A8>::dma_off(l, u); }
+  __device__ static int read_off(int l, int h) { return PCodec<MOE_MXFP4_B32_A8>::read_off(l, h); }
   __device__ static void frags(const u32x4 (&)[PK], float, bf16x8 (&)[H]) {}
 };
 
@@ -203,15 +229,16 @@ struct PLayout {
   static constexpr int FULL_ACT = 16 * H, HALF_ACT = 8 * H;
   static constexpr int FULL_W = 16 * PK, HALF_W = 32 * PK;
   static constexpr int SC_KIB = Cd::SC_KIB;
-  static constexpr int ITEM_KIB = (!Cd::HALF_ONLY && FULL_ACT + FULL_W > HALF_ACT + HALF_W) ? FULL_ACT + FULL_W
-                                                                                         : HALF_ACT + HALF_W;
+  static constexpr int ITEM_KIB = Cd::FULL_ONLY ? FULL_ACT + FULL_W
+                                 : (!Cd::HALF_ONLY && FULL_ACT + FULL_W > HALF_ACT + HALF_W) ? FULL_ACT + FULL_W
+                                                                                           : HALF_ACT + HALF_W;
   static constexpr int SC_OFF = ITEM_KIB * 1024;
   static constexpr int STAGE_KIB = ITEM_KIB + SC_KIB;
-  static constexpr int STAGES = Cd::HALF_ONLY ? 2 : 3;
+  static constexpr int STAGES = (Cd::HALF_ONLY || Cd::FULL_ONLY) ? 2 : 3;
   // DMA instructions per wave per stage; the shorter kind is padded with repeats of its last
   // load so both kinds issue the same count (the wait counts are compile-time)
   static constexpr int LF = Cd::HALF_ONLY ? 0 : 2 * H + 2 * PK, LH = H + 4 * PK;
-  static constexpr int L = (LF > LH ? LF : LH) + Cd::NSC;
+  static constexpr int L = (Cd::FULL_ONLY ? LF : (LF > LH ? LF : LH)) + Cd::NSC;
   static_assert(STAGES * STAGE_KIB <= 160, "LDS");
 };
 
@@ -256,7 +283,10 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   const int gb = planned && a.g_end > a.g_begin ? a.g_begin : 0;
   const int ge = planned && a.g_end > a.g_begin ? a.g_end : a.G;
   const int ibase = planned ? a.cum_blocks[gb] * (ntn >> 1) : 0;
-  const int total = planned ? a.cum_blocks[ge] * (ntn >> 1) - ibase : (a.M + PBM - 1) / PBM * ntn;
+  // FULL_ONLY (one group per launch): ceil(rows / 256) full items per column tile
+  const int total = Cd::FULL_ONLY ? (a.group_range[2 * gb + 1] - a.group_range[2 * gb] + PBM - 1) / PBM * ntn
+                    : planned     ? a.cum_blocks[ge] * (ntn >> 1) - ibase
+                                  : (a.M + PBM - 1) / PBM * ntn;
   // XCD-aware workgroup -> item map over the items that exist: XCD x (= blockIdx % 8) takes
   // items [x * per_xcd, (x + 1) * per_xcd)
   const int per_xcd = (total + NXCD - 1) / NXCD;
@@ -265,7 +295,14 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   if (item >= total) return;
   int g = 0, row0, ntile, rbeg = 0, rend = a.M;
   bool half = false;
-  if (planned) {
+  if (Cd::FULL_ONLY) {
+    g = gb;
+    rbeg = a.group_range[2 * g];
+    rend = a.group_range[2 * g + 1];
+    int mtile;
+    item_tiles(item, (rend - rbeg + PBM - 1) / PBM, ntn, mtile, ntile);
+    row0 = rbeg + mtile * PBM;
+  } else if (planned) {
     const int gi = item + ibase;
     // 128-row block gi / (ntn / 2) of the row space: its group and place from the plan's table
     // (one load), else a search over cum_blocks
@@ -318,6 +355,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   const float* s0 = (const float*)ws0;
   const float* s1 = (const float*)ws1;
   const int KT = a.K / KP;
+  const int KTS = a.K / 128;  // W4A8 / W8A8: exponent packets (one per 128-deep step) per column tile
   // reduction steps of this workgroup: split-K part blockIdx.y of ksplit (fp32 partial outputs)
   const int KSG = a.ksplit > 1 ? a.ksplit : 1;
   const int kstep0 = (int)blockIdx.y * (a.K / PBK) / KSG;
@@ -354,7 +392,8 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   int qdst[L], qstride[L];
   const int wts_off = (half ? Ly::HALF_ACT : Ly::FULL_ACT) * 1024;
   constexpr int LSC = Cd::SCALE_DMA ? 1 : 0;  // the last load moves the packet scales
-  constexpr bool A8 = C == MOE_MXFP4_B32_A8;   // the last two loads move the exponents
+  constexpr bool A8 = C == MOE_MXFP4_B32_A8 || C == MOE_MXFP8_B32_A8;  // the last two loads move the exponents
+  constexpr int AFMT = C == MOE_MXFP8_B32_A8 ? 0 : 4;  // A operand format of the block-scaled MFMA: fp8, fp4
 #pragma unroll
   for (int q = 0; q < L; ++q) {
     const int nact = half ? H : 2 * H;
@@ -365,7 +404,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       // moving bytes 4 (l % 16) .. + 4 of tile l / 16
       const int t = lane >> 4;
       const uint8_t* sp = t / WF == 0 ? ws0 : ws1;
-      qsrc[q] = sp + ((size_t)(gw * WF + t % WF) * KT) * 64 + (size_t)(lane & 15) * 4;
+      qsrc[q] = sp + ((size_t)(gw * WF + t % WF) * KTS) * 64 + (size_t)(lane & 15) * 4;
       qdst[q] = Ly::SC_OFF + wave * 256;
       qstride[q] = 64;
     } else if (A8 && q == L - 1) {
@@ -411,7 +450,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       qstride[q] = PK * PACKET_BYTES;
     }
   }
-  auto dma_one = [&](int q, int step) {
+  auto dma_one = [&](int q, int step) __attribute__((always_inline)) {
     const int st = kstep0 + min(step, nsteps - 1);
     if (A8 && q >= L - 2)
       __builtin_amdgcn_global_load_lds((const void*)(qsrc[q] + (size_t)st * qstride[q]),
@@ -444,7 +483,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   for (int m = 0; m < NMAT; ++m)
     mcur[m] = scale_mantissa(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv[m]), (kstep0 * PBK) >> 7)));
 
-  auto step_body = [&](int step, auto first_of_block, auto row_tiles) {
+  auto step_body = [&](int step, auto first_of_block, auto row_tiles) __attribute__((always_inline)) {
     constexpr bool RESCALE = SCALED && decltype(first_of_block)::value;
     constexpr int MTA = decltype(row_tiles)::value;  // row tiles of this wave that hold group rows
     // this wave's loads of `step` have landed; after the barrier, every wave's have, and no
@@ -462,23 +501,34 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
         mcur[m] = mn;
       }
     }
-    if constexpr (A8) {
-      // one block-scaled fp4 x fp8 MFMA per (row tile, column tile): the packet as stored (fp4
-      // codes in operand dwords 0-3) with its e8m0 byte, the two 16-byte activation chunks of the
-      // lane with the row tile's exponent byte
+    if constexpr (A8 && MTA == 0) {
+      // no rows in this wave's half of the item: only its share of the next stage's loads
+#pragma unroll
+      for (int q = 0; q < L; ++q) dma_one(q, step + D - 1);
+      return;
+    } else if constexpr (A8) {
+      // one block-scaled MFMA per (row tile, column tile): the weights as stored with their e8m0
+      // byte (fp4: one packet, codes in operand dwords 0-3; fp8: the step's two packets), the two
+      // 16-byte activation chunks of the lane with the row tile's exponent byte
       i32x8 af8[NT];
       int sa[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x4 pk = *(const u32x4*)(base + wbase + t * 1024);
-        af8[t] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+        const u32x4 pk = *(const u32x4*)(base + wbase + t * PK * 1024);
+        if constexpr (PK == 2) {
+          const u32x4 pk1 = *(const u32x4*)(base + wbase + (t * PK + 1) * 1024);
+          af8[t] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3],
+                         (int)pk1[0], (int)pk1[1], (int)pk1[2], (int)pk1[3]};
+        } else {
+          af8[t] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+        }
         sa[t] = base[Ly::SC_OFF + wave * 256 + t * 64 + lane];
       }
       // exponent of (token l % 16, block l / 16) of row tile rt: byte rt * 64 + 4 (l % 16) + l / 16
       const uint8_t* sbp = base + Ly::SC_OFF + 2048 + wrow * 8 * 64 + 4 * j16 + (lane >> 4);
       u32x4 b0n = *(const u32x4*)(base + aoff[0]), b1n = *(const u32x4*)(base + aoff[1]);
       int sbn = sbp[0];
-      constexpr int QA = (L + MTA - 1) / MTA;  // DMA loads per row tile
+      constexpr int QA = (L + MTA - 1) / (MTA > 0 ? MTA : 1);  // DMA loads per row tile
 #pragma unroll
       for (int j = 0; j < MTA; ++j) {
         const u32x4 b0 = b0n, b1 = b1n;
@@ -492,7 +542,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
                                (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          acc[t][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af8[t], bf, acc[t][j], 4, 0, 0, sa[t], 0, sb);
+          acc[t][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af8[t], bf, acc[t][j], AFMT, 0, 0, sa[t], 0, sb);
 #pragma unroll
         for (int u = 0; u < QA; ++u)
           if (j * QA + u < L) dma_one(j * QA + u, step + D - 1);
@@ -539,7 +589,8 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto run_steps = [&](auto row_tiles) {
+  // every instantiation inlined: an outlined copy would pass the captures through scratch memory
+  auto run_steps = [&](auto row_tiles) __attribute__((always_inline)) {
     for (int step = 0; step < nsteps; step += SPB) {
       step_body(step, std::true_type{}, row_tiles);
 #pragma unroll
@@ -555,7 +606,8 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     if (wave_rows > 96) run_steps(std::integral_constant<int, 8>{});
     else if (wave_rows > 64) run_steps(std::integral_constant<int, 6>{});
     else if (wave_rows > 32) run_steps(std::integral_constant<int, 4>{});
-    else run_steps(std::integral_constant<int, 2>{});
+    else if (!Cd::FULL_ONLY || wave_rows > 0) run_steps(std::integral_constant<int, 2>{});
+    else run_steps(std::integral_constant<int, 0>{});  // FULL_ONLY: the item's rows fit in the other half
   } else {
     run_steps(std::integral_constant<int, 8>{});
   }
@@ -716,6 +768,7 @@ static bool prefill_codec_ok(int c, int K) {
   else if (c == MOE_FP8_E4M3_B128) pbk = PCodec<MOE_FP8_E4M3_B128>::PBK;
   else if (c == MOE_MXFP4_B32) pbk = PCodec<MOE_MXFP4_B32>::PBK;
   else if (c == MOE_MXFP4_B32_A8) pbk = PCodec<MOE_MXFP4_B32_A8>::PBK;
+  else if (c == MOE_MXFP8_B32_A8) pbk = PCodec<MOE_MXFP8_B32_A8>::PBK;
   else return false;
   return K % pbk == 0 && K % 128 == 0 && K <= 64 * 128;
 }
@@ -736,6 +789,26 @@ hipError_t launch_w4a8_prefill(int epi, const GroupedArgs& a, int max_units, hip
     if (a.N % (2 * PEpi<EPI_PLAIN>::FULL_F)) return hipErrorInvalidValue;
     return launch_p<MOE_MXFP4_B32_A8, EPI_PLAIN>(a, max_units, st);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_w8a8_shared(int epi, const GroupedArgs& a, int rows, hipStream_t st) {
+  if (!prefill_codec_ok(MOE_MXFP8_B32_A8, a.K) || !a.act_scale || !a.cum_blocks || !a.group_range ||
+      a.g_end != a.g_begin + 1 || rows < 0)
+    return hipErrorInvalidValue;
+  auto go = [&](auto epi_c) -> hipError_t {
+    constexpr int EPI = decltype(epi_c)::value;
+    if (a.N % PEpi<EPI>::FULL_F) return hipErrorInvalidValue;
+    GroupedArgs b = a;
+    b.NTW = a.N / PEpi<EPI>::FULL_F;
+    long long n = (long long)(rows + PBM - 1) / PBM * b.NTW;  // the kernel's item count for the group
+    n = (n + NXCD - 1) / NXCD * NXCD;
+    if (n == 0) return hipSuccess;
+    grouped_prefill_kernel<MOE_MXFP8_B32_A8, EPI><<<(unsigned)n, PTHREADS, 0, st>>>(b);
+    return hipGetLastError();
+  };
+  if (epi == EPI_SWIGLU_Q8) return a.out_scale ? go(std::integral_constant<int, EPI_SWIGLU_Q8>{}) : hipErrorInvalidValue;
+  if (epi == EPI_PLAIN) return go(std::integral_constant<int, EPI_PLAIN>{});
   return hipErrorInvalidValue;
 }
 

@@ -70,6 +70,9 @@ hipError_t launch_grouped_decode(int act, int epi, int cr, int cs, const Grouped
 hipError_t launch_grouped_prefill(int act, int epi, int cr, int cs, const GroupedArgs& a, int max_tiles,
                                   hipStream_t st);
 hipError_t launch_w4a8_prefill(int epi, const GroupedArgs& a, int max_units, hipStream_t st);
+// W8A8 MXFP8 shared expert (one group, [g_begin, g_end) = [shared_group, shared_group + 1), of
+// `rows` rows): gate/up with the MXFP8-writing SwiGLU epilogue, or down.
+hipError_t launch_w8a8_shared(int epi, const GroupedArgs& a, int rows, hipStream_t st);
 int prefill_row_tile();
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down);
 bool prefill_scores_supported(int act, int K, int N);

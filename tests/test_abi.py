@@ -51,6 +51,12 @@ def _shape(**kw):
     (dict(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="mxfp4a8"), 2),
     (dict(H=512, I=256, w_routed="mxfp4a8", path="decode"), 2),
     (dict(H=512, I=128, w_routed="mxfp4a8"), 2), (dict(H=256, I=256, w_routed="mxfp4a8"), 2),
+    # W8A8 MXFP8: the shared expert only, beside W4A8 routed experts
+    (dict(H=512, I=256, w_routed="mxfp8a8"), 2),
+    (dict(H=512, I=256, I_shared=256, w_routed="bf16", w_shared="mxfp8a8"), 2),
+    (dict(H=512, I=256, I_shared=256, w_routed="mxfp4", w_shared="mxfp8a8"), 2),
+    (dict(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="mxfp8a8", path="decode"), 2),
+    (dict(act="f32", w_routed="f32", I_shared=128, w_shared="mxfp8a8"), 2),
 ])
 def test_shape_validation(kw, status):
     with pytest.raises(N.MoeError) as e:
@@ -63,6 +69,14 @@ def test_w4a8_shape_is_accepted_and_adds_quantised_activations():
     a8 = N.moe_workspace_size(_shape(H=512, I=256, w_routed="mxfp4a8"))
     assert a8 > base
     assert N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="bf16")) > a8
+
+
+def test_hybrid_shape_is_accepted_and_quantises_the_shared_rows_of_h():
+    bf = N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="bf16"))
+    mx = N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="mxfp8a8"))
+    # T more rows of h as MXFP8 codes (I bytes each) and exponents (I / 32 bytes each; regions are
+    # 256-byte aligned, so 4 rows of exponents may fit the padding already there)
+    assert mx - bf >= 4 * 256
 
 
 def test_workspace_grows_with_tokens_and_shared_expert():
@@ -80,10 +94,15 @@ def test_pack_sizes():
     assert N.moe_pack_size("mxfp4", 1, 7168, 3072) == (7168 * 3072 // 2, 7168 * 3072 // 32)
     # W4A8 weights are stored and packed exactly as MXFP4
     assert N.moe_pack_size("mxfp4a8", 2, 7168, 3072) == N.moe_pack_size("mxfp4", 2, 7168, 3072)
+    # MXFP8: fp8-sized packets (features padded to 512), one exponent byte per lane per pair of
+    # packets: 32 feature tiles x 2 pairs x 64
+    assert N.moe_pack_size("mxfp8a8", 1, 256, 384) == (32 * 4 * 1024, 32 * 2 * 64)
+    assert N.moe_pack_size("mxfp8a8", 2, 7168, 3072) == (2 * 7168 * 3072, 2 * 7168 * 3072 // 32)
     # the router's E is padded to 256 features (the width of one MFMA item)
     assert N.moe_pack_size("bf16", 1, 256, 8) == (256 * 256 * 2, 0)
     assert N.moe_pack_size("bf16", 1, 7168, 384) == (7168 * 512 * 2, 0)
-    for fmt, K, Nn in (("fp8", 7168, 100), ("fp8", 100, 128), ("bf16", 48, 64), ("mxfp4", 128, 3)):
+    for fmt, K, Nn in (("fp8", 7168, 100), ("fp8", 100, 128), ("bf16", 48, 64), ("mxfp4", 128, 3),
+                       ("mxfp8a8", 64, 256)):
         with pytest.raises(N.MoeError):
             N.moe_pack_size(fmt, 1, K, Nn)
 

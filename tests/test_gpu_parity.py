@@ -28,7 +28,7 @@ def _lib():
 
 # ------------------------------------------------------------------ the input generator
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8"])
 def test_gpu_generator_is_bit_identical_to_numpy(fmt):
     K, Nn = 256, 384
     c, s = G.alloc_matrices(fmt, 2, K, Nn, DEV)
@@ -48,7 +48,7 @@ def test_gpu_activations_bit_identical():
 
 # ------------------------------------------------------------------ packing
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8"])
 def test_pack_layout(fmt):
     """Unpack the packed bytes with numpy following the documented layout."""
     K, Nn = 256, 384
@@ -56,8 +56,7 @@ def test_pack_layout(fmt):
     G.fill_matrices(c, s, fmt, 3, 16, 0, K, Nn, K)
     packed, pscale = pack(fmt, c, s, K, Nn)
     torch.cuda.synchronize()
-    KP = {"f32": 16, "bf16": 32, "fp8": 64, "mxfp4": 128}[fmt]
-    ebytes = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}[fmt]
+    KP = {"f32": 16, "bf16": 32, "fp8": 64, "mxfp4": 128, "mxfp8a8": 64}[fmt]
     NT, KT = Nn // 16, K // KP
     NTp = (Nn + 255) // 256 * 16  # features padded to a multiple of 256 with zero packets
     raw = packed.cpu().numpy().reshape(NTp, KT, 64, 16)
@@ -68,7 +67,7 @@ def test_pack_layout(fmt):
         codes = np.empty((K, Nn), np.uint8)
         codes[:, 0::2], codes[:, 1::2] = stored & 15, stored >> 4
         lanes = np.stack([raw & 15, raw >> 4], axis=-1).reshape(NT, KT, 64, 32)
-    elif fmt == "fp8":
+    elif fmt in ("fp8", "mxfp8a8"):
         codes, lanes = stored, raw
     else:
         dt = np.float32 if fmt == "f32" else np.uint16
@@ -89,6 +88,14 @@ def test_pack_layout(fmt):
         for l in range(64):
             for kt in range(KT):
                 assert np.array_equal(ps[:, kt, l], sc[(kt * KP + (l // 16) * 32) // 32, np.arange(NT) * 16 + l % 16])
+    if fmt == "mxfp8a8":
+        # one exponent byte per lane per pair of packets: lane l of pair kt2 holds the exponent of
+        # feature l % 16 of the tile, elements kt2 * 128 + (l // 16) * 32 .. + 32
+        ps = pscale.cpu().numpy().reshape(NTp, K // 128, 64)[:NT]
+        sc = G.to_numpy_stored(s[0])
+        for l in range(64):
+            for kt2 in range(K // 128):
+                assert np.array_equal(ps[:, kt2, l], sc[kt2 * 4 + l // 16, np.arange(NT) * 16 + l % 16])
 
 
 # ------------------------------------------------------------------ whole layer, small shapes
@@ -132,13 +139,22 @@ SMALL = [
                                      w_shared="bf16", router="zipf", zipf_alpha=1.0, calib_tokens=512,
                                      seed=44)),
     ("w4a8-small-groups", L.LayerSpec("s15", T=96, H=1024, E=24, k=4, I=512, w_routed="mxfp4a8", seed=45)),
+    # the hybrid MXFP8-MXFP4 layer: W4A8 routed experts and a W8A8 MXFP8 shared expert, whose
+    # 256-row items leave a row half empty (T = 300: 44 rows in the last item; T = 1: one row)
+    ("hybrid-mx", L.LayerSpec("s16", T=300, H=512, E=6, k=2, I=256, shared=True, w_routed="mxfp4a8",
+                              w_shared="mxfp8a8", router="zipf", zipf_alpha=1.0, calib_tokens=512, seed=46)),
+    ("hybrid-mx-T200", L.LayerSpec("s17", T=200, H=1024, E=8, k=3, I=512, shared=True, w_routed="mxfp4a8",
+                                   w_shared="mxfp8a8", seed=47)),
+    ("hybrid-mx-one-token", L.LayerSpec("s18", T=1, H=512, E=4, k=2, I=256, shared=True, w_routed="mxfp4a8",
+                                        w_shared="mxfp8a8", seed=48)),
 ]
 
 
 def _prefill_ok(spec):
     fmts = ("bf16", "fp8", "mxfp4")
-    return (spec.act == "bf16" and spec.w_routed in fmts + ("mxfp4a8",) and (not spec.shared or spec.w_shared in fmts)
-            and spec.I % 256 == 0 and spec.H % 512 == 0)
+    shared_fmts = fmts + (("mxfp8a8",) if spec.w_routed == "mxfp4a8" else ())
+    return (spec.act == "bf16" and spec.w_routed in fmts + ("mxfp4a8",)
+            and (not spec.shared or spec.w_shared in shared_fmts) and spec.I % 256 == 0 and spec.H % 512 == 0)
 
 
 @pytest.mark.parametrize("name,spec", SMALL, ids=[s[0] for s in SMALL])
@@ -195,6 +211,8 @@ STAGE_SPECS = [
                               w_shared="fp8", seed=49)),
     ("w4a8+bf16", L.LayerSpec("st50", T=40, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
                               w_shared="bf16", seed=50)),
+    ("w4a8+w8a8", L.LayerSpec("st51", T=40, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
+                              w_shared="mxfp8a8", seed=51)),
 ]
 
 
@@ -255,9 +273,10 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
 # ------------------------------------------------------------------ full-size layers
 
 # the DeepSeek-V4-Pro-shaped layer at a prefill batch: MXFP4 routed experts in the prefill
-# kernel, the bf16 shared expert in a launch of its own; and the same layer with W4A8 routed
-# experts (MXFP8 activations on the block-scaled MFMA)
-FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8"]
+# kernel, the bf16 shared expert in a launch of its own; the same layer with W4A8 routed experts
+# (MXFP8 activations on the block-scaled MFMA); and the hybrid MXFP8-MXFP4 layer (W4A8 routed, W8A8
+# MXFP8 shared)
+FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx"]
 
 
 @pytest.mark.slow
@@ -358,6 +377,8 @@ GRAPH_SPECS = [
                                 w_shared="fp8", seed=62)),
     ("w4a8", L.LayerSpec("g3", T=200, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
                          w_shared="bf16", seed=63)),
+    ("hybrid-mx", L.LayerSpec("g4", T=300, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
+                              w_shared="mxfp8a8", seed=64)),
 ]
 
 
