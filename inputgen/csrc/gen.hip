@@ -6,7 +6,7 @@
 //   * N(0, s^2) = z * s (one fp32 multiply, round to nearest even);
 //   * stored formats: bf16 (round to nearest even), fp8 e4m3fn with one fp32 scale
 //     amax/448 per 128 x 128 block, MXFP4 e2m1 and MXFP8 e4m3fn with one e8m0 exponent per 32 K
-//     of a column.
+//     of a column, int8 with one fp32 scale amax/127 per column.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -237,6 +237,40 @@ __global__ void fill_mxfp8_kernel(uint8_t* codes, uint8_t* scales, uint32_t k0, 
   *(uint32_t*)(scales + (size_t)m * (K / 32) * N + (size_t)kb * N + c0) = E[0] | (E[1] << 8) | (E[2] << 16) | (E[3] << 24);
 }
 
+// Int8 per output channel: one thread per 4 consecutive columns of one K x N matrix, two passes over
+// the column (the maximum, then the codes): s = amax / 127, code = rint(w / s), clamped to +-127.
+__global__ void fill_int8_kernel(int8_t* codes, float* scales, uint32_t k0, uint32_t k1, uint32_t stream0, int count,
+                                 int K, int N, float sigma, const int32_t* T, const int32_t* TT) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)count * (N / 4)) return;
+  const int m = (int)(gid / (N / 4));
+  const int c0 = 4 * (int)(gid % (N / 4));
+  float amax[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < K; ++r) {
+    uint32_t w[4];
+    block_words(((uint64_t)r * N + c0) / 4, stream0 + (uint32_t)m, k0, k1, w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax[i] = fmaxf(amax[i], fabsf(__fmul_rn(normal_of(w[i], T, TT), sigma)));
+  }
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] = amax[i] > 0.0f ? __fdiv_rn(amax[i], 127.0f) : 1.0f;
+  int8_t* cm = codes + (size_t)m * K * N;
+  for (int r = 0; r < K; ++r) {
+    uint32_t w[4];
+    block_words(((uint64_t)r * N + c0) / 4, stream0 + (uint32_t)m, k0, k1, w);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float q = rintf(__fdiv_rn(__fmul_rn(normal_of(w[i], T, TT), sigma), sc[i]));
+      q = fminf(fmaxf(q, -127.0f), 127.0f);
+      word |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * i);
+    }
+    *(uint32_t*)(cm + (size_t)r * N + c0) = word;
+  }
+  *(float4*)(scales + (size_t)m * N + c0) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+}
+
 // A plain 16-byte-per-lane copy: the known-size reference for hardware byte counters.
 __global__ void __launch_bounds__(256) copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                      long long n16) {
@@ -394,6 +428,16 @@ int gen_fill_mxfp8(uint8_t* codes, uint8_t* scales, uint32_t k0, uint32_t k1, ui
   if (!threads) return 0;
   fill_mxfp8_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(codes, scales, k0, k1, stream0, count, K, N,
                                                                        sigma, T, TT);
+  return (int)hipGetLastError();
+}
+
+int gen_fill_int8(int8_t* codes, float* scales, uint32_t k0, uint32_t k1, uint32_t stream0, int count, int K, int N,
+                  float sigma, const int32_t* T, const int32_t* TT, hipStream_t st) {
+  if (N % 4) return -1;
+  const long long threads = (long long)count * (N / 4);
+  if (!threads) return 0;
+  fill_int8_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(codes, scales, k0, k1, stream0, count, K, N,
+                                                                      sigma, T, TT);
   return (int)hipGetLastError();
 }
 

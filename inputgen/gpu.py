@@ -43,6 +43,7 @@ def lib():
         _lib.gen_fill_fp8.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_fill_mxfp4.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_fill_mxfp8.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
+        _lib.gen_fill_int8.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_copy.argtypes = [p, p, i64, p]
         _lib.gen_stream_read.argtypes = [p, i64, p, p]
         _lib.gen_mfma_burst.argtypes = [i32, i32, i32, p, p]
@@ -115,6 +116,9 @@ def alloc_matrices(fmt: str, count: int, K: int, N: int, device):
     if fmt == "mxfp8a8":
         return (torch.empty((count, K, N), dtype=torch.uint8, device=device),
                 torch.empty((count, K // 32, N), dtype=torch.uint8, device=device))
+    if fmt == "int8":
+        return (torch.empty((count, K, N), dtype=torch.int8, device=device),
+                torch.empty((count, N), dtype=torch.float32, device=device))
     raise ValueError(fmt)
 
 
@@ -130,6 +134,9 @@ def fill_matrices(codes, scales, fmt: str, seed: int, tid: int, stream0: int, K:
     elif fmt == "fp8":
         _chk(lib().gen_fill_fp8(codes.data_ptr(), scales.data_ptr(), seed, tid, stream0, count, K, N, s,
                                 T.data_ptr(), TT.data_ptr(), st), "fp8")
+    elif fmt == "int8":
+        _chk(lib().gen_fill_int8(codes.data_ptr(), scales.data_ptr(), seed, tid, stream0, count, K, N, s,
+                                 T.data_ptr(), TT.data_ptr(), st), "int8")
     elif fmt == "mxfp8a8":
         _chk(lib().gen_fill_mxfp8(codes.data_ptr(), scales.data_ptr(), seed, tid, stream0, count, K, N, s,
                                   T.data_ptr(), TT.data_ptr(), st), "mxfp8")

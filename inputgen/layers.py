@@ -25,6 +25,8 @@ Stored formats (logical row-major, the layout in which the pages write the matri
 * ``mxfp8a8``: uint8[K, N] E4M3FN codes + uint8[K/32, N] e8m0 exponents (w = e4m3 * 2^(E-127),
   one exponent per 32 consecutive K of a column); the layer quantises the expert's activations to
   MXFP8 for its products (W8A8 MXFP8, the shared expert of the hybrid MXFP8-MXFP4 layer)
+* ``int8``: int8[K, N] codes + float32[N] scales, one per output column (w = code * s[n]); the layer
+  quantises the expert's activations to int8 per token for its products (Int8 W8A8)
 
 with (K, N) = (H, I) for gate and up and (I, H) for down.
 
@@ -49,7 +51,7 @@ TID_ROUTED = {"gate": 16, "up": 17, "down": 18}
 TID_SHARED = {"gate": 24, "up": 25, "down": 26}
 
 ACT_DTYPES = ("f32", "bf16")
-W_DTYPES = ("f32", "bf16", "fp8", "mxfp4", "mxfp4a8", "mxfp8a8")
+W_DTYPES = ("f32", "bf16", "fp8", "mxfp4", "mxfp4a8", "mxfp8a8", "int8")
 
 
 @dataclass(frozen=True)
@@ -94,12 +96,14 @@ CONFIGS = {
 # Further workloads measured beside the configurations above: the DeepSeek-V4-Pro-shaped layer at a
 # prefill batch (T * k = 64 E, where the path switches to the MFMA kernel), with MXFP4 routed
 # experts and bf16 activations, with W4A8 routed experts (activations quantised to MXFP8), and in
-# the hybrid MXFP8-MXFP4 scheme: W4A8 routed experts and a W8A8 MXFP8 shared expert.
+# the hybrid MXFP8-MXFP4 scheme: W4A8 routed experts and a W8A8 MXFP8 shared expert. The
+# DeepSeek-V3-shaped prefill layer with Int8 W8A8 routed and shared experts.
 EXTRA = {
     "v4p": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096),
     "v4p-w4a8": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-w4a8", T=4096, w_routed="mxfp4a8"),
     "v4p-mx": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-hybrid-mxfp8-mxfp4", T=4096,
                                     w_routed="mxfp4a8", w_shared="mxfp8a8"),
+    "v3-int8": CONFIGS["c5"].replace(name="deepseek-v3-moe-prefill-int8-w8a8", w_routed="int8", w_shared="int8"),
 }
 
 
@@ -150,6 +154,9 @@ def store_matrix(w: np.ndarray, fmt: str) -> dict:
         return {"w": c, "scale": s}
     if fmt == "mxfp8a8":
         c, s = px.quantize_mxfp8_k32(w)
+        return {"w": c, "scale": s}
+    if fmt == "int8":
+        c, s = px.quantize_int8_per_channel(w)
         return {"w": c, "scale": s}
     raise ValueError(fmt)
 

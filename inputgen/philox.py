@@ -193,6 +193,19 @@ def quantize_mxfp8_k32(w: np.ndarray):
     return f32_to_e4m3fn(v), E.astype(np.uint8)
 
 
+def quantize_int8_per_channel(w: np.ndarray):
+    """W[K, N] fp32 -> (codes int8[K, N], scales fp32[N]).
+
+    One scale per output column: s = amax / 127 (fp32 division), codes = w / s (fp32 division)
+    rounded to the nearest integer, ties to even, clamped to [-127, 127]. An all-zero column gets
+    s = 1.
+    """
+    amax = np.abs(w).max(axis=0).astype(np.float32)
+    s = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = np.rint((np.asarray(w, np.float32) / s[None, :]).astype(np.float32))
+    return np.clip(q, -127, 127).astype(np.int8), s
+
+
 def quantize_mxfp4_k32(w: np.ndarray):
     """W[K, N] fp32 -> (packed codes uint8[K, N/2], e8m0 scales uint8[K/32, N]).
 

@@ -17,6 +17,9 @@
  *   mxfp8a8  uint8[K][N] OCP E4M3FN + uint8[K/32][N] e8m0     (w = e4m3(code) * 2^(E-127));
  *            the expert's activations are quantised to MXFP8 before each of its products
  *            (W8A8 MXFP8, the shared expert of the hybrid MXFP8-MXFP4 scheme)
+ *   int8     int8[K][N] + float[N], one scale per output channel  (w = code * s[n]);
+ *            the expert's activations are quantised to int8 per token before each of its
+ *            products (Int8 W8A8, see oracle_int8_quantize)
  *
  * What it computes, step by step (sources: "AI infra book, ch. 6 Supernodes" (bojieli.github.io
  * ai-infra-book ch. 6) = [ch6]; "DeepSeek-V4-Pro on NVIDIA H200" report = [V4]):
@@ -36,7 +39,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_MXFP4_A8 = 4, OR_MXFP8_A8 = 5 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_MXFP4_A8 = 4, OR_MXFP8_A8 = 5, OR_INT8 = 6 };
 
 /* storage format of a weight format (W4A8 stores its weights as MXFP4) */
 static int stored(int fmt) { return fmt == OR_MXFP4_A8 ? OR_MXFP4 : fmt; }
@@ -101,6 +104,7 @@ static double w_at(const void* w, const void* scale, int fmt, int K, int N, int 
       uint8_t E = ((const uint8_t*)scale)[(size_t)(k / 32) * N + n];
       return oracle_decode_e4m3fn(((const uint8_t*)w)[i]) * oracle_decode_e8m0(E);
     }
+    case OR_INT8: return (double)((const int8_t*)w)[i] * (double)((const float*)scale)[n];
   }
   return NAN;
 }
@@ -112,7 +116,8 @@ static size_t w_bytes(int fmt, int K, int N) {
     case OR_BF16: return (size_t)K * N * 2;
     case OR_FP8: return (size_t)K * N;
     case OR_MXFP4: return (size_t)K * N / 2;
-    case OR_MXFP8_A8: return (size_t)K * N;
+    case OR_MXFP8_A8:
+    case OR_INT8: return (size_t)K * N;
   }
   return 0;
 }
@@ -121,6 +126,7 @@ static size_t s_bytes(int fmt, int K, int N) {
     case OR_FP8: return (size_t)(K / 128) * (N / 128) * 4;
     case OR_MXFP4:
     case OR_MXFP8_A8: return (size_t)(K / 32) * N;
+    case OR_INT8: return (size_t)N * 4;
   }
   return 0;
 }
@@ -286,6 +292,53 @@ static int mxfp8_roundtrip(int K, double* v) {
   return rc;
 }
 
+/* ---------------------------------------------------------------------------------------- */
+/* Int8 W8A8: activations quantised to int8 per token                                       */
+/*                                                                                          */
+/* [CANN] "CANN DeepSeek-V4推理优化", Int8 quantisation strategy: the routed and shared      */
+/* experts' linear layers run W8A8, weights statically quantised to int8 per output channel, */
+/* activations dynamically to int8 per token. Per token (one row of K values), in fp32: the  */
+/* largest magnitude a, the factor f = 127 / a and the scale s = a / 127 (fp32 divisions),    */
+/* and each code q = v * f (fp32 product) rounded to the nearest integer, ties to even,     */
+/* clamped to [-127, 127]; the row then stands for q * s. An all-zero row has s = 0, q = 0.  */
+/* The rows quantised here (bf16 values, or h after its bf16 rounding) are exact in fp32,    */
+/* so this decision is the same on any IEEE machine.                                        */
+/* ---------------------------------------------------------------------------------------- */
+
+int oracle_int8_quantize(int K, const double* v, int8_t* codes, float* scale) {
+  float a = 0.0f;
+  for (int i = 0; i < K; ++i) {
+    const float x = (float)v[i];
+    if ((double)x != v[i]) return 1; /* the row must be exact in fp32 */
+    a = fmaxf(a, fabsf(x));
+  }
+  if (a == 0.0f) {
+    memset(codes, 0, (size_t)K);
+    *scale = 0.0f;
+    return 0;
+  }
+  volatile float f = 127.0f / a, s = a / 127.0f; /* fp32 roundings, not extended precision */
+  for (int i = 0; i < K; ++i) {
+    volatile float p = (float)v[i] * f;
+    float q = rintf(p);
+    if (q > 127.0f) q = 127.0f;
+    if (q < -127.0f) q = -127.0f;
+    codes[i] = (int8_t)q;
+  }
+  *scale = s;
+  return 0;
+}
+
+/* v -> the value its int8 encoding stands for, in place. */
+static int int8_roundtrip(int K, double* v) {
+  int8_t* c = (int8_t*)malloc(K);
+  float s = 0.0f;
+  int rc = !c ? 2 : oracle_int8_quantize(K, v, c, &s);
+  for (int i = 0; i < K && !rc; ++i) v[i] = (double)c[i] * (double)s;
+  free(c);
+  return rc;
+}
+
 /* v rounded to the nearest bfloat16 (8 significant bits), ties to even. */
 static double bf16_round(double v) {
   if (v == 0.0 || !isfinite(v)) return v;
@@ -296,12 +349,13 @@ static double bf16_round(double v) {
 
 /* W4A8 (fmt mxfp4a8) and W8A8 MXFP8 (fmt mxfp8a8): the row is quantised to MXFP8 before gate/up;
  * h = SiLU(g) * v is rounded to bf16, the type the layer keeps it in between the two products,
- * then quantised to MXFP8 before down. Other formats multiply the rows as given. */
+ * then quantised to MXFP8 before down. Int8 W8A8 (fmt int8): the same with the per-token int8
+ * quantisation. Other formats multiply the rows as given. */
 int oracle_expert_ffn(int H, int I, int M, int fmt, const void* wg, const void* sg,
                       const void* wu, const void* su, const void* wd, const void* sd,
                       const double* u, double* y) {
   int bad = 0;
-  const int a8 = fmt == OR_MXFP4_A8 || fmt == OR_MXFP8_A8;
+  const int a8 = fmt == OR_MXFP4_A8 || fmt == OR_MXFP8_A8, i8 = fmt == OR_INT8;
 #pragma omp parallel for schedule(dynamic, 1) if (M > 1)
   for (int m = 0; m < M; ++m) {
     double* g = (double*)malloc(sizeof(double) * I);
@@ -312,12 +366,13 @@ int oracle_expert_ffn(int H, int I, int M, int fmt, const void* wg, const void* 
     } else {
       memcpy(uq, u + (size_t)m * H, sizeof(double) * H);
       if (a8 && mxfp8_roundtrip(H, uq)) bad = 1;
+      if (i8 && int8_roundtrip(H, uq)) bad = 1;
       oracle_row_matmul(H, I, fmt, wg, sg, uq, g);
       oracle_row_matmul(H, I, fmt, wu, su, uq, v);
       for (int i = 0; i < I; ++i) g[i] = silu(g[i]) * v[i];
-      if (a8) {
+      if (a8 || i8) {
         for (int i = 0; i < I; ++i) g[i] = bf16_round(g[i]);
-        if (mxfp8_roundtrip(I, g)) bad = 1;
+        if (a8 ? mxfp8_roundtrip(I, g) : int8_roundtrip(I, g)) bad = 1;
       }
       oracle_row_matmul(I, H, fmt, wd, sd, g, y + (size_t)m * H);
     }

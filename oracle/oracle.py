@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "moe_oracle.c")
 LIB = os.path.join(HERE, "libmoe_oracle.so")
 
-FMT = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "mxfp4a8": 4, "mxfp8a8": 5}
+FMT = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "mxfp4a8": 4, "mxfp8a8": 5, "int8": 6}
 
 _lib = None
 
@@ -45,6 +45,7 @@ def lib() -> ctypes.CDLL:
             getattr(_lib, name).argtypes = [ctypes.c_uint8]
         _lib.oracle_decode_matrix.argtypes = [i, i, i, p, p, p]
         _lib.oracle_mxfp8_quantize.argtypes = [i, p, p, p]
+        _lib.oracle_int8_quantize.argtypes = [i, p, p, p]
         _lib.oracle_row_matmul.argtypes = [i, i, i, p, p, p, p]
         _lib.oracle_route.argtypes = [i, i, i, i, i, p, p, p, p, p, p]
         _lib.oracle_permute.argtypes = [i, i, i, p, p, p, p]
@@ -69,11 +70,11 @@ def _check(rc, what):
 
 def _wdtype(fmt):
     return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "mxfp4": np.uint8,
-            "mxfp4a8": np.uint8, "mxfp8a8": np.uint8}[fmt]
+            "mxfp4a8": np.uint8, "mxfp8a8": np.uint8, "int8": np.int8}[fmt]
 
 
 def _sdtype(fmt):
-    return {"fp8": np.float32, "mxfp4": np.uint8, "mxfp4a8": np.uint8, "mxfp8a8": np.uint8}.get(fmt)
+    return {"fp8": np.float32, "mxfp4": np.uint8, "mxfp4a8": np.uint8, "mxfp8a8": np.uint8, "int8": np.float32}.get(fmt)
 
 
 def decode_scalar(fmt: str, code: int) -> float:
@@ -92,6 +93,18 @@ def mxfp8_quantize(v):
     for r in range(rows.shape[0]):
         _check(lib().oracle_mxfp8_quantize(K, _ptr(rows[r]), _ptr(codes[r]), _ptr(scales[r])), "mxfp8")
     return codes.reshape(v.shape), scales.reshape(v.shape[:-1] + (K // 32,))
+
+
+def int8_quantize(v):
+    """v[..., K] (rows exact in fp32) -> (int8 codes [..., K], fp32 scales [...]), per row."""
+    v = _c(v, np.float64)
+    K = v.shape[-1]
+    rows = v.reshape(-1, K)
+    codes = np.empty(rows.shape, np.int8)
+    scales = np.empty(rows.shape[0], np.float32)
+    for r in range(rows.shape[0]):
+        _check(lib().oracle_int8_quantize(K, _ptr(rows[r]), _ptr(codes[r]), _ptr(scales[r:r + 1])), "int8")
+    return codes.reshape(v.shape), scales.reshape(v.shape[:-1])
 
 
 def decode_matrix(fmt: str, K: int, N: int, w, scale=None) -> np.ndarray:

@@ -99,6 +99,17 @@ def test_mxfp8_scale_puts_block_max_in_256_to_512_saturating_at_448():
     assert np.all(dec[~inside] == np.sign(scaled[~inside]) * 448)
 
 
+def test_int8_per_channel_scale_and_codes():
+    """Int8 weights: s = amax / 127 per output column, the column maximum at code +-127, every
+    code the nearest integer to w / s."""
+    w = px.normal_f32(2, 4, 0, 0, 64 * 48).reshape(64, 48) * np.float32(0.02)
+    codes, s = px.quantize_int8_per_channel(w)
+    assert s.shape == (48,) and codes.dtype == np.int8
+    assert np.allclose(s, np.abs(w).max(axis=0) / 127, rtol=1e-6)
+    assert np.all(np.abs(codes.astype(np.int64)).max(axis=0) == 127)
+    assert np.all(np.abs(codes - w.astype(np.float64) / s) <= 0.5 + 1e-5)
+
+
 def test_generation_is_deterministic_and_seeded():
     s = L.CONFIGS["c1"]
     a, b = L.router_inputs(s), L.router_inputs(s)

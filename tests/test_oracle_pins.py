@@ -51,7 +51,7 @@ def test_bf16_matches_torch():
     assert np.array_equal(got, ref.astype(np.float64))
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8", "int8"])
 def test_decode_matrix_layout(fmt):
     """The matrix decoder against an independent numpy/torch decode of the stored layout."""
     K, N = 256, 256
@@ -68,6 +68,11 @@ def test_decode_matrix_layout(fmt):
     elif fmt == "mxfp8a8":
         v = torch.from_numpy(st["w"]).view(torch.float8_e4m3fn).double().numpy()
         ref = v * np.repeat(np.ldexp(1.0, st["scale"].astype(np.int64) - 127), 32, axis=0)
+    elif fmt == "int8":
+        ref = st["w"].astype(np.float64) * st["scale"].astype(np.float64)[None, :]
+        # per output column: the largest magnitude is code +-127, every value within half a step
+        assert np.array_equal(np.abs(st["w"].astype(np.int64)).max(axis=0), np.full(N, 127))
+        assert np.all(np.abs(ref - w) <= 0.5 * st["scale"][None, :] * (1 + 1e-6))
     else:
         lo, hi = st["w"] & 15, st["w"] >> 4
         codes = np.empty((K, N), np.uint8)
@@ -77,8 +82,8 @@ def test_decode_matrix_layout(fmt):
         ref = table[codes] * np.repeat(scale, 32, axis=0)
     assert np.array_equal(got, ref)
     # the stored value is the nearest representable one: relative error bound of the format
-    rel = {"f32": 0, "bf16": 2 ** -8, "fp8": 2 ** -3, "mxfp4": 0.5, "mxfp8a8": 2 ** -3}[fmt]
-    if fmt not in ("mxfp4", "mxfp8a8"):
+    rel = {"f32": 0, "bf16": 2 ** -8, "fp8": 2 ** -3, "mxfp4": 0.5, "mxfp8a8": 2 ** -3, "int8": 1}[fmt]
+    if fmt not in ("mxfp4", "mxfp8a8", "int8"):
         assert np.all(np.abs(got - w) <= rel * np.abs(w) + 2 ** -9 * 1e-1)
 
 
@@ -533,6 +538,83 @@ def test_layer_hybrid_mxfp8_shared_changes_only_the_shared_expert():
     dy = O.expert_ffn(xf, sh8, "mxfp8a8") - O.expert_ffn(xf, sh16, "bf16")
     assert np.allclose(a["y"] - b["y"], dy, rtol=1e-9, atol=1e-12)
     assert np.abs(dy).max() > 0
+
+
+# ------------------------------------------------------------------ Int8 W8A8
+# 'CANN DeepSeek-V4推理优化', Int8 quantisation strategy: routed and shared experts' linear layers
+# run W8A8, weights int8 per output channel (static), activations int8 per token (dynamic).
+
+def test_int8_quantize_hand_values():
+    """Per token, in fp32: f = 127 / max|v|, q = rint(v f) ties to even, s = max|v| / 127."""
+    v = np.array([127.0, -63.5, 0.5, 1.5, 2.5, -127.0, 0.0, -0.5])
+    c, sc = O.int8_quantize(v)
+    assert c.tolist() == [127, -64, 0, 2, 2, -127, 0, 0] and sc == np.float32(1.0)
+    v = np.array([2.0, 1.0, -1.0, 0.0])  # f = 63.5: 1.0 -> 63.5 -> 64 (even), -1.0 -> -64
+    c, sc = O.int8_quantize(v)
+    assert c.tolist() == [127, 64, -64, 0] and sc == np.float32(2.0) / np.float32(127.0)
+    c, sc = O.int8_quantize(np.zeros(5))
+    assert not c.any() and sc == 0.0
+    with pytest.raises(RuntimeError):  # rows must be exact in fp32
+        O.int8_quantize(np.array([1.0 + 2.0 ** -40]))
+
+
+def test_int8_quantize_error_bound_on_random_rows():
+    """Every code within [-127, 127], the row maximum at +-127, and q s within half a step of v."""
+    v = L.act_to_f64(L.store_act(px.normal_f32(5, 9, 0, 0, 8 * 512).reshape(8, 512), "bf16"), "bf16")
+    c, sc = O.int8_quantize(v)
+    assert np.all(np.abs(c.astype(np.int64)).max(axis=1) == 127)
+    err = np.abs(c.astype(np.float64) * sc[:, None].astype(np.float64) - v)
+    # half a step, widened by the separate fp32 roundings of f and s (f s = 1 within ~2^-23, times
+    # |q| <= 127) and of the product v f
+    assert np.all(err <= 0.5 * sc[:, None] * (1 + 1e-4))
+    assert (err / sc[:, None]).max() > 0.45  # and the bound is nearly reached
+
+
+def _int8_roundtrip_np(v):
+    """The per-token int8 round trip, written independently with numpy float32 operations."""
+    v32 = np.asarray(v, np.float32)
+    a = np.abs(v32).max(axis=-1, keepdims=True)
+    f = np.float32(127.0) / a
+    q = np.clip(np.rint((v32 * f).astype(np.float32)), -127, 127)
+    return q.astype(np.float64) * (a / np.float32(127.0)).astype(np.float64)
+
+
+def test_expert_ffn_int8_w8a8_is_quantised_swiglu():
+    """Int8 W8A8 FFN = down(Q(bf16(SiLU(Q(u) Wg) * (Q(u) Wu)))) with Q the per-token int8 round
+    trip, the products on the per-channel int8 weights; near the FFN of the unquantised weights."""
+    H, I, M = 256, 128, 4
+    s = L.LayerSpec("i", T=M, H=H, E=1, k=1, I=I, w_routed="int8")
+    wts = L.expert_weights(s, "routed", 0)
+    u = L.act_to_f64(L.store_act(px.normal_f32(3, 7, 0, 0, M * H).reshape(M, H), "bf16"), "bf16")
+    y = O.expert_ffn(u, wts, "int8")
+    g = wts["gate"].astype(np.float64) * wts["gate_scale"].astype(np.float64)
+    v = wts["up"].astype(np.float64) * wts["up_scale"].astype(np.float64)
+    d = wts["down"].astype(np.float64) * wts["down_scale"].astype(np.float64)
+    uq = _int8_roundtrip_np(u)
+    assert not np.array_equal(uq, u)
+    h = torch.nn.functional.silu(torch.from_numpy(uq @ g)).numpy() * (uq @ v)
+    ref = _int8_roundtrip_np(_bf16_round(h)) @ d
+    assert np.allclose(y, ref, rtol=1e-9, atol=1e-11)
+    f = {n: L.draw_f32(s.seed, L.TID_ROUTED[n], 0, shp, fan).astype(np.float32)
+         for n, shp, fan in (("gate", (H, I), H), ("up", (H, I), H), ("down", (I, H), I))}
+    y32 = O.expert_ffn(u, {"gate": f["gate"], "up": f["up"], "down": f["down"],
+                           "gate_scale": None, "up_scale": None, "down_scale": None}, "f32")
+    rel = np.linalg.norm(y - y32) / np.linalg.norm(y32)
+    assert 3e-3 < rel < 4e-2
+
+
+def test_layer_int8_routes_like_bf16():
+    """Int8 W8A8 changes only the experts' products: routing and permutation equal the bf16
+    layer's (same router inputs)."""
+    s = L.LayerSpec("i8", T=8, H=128, E=4, k=2, I=128, act="bf16", shared=True, w_routed="int8",
+                    w_shared="int8", seed=12)
+    r = L.router_inputs(s)
+    a = O.layer(s, r["x"], r["Wr"], r["bias"], L.stack_experts(s), L.expert_weights(s, "shared", 0))
+    sb = s.replace(w_routed="bf16", w_shared="bf16")
+    b = O.layer(sb, r["x"], r["Wr"], r["bias"], L.stack_experts(sb), L.expert_weights(sb, "shared", 0))
+    assert np.array_equal(a["topk_idx"], b["topk_idx"]) and np.array_equal(a["pair_slot"], b["pair_slot"])
+    rel = np.linalg.norm(a["y"] - b["y"]) / np.linalg.norm(b["y"])
+    assert 1e-3 < rel < 4e-2
 
 
 def test_layer_w4a8_routes_like_mxfp4():
