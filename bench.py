@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 HBM_PEAK_GBPS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "int8": 5000.0}
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads for the plain copy
 # kernel of known size that --calib-copy appends. Keyed by workload; an entry holds only while
@@ -35,7 +35,8 @@ TRAFFIC = {
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
                   "prefill": ("gemm_prefill.hip", "common.h", "kernels.h"),
-                  "w4a8": ("gemm_prefill.hip", "quant.hip", "common.h", "kernels.h")}
+                  "w4a8": ("gemm_prefill.hip", "quant.hip", "common.h", "kernels.h"),
+                  "int8": ("gemm_prefill.hip", "quant.hip", "common.h", "kernels.h")}
 
 
 def kernel_sha(path: str) -> str:
@@ -55,7 +56,7 @@ def measured_traffic(config: str, path: str):
 
 
 # bounded CPU-oracle samples (tokens): about 10-30 s of oracle work per config
-CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4, "v4p": 6, "v4p-w4a8": 6, "v4p-mx": 6}
+CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4, "v4p": 6, "v4p-w4a8": 6, "v4p-mx": 6, "v3-int8": 4}
 
 
 def log(*a):
@@ -67,10 +68,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx"],
+    ap.add_argument("--config", default="c2",
+                    choices=["c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8"],
                     help="c1-c5: the layer configurations; v4p, v4p-w4a8, v4p-mx: the V4-Pro-shaped layer at a "
                          "prefill batch with MXFP4 / W4A8 routed experts, and in the hybrid MXFP8-MXFP4 scheme "
-                         "(W4A8 routed, W8A8 MXFP8 shared)")
+                         "(W4A8 routed, W8A8 MXFP8 shared); v3-int8: the c5 layer with Int8 W8A8 experts")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=None)
@@ -191,13 +193,14 @@ def main():
 
     mfma_ceiling = None
     a8 = spec.w_routed == "mxfp4a8"
-    if not args.no_ceiling and (a8 or (spec.T * spec.k) / spec.E >= 64):
+    i8 = spec.w_routed == "int8"
+    if not args.no_ceiling and (a8 or i8 or (spec.T * spec.k) / spec.E >= 64):
         # the matrix-core rates this GPU sustains with GEMM-like (changing, random) operands:
         # register-only MFMA bursts of the GEMMs' instruction kinds, 2 waves per SIMD
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         mfma_ceiling = {}
         kinds = ((0, "bf16 16x16x32"), (1, "fp4 x fp8 16x16x128"), (2, "fp8 x fp8 16x16x128")) if a8 else \
-            ((0, "bf16 16x16x32"),)
+            ((3, "int8 16x16x64"),) if i8 else ((0, "bf16 16x16x32"),)
         for kind, name in kinds:
             iters = 2048 if kind else 8192
             G.mfma_burst(kind, iters, 512, sink)
@@ -231,12 +234,15 @@ def main():
         # and the shared rows in the hybrid scheme) or bf16 (a bf16 shared expert)
         gu_bytes = int(w_bytes + T * H * ab + 2 * T * H * q + T * k * I * q
                        + (T * I * (q if mx else ab) if spec.shared else 0))
+    elif i8:
+        # x read once as bf16, its int8 copy (and a scale per token) written and read once, h in bf16
+        gu_bytes = w_bytes + T * H * ab + 2 * (T * H + 4 * T) + R * I * ab
     else:
         gu_bytes = w_bytes + T * H * ab + R * I * ab
     gu_flops = 4 * H * I * R
     gu_ms = stage_ms[names.index("gate_up")]
-    prefill = a8 or (T * k) / spec.E >= 64
-    traffic_b = measured_traffic(args.config, "w4a8" if a8 else "prefill" if prefill else "decode")
+    prefill = a8 or i8 or (T * k) / spec.E >= 64
+    traffic_b = measured_traffic(args.config, "w4a8" if a8 else "int8" if i8 else "prefill" if prefill else "decode")
     hbm_ach = gu_bytes / (gu_ms * 1e-3) / 1e9
     hbm_roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(hbm_ach / HBM_PEAK_GBPS, 4),
@@ -254,12 +260,16 @@ def main():
                              "(bf16 peak 2500)")
         per_launch = {"flops": gu_flops, "routed_flops": fr, "shared_flops": fs, "bytes": gu_bytes,
                       "ms": round(gu_ms, 4)}
+    elif i8:
+        peak = MFMA_PEAK_TFLOPS["int8"]
+        kernel = "gate/up stage: x to int8 per token, Int8 W8A8 grouped GEMM (int8 peak 5000 TOP/s)"
+        per_launch = {"ops": gu_flops, "bytes": gu_bytes, "ms": round(gu_ms, 4)}
     else:
         peak = MFMA_PEAK_TFLOPS["bf16" if spec.act == "bf16" else "f32"]
         kernel = "gate/up grouped GEMM"
         per_launch = {"flops": gu_flops, "bytes": gu_bytes, "ms": round(gu_ms, 4)}
     mfma_ach = gu_flops / (gu_ms * 1e-3) / 1e12
-    mfma_roof = {"bound": "mfma", "achieved": round(mfma_ach, 1), "peak": peak, "unit": "TFLOP/s",
+    mfma_roof = {"bound": "mfma", "achieved": round(mfma_ach, 1), "peak": peak, "unit": "TOP/s" if i8 else "TFLOP/s",
                  "frac": round(mfma_ach / peak, 4)}
     if mfma_ceiling and prefill:
         if a8:
@@ -268,7 +278,7 @@ def main():
             t_meas = fr / (mfma_ceiling["fp4 x fp8 16x16x128"] * 1e12) + fs / (rs * 1e12)
             mfma_roof["frac_of_measured_mfma"] = round(t_meas / (gu_ms * 1e-3), 4)
         else:
-            mfma_roof["frac_of_measured_mfma"] = round(mfma_ach / mfma_ceiling["bf16 16x16x32"], 4)
+            mfma_roof["frac_of_measured_mfma"] = round(mfma_ach / mfma_ceiling["int8 16x16x64" if i8 else "bf16 16x16x32"], 4)
     t_hbm = gu_bytes / (HBM_PEAK_GBPS * 1e9)
     t_mfma = gu_flops / (peak * 1e12)
     binding, other = (mfma_roof, hbm_roof) if prefill and t_mfma >= t_hbm else (hbm_roof, mfma_roof)

@@ -38,7 +38,7 @@ int pad64(int n) { return (n + 63) / 64 * 64; }
 int pad256(int n) { return (n + 255) / 256 * 256; }
 constexpr int ROW_BLOCK = 64;
 
-bool valid_fmt(int f) { return f >= MOE_F32 && f <= MOE_MXFP8_B32_A8; }
+bool valid_fmt(int f) { return f >= MOE_F32 && f <= MOE_INT8_W8A8; }
 // storage format: W4A8 weights are stored and packed as MXFP4
 moe_dtype stored_fmt(moe_dtype f) { return f == MOE_MXFP4_B32_A8 ? MOE_MXFP4_B32 : f; }
 
@@ -54,6 +54,8 @@ moe_status packed_sizes(moe_dtype fmt, int count, int K, int N, size_t* bytes, s
   if (fmt == MOE_MXFP4_B32 && N % 2) return fail(MOE_ERR_INVALID_ARG, "MXFP4 packs N=%d in pairs", N);
   if (fmt == MOE_MXFP8_B32_A8 && K % 128)
     return fail(MOE_ERR_INVALID_ARG, "MXFP8 scales are packed per 128 reduction elements (K=%d)", K);
+  if (fmt == MOE_INT8_W8A8 && K % 128)
+    return fail(MOE_ERR_INVALID_ARG, "INT8 products run 128 reduction elements per step (K=%d)", K);
   const size_t NT = pad256(N) / 16, KT = K / KP;
   *bytes = (size_t)count * NT * KT * PACKET_BYTES;
   if (fmt == MOE_FP8_E4M3_B128)
@@ -62,6 +64,8 @@ moe_status packed_sizes(moe_dtype fmt, int count, int K, int N, size_t* bytes, s
     *sbytes = (size_t)count * NT * KT * 64;
   else if (fmt == MOE_MXFP8_B32_A8)
     *sbytes = (size_t)count * NT * (K / 128) * 64;
+  else if (fmt == MOE_INT8_W8A8)
+    *sbytes = (size_t)count * NT * 16 * 4;
   else
     *sbytes = 0;
   return MOE_OK;
@@ -91,6 +95,15 @@ moe_status check_shape(const moe_shape* s) {
     return fail(MOE_ERR_UNSUPPORTED, "W8A8 MXFP8 (MOE_MXFP8_B32_A8) applies to the shared expert only");
   if (s->I_shared && s->w_shared == MOE_MXFP8_B32_A8 && s->w_routed != MOE_MXFP4_B32_A8)
     return fail(MOE_ERR_UNSUPPORTED, "a W8A8 MXFP8 shared expert needs W4A8 routed experts (MOE_MXFP4_B32_A8)");
+  const bool ri8 = s->w_routed == MOE_INT8_W8A8, si8 = s->I_shared && s->w_shared == MOE_INT8_W8A8;
+  if ((ri8 && s->I_shared && !si8) || (si8 && !ri8))
+    return fail(MOE_ERR_UNSUPPORTED, "INT8 W8A8 experts: routed and shared both INT8 (or no shared expert)");
+  if (s->w_routed == MOE_INT8_W8A8 &&
+      (s->path == MOE_PATH_DECODE || !prefill_supported(s->act, s->w_routed, s->w_routed, s->H, s->I, s->H) ||
+       !prefill_supported(s->act, s->w_routed, s->w_routed, s->I, s->I, s->H)))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "INT8 W8A8 experts run on the prefill path only: BF16 activations, I a multiple of 256, "
+                "H a multiple of 512");
   if (s->w_routed == MOE_MXFP4_B32_A8 &&
       (s->path == MOE_PATH_DECODE ||
        !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
@@ -178,6 +191,12 @@ Ws ws_layout(const moe_shape& s) {
     w.xs = take((size_t)s.T * (s.H / 32));
     w.hq = take(QR * s.I);
     w.hs = take(QR * (s.I / 32));
+  } else if (s.w_routed == MOE_INT8_W8A8) {
+    // Int8 W8A8: int8 codes and fp32 per-row scales of x and of every row of h
+    w.xq = take((size_t)s.T * s.H);
+    w.xs = take((size_t)s.T * 4);
+    w.hq = take(R * s.I);
+    w.hs = take(R * 4);
   }
   w.total = o;
   return w;
@@ -200,7 +219,8 @@ T* at(void* ws, size_t off) {
 moe_status check_weights(const moe_weights* w, moe_dtype fmt, const char* what) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "%s weights are NULL", what);
   if (!w->gate || !w->up || !w->down) return fail(MOE_ERR_INVALID_ARG, "%s weight pointer is NULL", what);
-  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP4_B32 || fmt == MOE_MXFP4_B32_A8 || fmt == MOE_MXFP8_B32_A8) &&
+  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP4_B32 || fmt == MOE_MXFP4_B32_A8 || fmt == MOE_MXFP8_B32_A8 ||
+       fmt == MOE_INT8_W8A8) &&
       (!w->gate_scale || !w->up_scale || !w->down_scale))
     return fail(MOE_ERR_INVALID_ARG, "%s scales are NULL", what);
   return MOE_OK;
@@ -244,7 +264,7 @@ bool use_prefill(const moe_shape& s) {
   const int cs = s.I_shared ? s.w_shared : s.w_routed;
   if (!prefill_supported(s.act, s.w_routed, cs, s.H, s.I, s.H) || !prefill_supported(s.act, s.w_routed, cs, s.I, s.I, s.H))
     return false;
-  if (s.path == MOE_PATH_PREFILL || s.w_routed == MOE_MXFP4_B32_A8) return true;
+  if (s.path == MOE_PATH_PREFILL || s.w_routed == MOE_MXFP4_B32_A8 || s.w_routed == MOE_INT8_W8A8) return true;
   if (s.path == MOE_PATH_DECODE) return false;
   return (long long)s.T * s.k >= 64LL * s.E;
 }
@@ -368,10 +388,20 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
     }
     return launch_w8a8_shared(epi == EPI_SWIGLU ? EPI_SWIGLU_Q8 : epi, sa, s.T, st);
   };
+  const bool i8 = s.w_routed == MOE_INT8_W8A8;
   if (a8) {
     e = launch_quant_mxfp8(x, s.T, s.H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), st);
     if (e != hipSuccess) return hip_status(e, "MXFP8 quantisation of x");
     e = launch_a8(EPI_SWIGLU, a, at<void>(ws, L.xq), at<void>(ws, L.xs), s.H, s.T, slot_token);
+  } else if (i8) {
+    // Int8 W8A8: x to int8 per token, then one launch over the routed and shared groups, which
+    // writes h in bf16 (quantised per row before down)
+    e = launch_quant_int8(x, s.T, s.H, at<int8_t>(ws, L.xq), at<float>(ws, L.xs), st);
+    if (e != hipSuccess) return hip_status(e, "int8 quantisation of x");
+    GroupedArgs ia = a;
+    ia.act = at<void>(ws, L.xq);
+    ia.act_scale = at<void>(ws, L.xs);
+    e = launch_int8_prefill(EPI_SWIGLU, ia, max_rb, st);
   } else {
     e = prefill ? launch_grouped_prefill(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st)
                 : launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
@@ -403,6 +433,13 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.ldo_s = s.H;
   if (a8) {
     e = launch_a8(EPI_PLAIN, a, at<void>(ws, L.hq), at<void>(ws, L.hs), s.I, P, nullptr);
+  } else if (i8) {
+    e = launch_quant_int8(at<void>(ws, L.h), P + S * s.T, s.I, at<int8_t>(ws, L.hq), at<float>(ws, L.hs), st);
+    if (e != hipSuccess) return hip_status(e, "int8 quantisation of h");
+    GroupedArgs ia = a;
+    ia.act = at<void>(ws, L.hq);
+    ia.act_scale = at<void>(ws, L.hs);
+    e = launch_int8_prefill(EPI_PLAIN, ia, max_rb, st);
   } else {
     e = prefill ? launch_grouped_prefill(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st)
                 : launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);

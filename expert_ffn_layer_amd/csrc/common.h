@@ -13,6 +13,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int WAVE = 64;
 
@@ -37,7 +38,7 @@ constexpr int WAVE = 64;
 constexpr int PACKET_BYTES = 1024;
 
 __host__ __device__ constexpr int kp_of(int fmt) {
-  return fmt == MOE_F32 ? 16 : fmt == MOE_BF16 ? 32 : (fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP8_B32_A8) ? 64 : 128;
+  return fmt == MOE_F32 ? 16 : fmt == MOE_BF16 ? 32 : (fmt == MOE_FP8_E4M3_B128 || fmt == MOE_MXFP8_B32_A8 || fmt == MOE_INT8_W8A8) ? 64 : 128;
 }
 
 // bf16 bit helpers (raw uint16 storage)

@@ -212,6 +212,30 @@ struct PCodec<MOE_MXFP8_B32_A8> {
   __device__ static void frags(const u32x4 (&)[PK], float, bf16x8 (&)[H]) {}
 };
 
+// Int8 W8A8: int8 weight packets (16 features x 64 K, laid out as fp8 packets) times int8
+// activation rows on v_mfma_i32_16x16x64_i8, which adds the products of the codes exactly in int32.
+// Its A and B operands take the same lane layout (lane (f, g): 16 bytes of feature or token f), so
+// packet lane (f, g) and the activation chunk of the same run pair the same reduction elements,
+// whatever order the instruction adds them in. One step is 128 deep: two MFMAs per (row tile,
+// column tile), half h on the step's packet h and on chunk 4h + g of the token's 128-byte line (the
+// W4A8 activation layout). No scale enters the loop: the epilogue multiplies each sum by its row's
+// activation scale and its feature's weight scale. A half item takes 80 KiB per stage (64 KiB of
+// packets), so two stages.
+template <>
+struct PCodec<MOE_INT8_W8A8> {
+  static constexpr int KP = 64;
+  static constexpr int PBK = 128;
+  static constexpr int H = 2;
+  static constexpr int PK = 2;
+  static constexpr bool HALF_ONLY = false, FULL_ONLY = false;
+  static constexpr bool SCALE_DMA = false;
+  static constexpr int ACT_BYTES = 1, NSC = 0, SC_KIB = 0;
+  __device__ static int dma_row(int l, int u) { return PCodec<MOE_MXFP4_B32_A8>::dma_row(l, u); }
+  __device__ static int dma_off(int l, int u) { return PCodec<MOE_MXFP4_B32_A8>::dma_off(l, u); }
+  __device__ static int read_off(int l, int h) { return PCodec<MOE_MXFP4_B32_A8>::read_off(l, h); }
+  __device__ static void frags(const u32x4 (&)[PK], float, bf16x8 (&)[H]) {}
+};
+
 template <int EPI>
 struct PEpi {
   static constexpr int NMAT = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) ? 2 : 1;
@@ -234,7 +258,7 @@ struct PLayout {
                                                                                            : HALF_ACT + HALF_W;
   static constexpr int SC_OFF = ITEM_KIB * 1024;
   static constexpr int STAGE_KIB = ITEM_KIB + SC_KIB;
-  static constexpr int STAGES = (Cd::HALF_ONLY || Cd::FULL_ONLY) ? 2 : 3;
+  static constexpr int STAGES = (Cd::HALF_ONLY || Cd::FULL_ONLY || 3 * STAGE_KIB > 160) ? 2 : 3;
   // DMA instructions per wave per stage; the shorter kind is padded with repeats of its last
   // load so both kinds issue the same count (the wait counts are compile-time)
   static constexpr int LF = Cd::HALF_ONLY ? 0 : 2 * H + 2 * PK, LH = H + 4 * PK;
@@ -394,6 +418,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
   constexpr int LSC = Cd::SCALE_DMA ? 1 : 0;  // the last load moves the packet scales
   constexpr bool A8 = C == MOE_MXFP4_B32_A8 || C == MOE_MXFP8_B32_A8;  // the last two loads move the exponents
   constexpr int AFMT = C == MOE_MXFP8_B32_A8 ? 0 : 4;  // A operand format of the block-scaled MFMA: fp8, fp4
+  constexpr bool I8 = C == MOE_INT8_W8A8;  // int8 x int8, int32 sums
 #pragma unroll
   for (int q = 0; q < L; ++q) {
     const int nact = half ? H : 2 * H;
@@ -501,10 +526,43 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
         mcur[m] = mn;
       }
     }
-    if constexpr (A8 && MTA == 0) {
+    if constexpr ((A8 || I8) && MTA == 0) {
       // no rows in this wave's half of the item: only its share of the next stage's loads
 #pragma unroll
       for (int q = 0; q < L; ++q) dma_one(q, step + D - 1);
+      return;
+    } else if constexpr (I8) {
+      // two int8 MFMAs per (row tile, column tile): packet h of the tile's step and the lane's
+      // activation chunk of half h; the int32 sums live in the accumulator registers' bits
+      u32x4 aw[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) aw[t][h] = *(const u32x4*)(base + wbase + (t * PK + h) * 1024);
+      u32x4 b0n = *(const u32x4*)(base + aoff[0]), b1n = *(const u32x4*)(base + aoff[1]);
+      constexpr int QA = (L + MTA - 1) / (MTA > 0 ? MTA : 1);
+#pragma unroll
+      for (int j = 0; j < MTA; ++j) {
+        const u32x4 b0 = b0n, b1 = b1n;
+        if (j + 1 < MTA) {
+          b0n = *(const u32x4*)(base + aoff[0] + (j + 1) * H * 1024);
+          b1n = *(const u32x4*)(base + aoff[1] + (j + 1) * H * 1024);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t][j] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, aw[t][0]), __builtin_bit_cast(i32x4, b0),
+                                                           __builtin_bit_cast(i32x4, acc[t][j]), 0, 0, 0));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t][j] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, aw[t][1]), __builtin_bit_cast(i32x4, b1),
+                                                           __builtin_bit_cast(i32x4, acc[t][j]), 0, 0, 0));
+#pragma unroll
+        for (int u = 0; u < QA; ++u)
+          if (j * QA + u < L) dma_one(j * QA + u, step + D - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       return;
     } else if constexpr (A8) {
       // one block-scaled MFMA per (row tile, column tile): the weights as stored with their e8m0
@@ -597,7 +655,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
       for (int u = 1; u < SPB; ++u) step_body(step + u, std::false_type{}, row_tiles);
     }
   };
-  if constexpr (A8) {
+  if constexpr (A8 || I8) {
     // W4A8 leaves the row tiles past the group's end out of the MFMA stream, 32 rows at a time:
     // each wave runs the loop compiled for 2, 4, 6 or 8 row tiles, chosen once per item, so the
     // stream has no branches. Their accumulators stay zero and are never stored. (Padding MFMAs
@@ -612,6 +670,36 @@ __global__ void __launch_bounds__(PTHREADS, 1) grouped_prefill_kernel(GroupedArg
     run_steps(std::integral_constant<int, 8>{});
   }
   MOE_WAIT_VMCNT(0);  // the clamped tail DMAs must land before the workgroup's LDS is released
+
+  if constexpr (I8) {
+    // int32 sums -> fp32, times the row's activation scale (its token's for gathered rows) and the
+    // feature's weight scale; rows past the group's end are never stored
+    const float* asc = (const float*)a.act_scale;
+    float rsc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rr = wrow * 128 + j * 16 + j16;
+      rsc[j] = 0.f;
+      if (rr < nr) {
+        const int r = row0 + rr;
+        const int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
+        if ((unsigned)src < (unsigned)a.act_rows) rsc[j] = asc[src];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 cs = *(const f32x4*)((t / WF == 0 ? s0 : s1) + ftile[t] * 16 + 4 * g4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // reinterpret the whole register vector (a bit cast of one vector element read element 0)
+        const i32x4 iv = __builtin_bit_cast(i32x4, acc[t][j]);
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (float)iv[i] * rsc[j] * cs[i];
+        acc[t][j] = v;
+      }
+    }
+  }
 
   // epilogue: lane holds features 4*(lane/16) + i of each 16-feature tile, row j*16 + lane%16
   uint8_t* out;
@@ -769,6 +857,7 @@ static bool prefill_codec_ok(int c, int K) {
   else if (c == MOE_MXFP4_B32) pbk = PCodec<MOE_MXFP4_B32>::PBK;
   else if (c == MOE_MXFP4_B32_A8) pbk = PCodec<MOE_MXFP4_B32_A8>::PBK;
   else if (c == MOE_MXFP8_B32_A8) pbk = PCodec<MOE_MXFP8_B32_A8>::PBK;
+  else if (c == MOE_INT8_W8A8) pbk = PCodec<MOE_INT8_W8A8>::PBK;
   else return false;
   return K % pbk == 0 && K % 128 == 0 && K <= 64 * 128;
 }
@@ -788,6 +877,19 @@ hipError_t launch_w4a8_prefill(int epi, const GroupedArgs& a, int max_units, hip
   if (epi == EPI_PLAIN) {
     if (a.N % (2 * PEpi<EPI_PLAIN>::FULL_F)) return hipErrorInvalidValue;
     return launch_p<MOE_MXFP4_B32_A8, EPI_PLAIN>(a, max_units, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_int8_prefill(int epi, const GroupedArgs& a, int max_units, hipStream_t st) {
+  if (!prefill_codec_ok(MOE_INT8_W8A8, a.K) || !a.act_scale) return hipErrorInvalidValue;
+  if (epi == EPI_SWIGLU) {
+    if (a.N % (2 * PEpi<EPI_SWIGLU>::FULL_F)) return hipErrorInvalidValue;
+    return launch_p<MOE_INT8_W8A8, EPI_SWIGLU>(a, max_units, st);
+  }
+  if (epi == EPI_PLAIN) {
+    if (a.N % (2 * PEpi<EPI_PLAIN>::FULL_F)) return hipErrorInvalidValue;
+    return launch_p<MOE_INT8_W8A8, EPI_PLAIN>(a, max_units, st);
   }
   return hipErrorInvalidValue;
 }

@@ -46,7 +46,8 @@ struct GroupedArgs {
   int ksplit;  // > 1: fp32 output only; workgroup y sums K part y into out + y * M * ldo
   const void* zero_row;  // prefill: K zero activations that rows past a group's end read, or null
   int g_begin, g_end;    // prefill: groups of this launch (g_end <= g_begin: all groups)
-  const void* act_scale; // W4A8: e8m0 exponents of the MXFP8 activations, [row][K/32], gathered as act
+  const void* act_scale; // W4A8: e8m0 exponents of the MXFP8 activations, [row][K/32], gathered as act;
+                         // Int8 W8A8: fp32 scale per activation row
   void* out_scale;       // EPI_SWIGLU_Q8: e8m0 exponents of the output, [row][N/64] (N = 2 I)
 };
 
@@ -73,6 +74,11 @@ hipError_t launch_w4a8_prefill(int epi, const GroupedArgs& a, int max_units, hip
 // W8A8 MXFP8 shared expert (one group, [g_begin, g_end) = [shared_group, shared_group + 1), of
 // `rows` rows): gate/up with the MXFP8-writing SwiGLU epilogue, or down.
 hipError_t launch_w8a8_shared(int epi, const GroupedArgs& a, int rows, hipStream_t st);
+// Int8 W8A8 over all groups: act holds int8 rows, act_scale their fp32 scales (gathered like the
+// rows); gate/up (EPI_SWIGLU, h in bf16) or down (EPI_PLAIN).
+hipError_t launch_int8_prefill(int epi, const GroupedArgs& a, int max_units, hipStream_t st);
+// bf16 rows -> int8 codes and one fp32 scale per row (Int8 W8A8 activations)
+hipError_t launch_quant_int8(const void* src, int rows, int K, int8_t* codes, float* scales, hipStream_t st);
 int prefill_row_tile();
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down);
 bool prefill_scores_supported(int act, int K, int N);

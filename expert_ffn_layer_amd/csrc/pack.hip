@@ -39,12 +39,16 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ s
       uint32_t hi = in ? w[(size_t)(k0 + 2 * i + 1) * N + n] : 0u;
       o[i] = lo | (hi << 16);
     }
-  } else if (FMT == MOE_FP8_E4M3_B128 || FMT == MOE_MXFP8_B32_A8) {
+  } else if (FMT == MOE_FP8_E4M3_B128 || FMT == MOE_MXFP8_B32_A8 || FMT == MOE_INT8_W8A8) {
     const uint8_t* w = src + (size_t)m * K * N;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       uint32_t b = in ? w[(size_t)(k0 + i) * N + n] : 0u;
       o[i >> 2] |= b << (8 * (i & 3));
+    }
+    if (FMT == MOE_INT8_W8A8 && kt == 0 && l < 16) {
+      // the per-feature scales, one float per (padded) feature: zero past N
+      ((float*)dst_scale)[(size_t)m * NT * 16 + n] = in ? ((const float*)src_scale)[(size_t)m * N + n] : 0.0f;
     }
     if (FMT == MOE_MXFP8_B32_A8 && (kt & 1) == 0) {
       // one exponent byte per lane per pair of packets (128 reduction elements): lane l takes
@@ -96,6 +100,9 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t moe_launch_pack(int 
     case MOE_MXFP4_B32: pack_kernel<MOE_MXFP4_B32><<<grid, block, 0, stream>>>(s, ss, d, ds, count, K, N, NT, total); break;
     case MOE_MXFP8_B32_A8:
       pack_kernel<MOE_MXFP8_B32_A8><<<grid, block, 0, stream>>>(s, ss, d, ds, count, K, N, NT, total);
+      break;
+    case MOE_INT8_W8A8:
+      pack_kernel<MOE_INT8_W8A8><<<grid, block, 0, stream>>>(s, ss, d, ds, count, K, N, NT, total);
       break;
     default: return hipErrorInvalidValue;
   }

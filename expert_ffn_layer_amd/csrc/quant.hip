@@ -1,4 +1,5 @@
-// Activation quantisation for W4A8 routed experts: bf16 token rows -> OCP MXFP8.
+// Activation quantisation: bf16 rows -> OCP MXFP8 for W4A8 and W8A8 MXFP8 experts, and -> int8 per
+// row for Int8 W8A8 experts.
 //
 // 'CANN DeepSeek-V4推理优化' (quantisation strategy) runs the routed experts' linear layers as
 // W4A8: 4-bit weights times 8-bit activations. On gfx950 the 8-bit side is OCP MXFP8, the format
@@ -53,7 +54,50 @@ __global__ void __launch_bounds__(QTHREADS) quant_mxfp8_kernel(const uint16_t* _
   }
 }
 
+// Int8 W8A8: row `row` of src (bf16, K a multiple of 8) -> int8 codes and one fp32 scale per row.
+// One wave per row: the row's largest magnitude by a wave-wide xor reduction, then f = 127 / max and
+// s = max / 127 (IEEE fp32 divisions) and code = rint(v * f) (fp32 product, ties to even), clamped
+// to +-127; the row is read a second time for the codes (it is in cache). An all-zero row gets
+// s = 0 and zero codes.
+__global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __restrict__ src, int rows, int K,
+                                                              int8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (QTHREADS / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* in = src + (size_t)row * K;
+  float amax = 0.f;
+  for (int c = 8 * lane; c < K; c += 512) {
+    const u32x4 v = *(const u32x4*)(in + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16lo(v[i])), __builtin_fabsf(bf16hi(v[i]))));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+  const float f = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
+  for (int c = 8 * lane; c < K; c += 512) {
+    const u32x4 v = *(const u32x4*)(in + c);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = (i & 1) ? bf16hi(v[i >> 1]) : bf16lo(v[i >> 1]);
+      const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fmul_rn(x, f)), -127.f), 127.f);
+      w[i >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (i & 3));
+    }
+    *(u32x2*)(codes + (size_t)row * K + c) = u32x2{w[0], w[1]};
+  }
+  if (lane == 0) scales[row] = __fdiv_rn(amax, 127.0f);
+}
+
 }  // namespace
+
+hipError_t launch_quant_int8(const void* src, int rows, int K, int8_t* codes, float* scales, hipStream_t st) {
+  if (K % 8) return hipErrorInvalidValue;
+  const int blocks = (rows + QTHREADS / 64 - 1) / (QTHREADS / 64);
+  if (blocks == 0) return hipSuccess;
+  quant_int8_kernel<<<blocks, QTHREADS, 0, st>>>((const uint16_t*)src, rows, K, codes, scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_mxfp8(const void* src, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   if (K % 32) return hipErrorInvalidValue;

@@ -13,7 +13,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-DTYPE = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "mxfp4a8": 4, "mxfp8a8": 5}
+DTYPE = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "mxfp4a8": 4, "mxfp8a8": 5, "int8": 6}
 PATH = {"auto": 0, "decode": 1, "prefill": 2}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}

@@ -17,7 +17,7 @@ FLOPs it must do, independent of how a kernel moves them.
 from __future__ import annotations
 
 # bytes per parameter of each stored format, and bytes of block scales per parameter
-PARAM_BYTES = {"f32": 4.0, "bf16": 2.0, "fp8": 1.0, "mxfp4": 0.5, "mxfp4a8": 0.5, "mxfp8a8": 1.0}
+PARAM_BYTES = {"f32": 4.0, "bf16": 2.0, "fp8": 1.0, "mxfp4": 0.5, "mxfp4a8": 0.5, "mxfp8a8": 1.0, "int8": 1.0}
 ACT_BYTES = {"f32": 4, "bf16": 2}
 
 
@@ -37,6 +37,8 @@ def matrix_bytes(K: int, N: int, fmt: str) -> int:
         return K * N // 2 + (K // 32) * N
     if fmt == "mxfp8a8":  # E4M3FN codes + one e8m0 byte per 32 K-elements of a column
         return K * N + (K // 32) * N
+    if fmt == "int8":  # int8 codes + one fp32 scale per output column
+        return K * N + 4 * N
     raise ValueError(fmt)
 
 

@@ -63,13 +63,23 @@ typedef enum {
                              one e8m0 exponent floor(log2 max|v|) - 8 per 32 reduction elements)
                              and multiplied by the block-scaled fp4 x fp8 matrix instruction.
                              Only as w_routed, with BF16 activations, on the prefill path. */
-  MOE_MXFP8_B32_A8 = 5    /* W8A8 MXFP8 shared expert of the hybrid MXFP8-MXFP4 scheme (same
+  MOE_MXFP8_B32_A8 = 5,   /* W8A8 MXFP8 shared expert of the hybrid MXFP8-MXFP4 scheme (same
                              passage: the shared expert's linear layers run W8A8, weights and
                              activations both MXFP8). Weights: OCP E4M3FN codes + one e8m0
                              exponent per 32 reduction elements, w = e4m3(c) * 2^(E-127). The
                              activations are quantised to MXFP8 as for MOE_MXFP4_B32_A8 and both
                              operands go to the block-scaled fp8 x fp8 matrix instruction. Only
                              as w_shared, with w_routed = MOE_MXFP4_B32_A8. */
+  MOE_INT8_W8A8 = 6       /* Int8 W8A8 experts (same page, Int8 quantisation strategy: the routed
+                             and shared experts' linear layers run W8A8, weights statically
+                             quantised per output channel, activations dynamically per token).
+                             Weights: int8 codes + one fp32 scale per output feature, w = c * s[n].
+                             Each row of x and of h (after its bf16 rounding) is quantised in fp32:
+                             f = 127 / max|v|, s = max|v| / 127, code = rint(v * f) (ties to even,
+                             clamped to +-127); an all-zero row has s = 0. The products accumulate
+                             the codes exactly in int32 on the int8 matrix instruction, then scale
+                             by s_row * s[n]. As w_routed, with no shared expert or an INT8 one;
+                             BF16 activations; on the prefill path. */
 } moe_dtype;
 
 typedef enum {
@@ -77,10 +87,9 @@ typedef enum {
                              shape, else decode */
   MOE_PATH_DECODE = 1,    /* weight-streaming grouped GEMM (few rows per expert) */
   MOE_PATH_PREFILL = 2    /* LDS-tiled MFMA grouped GEMM (many rows per expert): BF16
-                             activations, BF16 / FP8 / MXFP4 / W4A8 / W8A8 MXFP8 weights, I a
-                             multiple of 256,
-                             H a multiple of 512; MOE_ERR_UNSUPPORTED otherwise. W4A8 routed
-                             experts always take this path (AUTO included). */
+                             activations, BF16 / FP8 / MXFP4 / W4A8 / W8A8 MXFP8 / INT8 weights, I
+                             a multiple of 256, H a multiple of 512; MOE_ERR_UNSUPPORTED otherwise.
+                             W4A8 and INT8 routed experts always take this path (AUTO included). */
 } moe_path;
 
 typedef struct {
@@ -124,16 +133,18 @@ const char* moe_last_error(void);
  *   MOE_MXFP4_B32      uint8[K][N/2] codes, even n in the low nibble + uint8[K/32][N] e8m0
  *                      exponents (w = e2m1(c) * 2^(E-127)); MOE_MXFP4_B32_A8 the same
  *   MOE_MXFP8_B32_A8   uint8[K][N] codes + uint8[K/32][N] e8m0 exponents (w = e4m3(c) * 2^(E-127))
+ *   MOE_INT8_W8A8      int8[K][N] codes + float[N] scales (w = c * s[n])
  * Packed layout: 1 KiB packets of 16 features x KP reduction elements (KP = 16, 32, 64, 128 for
- * F32, BF16, FP8 and MXFP8, MXFP4), packet (nt, kt) at byte (nt*(K/KP) + kt)*1024, lane l of a
+ * F32, BF16, FP8 / MXFP8 / INT8, MXFP4), packet (nt, kt) at byte (nt*(K/KP) + kt)*1024, lane l of a
  * packet holding feature nt*16 + l%16 and reduction run kt*KP + (l/16)*KP/4 + [0, KP/4). FP8
  * scales are copied unchanged; MXFP4 scales are regrouped one byte per lane per packet, and
  * MXFP8 scales one byte per lane per pair of packets (128 reduction elements): byte
  * (nt*(K/128) + kt2)*64 + l is the exponent of feature nt*16 + l%16, reduction elements
- * kt2*128 + (l/16)*32 + [0, 32).
+ * kt2*128 + (l/16)*32 + [0, 32). INT8 scales are copied per matrix into pad256(N) floats, zero
+ * past N.
  * N is padded up to a multiple of 256 with zero features (only the router, N = E, needs it).
- * Requirements: K a multiple of KP (and of 128 for FP8 and MXFP8), N a multiple of 16 (128 for
- * FP8, 2 for MXFP4) before padding. `packed_scale` may be NULL for F32 / BF16.
+ * Requirements: K a multiple of KP (and of 128 for FP8, MXFP8 and INT8), N a multiple of 16 (128
+ * for FP8, 2 for MXFP4) before padding. `packed_scale` may be NULL for F32 / BF16.
  * Router: pack Wr[H][E] as one K = H, N = E matrix in the `act` format.
  */
 moe_status moe_pack_size(moe_dtype fmt, int32_t count, int32_t K, int32_t N,

@@ -301,9 +301,10 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const v4u* __restrict_
 // operands rotating over 5 random register sets so consecutive instructions see different data
 // (constant operands draw less power and overstate the rate). KIND 0: v_mfma_f32_16x16x32_bf16;
 // KIND 1: v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 (e2m1) x fp8 (e4m3) operands; KIND 2: the same
-// instruction with fp8 x fp8.
+// instruction with fp8 x fp8; KIND 3: v_mfma_i32_16x16x64_i8.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 __device__ __forceinline__ uint32_t burst_hash(uint32_t x) {
   x ^= x >> 16;
@@ -337,6 +338,24 @@ __global__ void __launch_bounds__(512, 1) mfma_burst_kernel(int iters, unsigned*
       for (int j = 0; j < 16; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j % NS], b[(j * 3 + 1) % NS], acc[j], 0, 0, 0);
     }
+  } else if constexpr (KIND == 3) {
+    i32x4_t a[NS], b[NS], iacc[16];
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[q][i] = (int)burst_hash(t * 97 + q * 8 + i);
+        b[q][i] = (int)burst_hash(~(t * 89 + q * 8 + i));
+      }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) iacc[j] = i32x4_t{0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        iacc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j % NS], b[(j * 3 + 1) % NS], iacc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = f32x4_t{(float)iacc[j][0], (float)iacc[j][1], (float)iacc[j][2], (float)iacc[j][3]};
   } else {
     constexpr int AF = KIND == 2 ? 0 : 4;  // A operand format: fp8 or fp4
     i32x8_t a[NS], b[NS];
@@ -374,13 +393,14 @@ int gen_stream_read(const void* src, long long bytes, void* sink, hipStream_t st
 }
 
 // MFMA burst over `blocks` workgroups of 512 threads, `iters` x 16 MFMAs per wave; kind 0 bf16
-// 16x16x32 (16384 FLOP each), kind 1 fp4 x fp8 and kind 2 fp8 x fp8 16x16x128 (65536 FLOP each).
-// sink: one uint32.
+// 16x16x32 (16384 FLOP each), kind 1 fp4 x fp8 and kind 2 fp8 x fp8 16x16x128 (65536 FLOP each),
+// kind 3 int8 16x16x64 (32768 OP each). sink: one uint32.
 int gen_mfma_burst(int kind, int iters, int blocks, void* sink, hipStream_t st) {
-  if (iters < 1 || blocks < 1 || kind < 0 || kind > 2) return -1;
+  if (iters < 1 || blocks < 1 || kind < 0 || kind > 3) return -1;
   if (kind == 0) mfma_burst_kernel<0><<<blocks, 512, 0, st>>>(iters, (unsigned*)sink);
   else if (kind == 1) mfma_burst_kernel<1><<<blocks, 512, 0, st>>>(iters, (unsigned*)sink);
-  else mfma_burst_kernel<2><<<blocks, 512, 0, st>>>(iters, (unsigned*)sink);
+  else if (kind == 2) mfma_burst_kernel<2><<<blocks, 512, 0, st>>>(iters, (unsigned*)sink);
+  else mfma_burst_kernel<3><<<blocks, 512, 0, st>>>(iters, (unsigned*)sink);
   return (int)hipGetLastError();
 }
 

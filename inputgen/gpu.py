@@ -77,10 +77,10 @@ def copy(src, dst):
 
 
 def mfma_burst(kind: int, iters: int, blocks: int, sink) -> float:
-    """One MFMA burst (kind 0: bf16 16x16x32, kind 1: fp4 x fp8, kind 2: fp8 x fp8 16x16x128);
-    returns its FLOPs."""
+    """One MFMA burst (kind 0: bf16 16x16x32, kind 1: fp4 x fp8, kind 2: fp8 x fp8 16x16x128, kind 3:
+    int8 16x16x64); returns its FLOPs (OPs)."""
     _chk(lib().gen_mfma_burst(kind, iters, blocks, ctypes.c_void_p(sink.data_ptr()), _stream()), "mfma_burst")
-    return float(blocks) * 8 * iters * 16 * (16384 if kind == 0 else 65536)
+    return float(blocks) * 8 * iters * 16 * {0: 16384, 1: 65536, 2: 65536, 3: 32768}[kind]
 
 
 def stream_read(src, sink):

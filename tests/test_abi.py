@@ -57,6 +57,11 @@ def _shape(**kw):
     (dict(H=512, I=256, I_shared=256, w_routed="mxfp4", w_shared="mxfp8a8"), 2),
     (dict(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="mxfp8a8", path="decode"), 2),
     (dict(act="f32", w_routed="f32", I_shared=128, w_shared="mxfp8a8"), 2),
+    # Int8 W8A8: routed and shared both INT8 (or no shared expert), prefill only
+    (dict(H=512, I=256, I_shared=256, w_routed="int8", w_shared="bf16"), 2),
+    (dict(H=512, I=256, I_shared=256, w_routed="bf16", w_shared="int8"), 2),
+    (dict(H=512, I=256, w_routed="int8", path="decode"), 2),
+    (dict(H=256, I=256, w_routed="int8"), 2),
 ])
 def test_shape_validation(kw, status):
     with pytest.raises(N.MoeError) as e:
@@ -79,6 +84,12 @@ def test_hybrid_shape_is_accepted_and_quantises_the_shared_rows_of_h():
     assert mx - bf >= 4 * 256
 
 
+def test_int8_shape_is_accepted_with_and_without_a_shared_expert():
+    assert N.moe_workspace_size(_shape(H=512, I=256, w_routed="int8")) > 0
+    assert N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="int8", w_shared="int8")) > \
+        N.moe_workspace_size(_shape(H=512, I=256, w_routed="int8"))
+
+
 def test_workspace_grows_with_tokens_and_shared_expert():
     a = N.moe_workspace_size(_shape(T=4))
     b = N.moe_workspace_size(_shape(T=64))
@@ -98,11 +109,13 @@ def test_pack_sizes():
     # packets: 32 feature tiles x 2 pairs x 64
     assert N.moe_pack_size("mxfp8a8", 1, 256, 384) == (32 * 4 * 1024, 32 * 2 * 64)
     assert N.moe_pack_size("mxfp8a8", 2, 7168, 3072) == (2 * 7168 * 3072, 2 * 7168 * 3072 // 32)
+    # INT8: fp8-sized packets, one fp32 scale per padded feature
+    assert N.moe_pack_size("int8", 3, 256, 384) == (3 * 32 * 4 * 1024, 3 * 512 * 4)
     # the router's E is padded to 256 features (the width of one MFMA item)
     assert N.moe_pack_size("bf16", 1, 256, 8) == (256 * 256 * 2, 0)
     assert N.moe_pack_size("bf16", 1, 7168, 384) == (7168 * 512 * 2, 0)
     for fmt, K, Nn in (("fp8", 7168, 100), ("fp8", 100, 128), ("bf16", 48, 64), ("mxfp4", 128, 3),
-                       ("mxfp8a8", 64, 256)):
+                       ("mxfp8a8", 64, 256), ("int8", 64, 256)):
         with pytest.raises(N.MoeError):
             N.moe_pack_size(fmt, 1, K, Nn)
 

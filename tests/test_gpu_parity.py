@@ -28,7 +28,7 @@ def _lib():
 
 # ------------------------------------------------------------------ the input generator
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8", "int8"])
 def test_gpu_generator_is_bit_identical_to_numpy(fmt):
     K, Nn = 256, 384
     c, s = G.alloc_matrices(fmt, 2, K, Nn, DEV)
@@ -48,7 +48,7 @@ def test_gpu_activations_bit_identical():
 
 # ------------------------------------------------------------------ packing
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "mxfp4", "mxfp8a8", "int8"])
 def test_pack_layout(fmt):
     """Unpack the packed bytes with numpy following the documented layout."""
     K, Nn = 256, 384
@@ -56,7 +56,7 @@ def test_pack_layout(fmt):
     G.fill_matrices(c, s, fmt, 3, 16, 0, K, Nn, K)
     packed, pscale = pack(fmt, c, s, K, Nn)
     torch.cuda.synchronize()
-    KP = {"f32": 16, "bf16": 32, "fp8": 64, "mxfp4": 128, "mxfp8a8": 64}[fmt]
+    KP = {"f32": 16, "bf16": 32, "fp8": 64, "mxfp4": 128, "mxfp8a8": 64, "int8": 64}[fmt]
     NT, KT = Nn // 16, K // KP
     NTp = (Nn + 255) // 256 * 16  # features padded to a multiple of 256 with zero packets
     raw = packed.cpu().numpy().reshape(NTp, KT, 64, 16)
@@ -69,6 +69,8 @@ def test_pack_layout(fmt):
         lanes = np.stack([raw & 15, raw >> 4], axis=-1).reshape(NT, KT, 64, 32)
     elif fmt in ("fp8", "mxfp8a8"):
         codes, lanes = stored, raw
+    elif fmt == "int8":
+        codes, lanes = stored, raw.view(np.int8)
     else:
         dt = np.float32 if fmt == "f32" else np.uint16
         codes, lanes = stored, raw.view(dt).reshape(NT, KT, 64, -1)
@@ -88,6 +90,10 @@ def test_pack_layout(fmt):
         for l in range(64):
             for kt in range(KT):
                 assert np.array_equal(ps[:, kt, l], sc[(kt * KP + (l // 16) * 32) // 32, np.arange(NT) * 16 + l % 16])
+    if fmt == "int8":
+        ps = pscale.cpu().numpy().view(np.float32)
+        assert ps.size == NTp * 16
+        assert np.array_equal(ps[:Nn], s[0].cpu().numpy()) and not ps[Nn:].any()
     if fmt == "mxfp8a8":
         # one exponent byte per lane per pair of packets: lane l of pair kt2 holds the exponent of
         # feature l % 16 of the tile, elements kt2 * 128 + (l // 16) * 32 .. + 32
@@ -147,13 +153,20 @@ SMALL = [
                                    w_shared="mxfp8a8", seed=47)),
     ("hybrid-mx-one-token", L.LayerSpec("s18", T=1, H=512, E=4, k=2, I=256, shared=True, w_routed="mxfp4a8",
                                         w_shared="mxfp8a8", seed=48)),
+    # Int8 W8A8 experts (int8 x int8 MFMA, exact int32 sums): ragged Zipf groups with an int8 shared
+    # expert, many small groups without one, a single token
+    ("int8-shared", L.LayerSpec("s19", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="int8",
+                                w_shared="int8", router="zipf", zipf_alpha=1.0, calib_tokens=512, seed=49)),
+    ("int8-small-groups", L.LayerSpec("s20", T=96, H=1024, E=24, k=4, I=512, w_routed="int8", seed=50)),
+    ("int8-one-token", L.LayerSpec("s21", T=1, H=512, E=4, k=2, I=256, shared=True, w_routed="int8",
+                                   w_shared="int8", seed=51)),
 ]
 
 
 def _prefill_ok(spec):
     fmts = ("bf16", "fp8", "mxfp4")
-    shared_fmts = fmts + (("mxfp8a8",) if spec.w_routed == "mxfp4a8" else ())
-    return (spec.act == "bf16" and spec.w_routed in fmts + ("mxfp4a8",)
+    shared_fmts = fmts + (("mxfp8a8",) if spec.w_routed == "mxfp4a8" else ("int8",) if spec.w_routed == "int8" else ())
+    return (spec.act == "bf16" and spec.w_routed in fmts + ("mxfp4a8", "int8")
             and (not spec.shared or spec.w_shared in shared_fmts) and spec.I % 256 == 0 and spec.H % 512 == 0)
 
 
@@ -162,8 +175,8 @@ def _prefill_ok(spec):
 def test_layer_small(name, spec, path):
     if path == "prefill" and not _prefill_ok(spec):
         pytest.skip("the prefill kernel takes bf16 activations, I % 256 == 0 and H % 512 == 0")
-    if path == "decode" and spec.w_routed == "mxfp4a8":
-        pytest.skip("W4A8 routed experts run on the prefill path only (the decode path is refused)")
+    if path == "decode" and spec.w_routed in ("mxfp4a8", "int8"):
+        pytest.skip("W4A8 and Int8 W8A8 experts run on the prefill path only (the decode path is refused)")
     say("layer", name, path, spec)
     lay, pl = build(spec, DEV, path)
     y, idx, w = run(spec, lay, pl)
@@ -213,6 +226,8 @@ STAGE_SPECS = [
                               w_shared="bf16", seed=50)),
     ("w4a8+w8a8", L.LayerSpec("st51", T=40, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
                               w_shared="mxfp8a8", seed=51)),
+    ("int8", L.LayerSpec("st52", T=40, H=512, E=8, k=2, I=256, shared=True, w_routed="int8",
+                         w_shared="int8", seed=52)),
 ]
 
 
@@ -275,8 +290,8 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
 # the DeepSeek-V4-Pro-shaped layer at a prefill batch: MXFP4 routed experts in the prefill
 # kernel, the bf16 shared expert in a launch of its own; the same layer with W4A8 routed experts
 # (MXFP8 activations on the block-scaled MFMA); and the hybrid MXFP8-MXFP4 layer (W4A8 routed, W8A8
-# MXFP8 shared)
-FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx"]
+# MXFP8 shared); the DeepSeek-V3-shaped prefill layer with Int8 W8A8 experts
+FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8"]
 
 
 @pytest.mark.slow
@@ -379,6 +394,8 @@ GRAPH_SPECS = [
                          w_shared="bf16", seed=63)),
     ("hybrid-mx", L.LayerSpec("g4", T=300, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
                               w_shared="mxfp8a8", seed=64)),
+    ("int8", L.LayerSpec("g5", T=300, H=512, E=8, k=2, I=256, shared=True, w_routed="int8",
+                         w_shared="int8", seed=65)),
 ]
 
 
