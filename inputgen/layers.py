@@ -47,6 +47,8 @@ TID_X = 1
 TID_WR = 2
 TID_XCAL = 3
 TID_RANK = 4
+TID_TOKENS = 5
+TID_HASH = 6
 TID_ROUTED = {"gate": 16, "up": 17, "down": 18}
 TID_SHARED = {"gate": 24, "up": 25, "down": 26}
 
@@ -278,3 +280,29 @@ def router_inputs(spec: LayerSpec) -> dict:
     bias = zipf_bias(spec, Wr) if spec.router == "zipf" else None
     x, attempts = activations(spec, Wr, bias)
     return {"x": x, "Wr": Wr, "bias": bias, "attempts": attempts}
+
+
+# ----------------------------------------------------------------------------------------------
+# hash routing inputs
+# ----------------------------------------------------------------------------------------------
+
+def hash_inputs(spec: LayerSpec, vocab: int):
+    """Token ids uniform in [0, vocab) and a [vocab][k] int32 table of k distinct experts per id.
+
+    Token t's id is word t of stream 0 of (seed, TID_TOKENS) mod vocab; row v of the table takes
+    words of stream v of (seed, TID_HASH) mod E in order, skipping experts already in the row.
+    """
+    ids = (px.uniform_words(spec.seed, TID_TOKENS, 0, 0, spec.T).astype(np.int64) % vocab).astype(np.int32)
+    table = np.empty((vocab, spec.k), np.int32)
+    for v in range(vocab):
+        words = px.uniform_words(spec.seed, TID_HASH, v, 0, 8 * spec.k + 64).astype(np.int64) % spec.E
+        row = []
+        for e in words:
+            if e not in row:
+                row.append(int(e))
+                if len(row) == spec.k:
+                    break
+        assert len(row) == spec.k, "hash table row %d: too few distinct draws" % v
+        table[v] = row
+    return ids, table
+

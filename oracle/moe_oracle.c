@@ -204,6 +204,53 @@ int oracle_route(int T, int H, int E, int k, int act, const void* x, const void*
 }
 
 /* ---------------------------------------------------------------------------------------- */
+/* hash routing                                                                              */
+/*                                                                                          */
+/* [CANN] "CANN DeepSeek-V4推理优化", MoE section: the first layers choose experts by hash      */
+/* routing, the later ones by the learned router. Read plainly: the k experts of a token are */
+/* a fixed function of its token id (row id of a [vocab][k] table), independent of x; the   */
+/* weights stay those of the router (step 3) renormalised over that set. Output order: the   */
+/* valid entries (in [0, E)) ascending by expert index, equal indices in table order, then   */
+/* the invalid ones (or all k for an id outside [0, vocab)) as index -1 with weight 0.        */
+/* ---------------------------------------------------------------------------------------- */
+
+int oracle_route_hash(int T, int H, int E, int k, int act, const void* x, const void* Wr,
+                      const float* bias, const int32_t* token_ids, const int32_t* table, int vocab,
+                      int32_t* topk_idx, double* topk_w) {
+  if (T < 0 || H < 1 || E < 1 || k < 1 || k > 16 || vocab < 0) return 1;
+  double* l = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * E);
+  if (!l) return 2;
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * k);
+  double* w = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * k);
+  int rc = (!idx || !w) ? 2 : oracle_route(T, H, E, k, act, x, Wr, bias, idx, w, l);
+  for (int t = 0; t < T && !rc; ++t) {
+    const double* lt = l + (size_t)t * E;
+    const int id = token_ids[t];
+    int e_of[16], key[16];
+    for (int r = 0; r < k; ++r) {
+      const int e = (id >= 0 && id < vocab) ? table[(size_t)id * k + r] : -1;
+      e_of[r] = (e >= 0 && e < E) ? e : -1;
+      key[r] = (e_of[r] >= 0 ? e_of[r] : E + r) * 16 + r; /* unique: table order breaks ties */
+    }
+    double m = -INFINITY, z = 0.0;
+    for (int r = 0; r < k; ++r)
+      if (e_of[r] >= 0 && lt[e_of[r]] > m) m = lt[e_of[r]];
+    for (int r = 0; r < k; ++r)
+      if (e_of[r] >= 0) z += exp(lt[e_of[r]] - m);
+    for (int r = 0; r < k; ++r) {
+      int rank = 0;
+      for (int q = 0; q < k; ++q) rank += key[q] < key[r];
+      topk_idx[(size_t)t * k + rank] = e_of[r];
+      topk_w[(size_t)t * k + rank] = e_of[r] >= 0 ? exp(lt[e_of[r]] - m) / z : 0.0;
+    }
+  }
+  free(l);
+  free(idx);
+  free(w);
+  return rc;
+}
+
+/* ---------------------------------------------------------------------------------------- */
 /* step 4: permutation (a stable counting sort of the pairs q = t*k + j by expert)           */
 /* ---------------------------------------------------------------------------------------- */
 
@@ -215,6 +262,7 @@ int oracle_permute(int T, int k, int E, const int32_t* topk_idx, int32_t* expert
   for (int e = 0; e <= E; ++e) expert_offsets[e] = 0;
   for (int q = 0; q < P; ++q) {
     int e = topk_idx[q];
+    if (e == -1) continue; /* "no expert" (hash routing's invalid entries): skipped */
     if (e < 0 || e >= E) {
       free(fill);
       return 1;
@@ -224,6 +272,10 @@ int oracle_permute(int T, int k, int E, const int32_t* topk_idx, int32_t* expert
   for (int e = 0; e < E; ++e) expert_offsets[e + 1] += expert_offsets[e];
   for (int e = 0; e < E; ++e) fill[e] = expert_offsets[e];
   for (int q = 0; q < P; ++q) {
+    if (topk_idx[q] == -1) {
+      pair_slot[q] = -1;
+      continue;
+    }
     int slot = fill[topk_idx[q]]++;
     slot_token[slot] = q / k;
     pair_slot[q] = slot;
@@ -401,15 +453,15 @@ int oracle_combine_token(int H, int k, const double* w, const double* yk, const 
 /* the whole layer, steps 1-7                                                                */
 /* ---------------------------------------------------------------------------------------- */
 
-int oracle_layer(int T, int H, int E, int k, int I, int act, const void* x, const void* Wr,
-                 const float* bias, int fmt_r, const void* rg, const void* rsg, const void* ru,
-                 const void* rsu, const void* rd, const void* rsd, int has_shared, int fmt_s,
-                 const void* sg, const void* ssg, const void* su, const void* ssu,
-                 const void* sd, const void* ssd, int32_t* topk_idx, double* topk_w,
-                 int32_t* expert_offsets, int32_t* slot_token, int32_t* pair_slot, double* y) {
+/* steps 4-7 from a given routing (topk_idx, topk_w) */
+static int layer_after_route(int T, int H, int E, int k, int I, int act, const void* x, int fmt_r,
+                             const void* rg, const void* rsg, const void* ru, const void* rsu,
+                             const void* rd, const void* rsd, int has_shared, int fmt_s,
+                             const void* sg, const void* ssg, const void* su, const void* ssu,
+                             const void* sd, const void* ssd, const int32_t* topk_idx,
+                             const double* topk_w, int32_t* expert_offsets, int32_t* slot_token,
+                             int32_t* pair_slot, double* y) {
   int P = T * k, rc;
-  rc = oracle_route(T, H, E, k, act, x, Wr, bias, topk_idx, topk_w, NULL);
-  if (rc) return rc;
   rc = oracle_permute(T, k, E, topk_idx, expert_offsets, slot_token, pair_slot);
   if (rc) return rc;
   size_t gw = w_bytes(fmt_r, H, I), gs = s_bytes(fmt_r, H, I);
@@ -418,8 +470,8 @@ int oracle_layer(int T, int H, int E, int k, int I, int act, const void* x, cons
   double* yperm = (double*)malloc(sizeof(double) * (size_t)P * H);
   double* ysh = has_shared ? (double*)malloc(sizeof(double) * (size_t)T * H) : NULL;
   if (!xin || !yperm || (has_shared && !ysh)) return 2;
-  /* rows of each expert's group, gathered in slot order */
-  for (int r = 0; r < P; ++r)
+  /* rows of each expert's group, gathered in slot order (the expert_offsets[E] pairs with one) */
+  for (int r = 0; r < expert_offsets[E]; ++r)
     for (int h = 0; h < H; ++h) xin[(size_t)r * H + h] = act_at(x, act, (size_t)slot_token[r] * H + h);
   for (int e = 0; e < E && !rc; ++e) {
     int r0 = expert_offsets[e], M = expert_offsets[e + 1] - r0;
@@ -438,8 +490,13 @@ int oracle_layer(int T, int H, int E, int k, int I, int act, const void* x, cons
     double* yk = (double*)malloc(sizeof(double) * (size_t)k * H);
     if (!yk) rc = 2;
     for (int t = 0; t < T && !rc; ++t) {
-      for (int j = 0; j < k; ++j)
-        memcpy(yk + (size_t)j * H, yperm + (size_t)pair_slot[(size_t)t * k + j] * H, sizeof(double) * H);
+      for (int j = 0; j < k; ++j) {
+        const int32_t ps = pair_slot[(size_t)t * k + j];
+        if (ps >= 0)
+          memcpy(yk + (size_t)j * H, yperm + (size_t)ps * H, sizeof(double) * H);
+        else /* a pair without an expert (hash routing's invalid entries) adds nothing */
+          memset(yk + (size_t)j * H, 0, sizeof(double) * H);
+      }
       oracle_combine_token(H, k, topk_w + (size_t)t * k, yk, ysh ? ysh + (size_t)t * H : NULL,
                            y + (size_t)t * H);
     }
@@ -449,4 +506,30 @@ int oracle_layer(int T, int H, int E, int k, int I, int act, const void* x, cons
   free(yperm);
   free(ysh);
   return rc;
+}
+
+int oracle_layer(int T, int H, int E, int k, int I, int act, const void* x, const void* Wr,
+                 const float* bias, int fmt_r, const void* rg, const void* rsg, const void* ru,
+                 const void* rsu, const void* rd, const void* rsd, int has_shared, int fmt_s,
+                 const void* sg, const void* ssg, const void* su, const void* ssu,
+                 const void* sd, const void* ssd, int32_t* topk_idx, double* topk_w,
+                 int32_t* expert_offsets, int32_t* slot_token, int32_t* pair_slot, double* y) {
+  int rc = oracle_route(T, H, E, k, act, x, Wr, bias, topk_idx, topk_w, NULL);
+  if (rc) return rc;
+  return layer_after_route(T, H, E, k, I, act, x, fmt_r, rg, rsg, ru, rsu, rd, rsd, has_shared, fmt_s, sg,
+                           ssg, su, ssu, sd, ssd, topk_idx, topk_w, expert_offsets, slot_token, pair_slot, y);
+}
+
+/* the whole layer with hash routing (steps 1-3 replaced by oracle_route_hash) */
+int oracle_layer_hash(int T, int H, int E, int k, int I, int act, const void* x, const void* Wr,
+                      const float* bias, const int32_t* token_ids, const int32_t* table, int vocab,
+                      int fmt_r, const void* rg, const void* rsg, const void* ru, const void* rsu,
+                      const void* rd, const void* rsd, int has_shared, int fmt_s, const void* sg,
+                      const void* ssg, const void* su, const void* ssu, const void* sd,
+                      const void* ssd, int32_t* topk_idx, double* topk_w, int32_t* expert_offsets,
+                      int32_t* slot_token, int32_t* pair_slot, double* y) {
+  int rc = oracle_route_hash(T, H, E, k, act, x, Wr, bias, token_ids, table, vocab, topk_idx, topk_w);
+  if (rc) return rc;
+  return layer_after_route(T, H, E, k, I, act, x, fmt_r, rg, rsg, ru, rsu, rd, rsd, has_shared, fmt_s, sg,
+                           ssg, su, ssu, sd, ssd, topk_idx, topk_w, expert_offsets, slot_token, pair_slot, y);
 }

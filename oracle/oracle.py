@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         _lib.oracle_expert_ffn.argtypes = [i, i, i, i, p, p, p, p, p, p, p, p]
         _lib.oracle_combine_token.argtypes = [i, i, p, p, p, p]
         _lib.oracle_layer.argtypes = [i] * 6 + [p, p, p] + [i] + [p] * 6 + [i, i] + [p] * 6 + [p] * 6
+        _lib.oracle_route_hash.argtypes = [i] * 5 + [p, p, p, p, p, i, p, p]
+        _lib.oracle_layer_hash.argtypes = [i] * 6 + [p, p, p, p, p, i] + [i] + [p] * 6 + [i, i] + [p] * 6 + [p] * 6
     return _lib
 
 
@@ -141,6 +143,22 @@ def route(x, Wr, bias, k: int, act: str):
     return idx, w, logits
 
 
+def route_hash(x, Wr, bias, token_ids, table, k: int, act: str):
+    """Hash routing: the experts of token t are table[token_ids[t]] (a [vocab][k] int32 table);
+    -> (topk_idx int32[T,k], topk_w float64[T,k])."""
+    x = _c(x, _wdtype(act))
+    Wr = _c(Wr, _wdtype(act))
+    tid = _c(token_ids, np.int32)
+    tab = _c(table, np.int32)
+    T, H = x.shape
+    E = Wr.shape[1]
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    _check(lib().oracle_route_hash(T, H, E, k, FMT[act], _ptr(x), _ptr(Wr), _ptr(_c(bias, np.float32)), _ptr(tid),
+                                   _ptr(tab), tab.shape[0], _ptr(idx), _ptr(w)), "route_hash")
+    return idx, w
+
+
 def permute(topk_idx, E: int):
     """-> (expert_offsets int32[E+1], slot_token int32[T*k], pair_slot int32[T*k])."""
     idx = _c(topk_idx, np.int32)
@@ -177,8 +195,9 @@ def combine_token(w, yk, ysh=None) -> np.ndarray:
     return y
 
 
-def layer(spec, x, Wr, bias, routed: dict, shared: dict | None):
-    """The whole layer. ``routed`` holds the E experts stacked on a leading axis."""
+def layer(spec, x, Wr, bias, routed: dict, shared: dict | None, hash_routing=None):
+    """The whole layer. ``routed`` holds the E experts stacked on a leading axis. ``hash_routing``
+    = (token_ids, table) routes by the table instead of the router's top-k."""
     T, H, E, k, I = spec.T, spec.H, spec.E, spec.k, spec.I
     fr, fs = spec.w_routed, spec.w_shared
     x = _c(x, _wdtype(spec.act))
@@ -195,12 +214,18 @@ def layer(spec, x, Wr, bias, routed: dict, shared: dict | None):
         "expert_offsets": np.empty(E + 1, np.int32), "slot_token": np.empty(T * k, np.int32),
         "pair_slot": np.empty(T * k, np.int32), "y": np.empty((T, H), np.float64),
     }
-    rc = lib().oracle_layer(
-        T, H, E, k, I, FMT[spec.act], _ptr(x), _ptr(Wr), _ptr(_c(bias, np.float32)),
+    common = (
         FMT[fr], _ptr(r[0]), _ptr(rs[0]), _ptr(r[1]), _ptr(rs[1]), _ptr(r[2]), _ptr(rs[2]),
         1 if shared is not None else 0, FMT[fs] if shared is not None else 0,
         _ptr(s[0]), _ptr(ss[0]), _ptr(s[1]), _ptr(ss[1]), _ptr(s[2]), _ptr(ss[2]),
         _ptr(out["topk_idx"]), _ptr(out["topk_w"]), _ptr(out["expert_offsets"]),
         _ptr(out["slot_token"]), _ptr(out["pair_slot"]), _ptr(out["y"]))
+    head = (T, H, E, k, I, FMT[spec.act], _ptr(x), _ptr(Wr), _ptr(_c(bias, np.float32)))
+    if hash_routing is None:
+        rc = lib().oracle_layer(*head, *common)
+    else:
+        tid = _c(hash_routing[0], np.int32)
+        tab = _c(hash_routing[1], np.int32)
+        rc = lib().oracle_layer_hash(*head, _ptr(tid), _ptr(tab), tab.shape[0], *common)
     _check(rc, "layer")
     return out

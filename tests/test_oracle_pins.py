@@ -540,6 +540,83 @@ def test_layer_hybrid_mxfp8_shared_changes_only_the_shared_expert():
     assert np.abs(dy).max() > 0
 
 
+# ------------------------------------------------------------------ hash routing
+# 'CANN DeepSeek-V4推理优化', MoE section: the first layers route by hash, the later ones by the
+# learned router. Read plainly: the experts are a fixed row of a table indexed by token id; the
+# weights stay the router's softmax, renormalised over that set.
+
+def test_route_hash_with_the_topk_table_equals_score_routing():
+    """A table whose row t holds token t's top-k (in shuffled order) reproduces score routing."""
+    s = _tiny(T=24, E=16, k=4)
+    r = L.router_inputs(s)
+    idx, w, _ = O.route(r["x"], r["Wr"], r["bias"], s.k, s.act)
+    rng = np.random.default_rng(3)
+    table = np.stack([rng.permutation(row) for row in idx]).astype(np.int32)
+    hidx, hw = O.route_hash(r["x"], r["Wr"], r["bias"], np.arange(s.T, dtype=np.int32), table, s.k, s.act)
+    assert np.array_equal(hidx, idx)
+    assert np.allclose(hw, w, rtol=1e-14, atol=0)
+
+
+def test_route_hash_brute_force_weights_and_order():
+    """Against a numpy softmax of the pinned router scores over each token's table row."""
+    s = _tiny(T=30, E=12, k=3, seed=21)
+    r = L.router_inputs(s)
+    _, _, logits = O.route(r["x"], r["Wr"], r["bias"], s.k, s.act)
+    ids, table = L.hash_inputs(s, 7)
+    hidx, hw = O.route_hash(r["x"], r["Wr"], r["bias"], ids, table, s.k, s.act)
+    for t in range(s.T):
+        row = sorted(table[ids[t]])
+        assert list(hidx[t]) == row
+        l = logits[t, row]
+        ref = np.exp(l - l.max()) / np.exp(l - l.max()).sum()
+        assert np.allclose(hw[t], ref, rtol=1e-13)
+        assert abs(hw[t].sum() - 1) < 1e-13
+
+
+def test_route_hash_invalid_ids_and_entries_and_duplicates():
+    """Ids outside [0, vocab) give k times (-1, 0); entries outside [0, E) become (-1, 0) after the
+    valid ones; a duplicated expert is kept twice, in table order, each with its own weight."""
+    s = _tiny(T=4, E=8, k=3, seed=22)
+    r = L.router_inputs(s)
+    _, _, logits = O.route(r["x"], r["Wr"], r["bias"], s.k, s.act)
+    table = np.array([[5, 1, 3], [7, 8, 2], [4, 4, -3], [0, 6, 2]], np.int32)
+    ids = np.array([-1, 1, 2, 4], np.int32)
+    hidx, hw = O.route_hash(r["x"], r["Wr"], r["bias"], ids, table, s.k, s.act)
+    assert hidx[0].tolist() == [-1, -1, -1] and not hw[0].any()
+    assert hidx[1].tolist() == [2, 7, -1] and hw[1, 2] == 0
+    l = logits[1, [2, 7]]
+    assert np.allclose(hw[1, :2], np.exp(l - l.max()) / np.exp(l - l.max()).sum(), rtol=1e-13)
+    assert hidx[2].tolist() == [4, 4, -1] and np.allclose(hw[2], [0.5, 0.5, 0.0])
+    assert hidx[3].tolist() == [-1, -1, -1]  # id 4 is outside a 4-row table
+
+
+def test_layer_hash_equals_score_layer_with_the_topk_table_and_skips_invalid_pairs():
+    """The hash-routed layer with the top-k table is the score-routed layer; with a table entry
+    made invalid, the token's output loses exactly that pair's weighted expert row."""
+    s = _tiny(T=6, H=128, E=4, k=2, seed=23, shared=True)
+    r = L.router_inputs(s)
+    routed = L.stack_experts(s)
+    sh = L.expert_weights(s, "shared", 0)
+    a = O.layer(s, r["x"], r["Wr"], r["bias"], routed, sh)
+    table = a["topk_idx"][:, ::-1].copy()
+    ids = np.arange(s.T, dtype=np.int32)
+    b = O.layer(s, r["x"], r["Wr"], r["bias"], routed, sh, hash_routing=(ids, table))
+    assert np.array_equal(a["topk_idx"], b["topk_idx"])
+    # the same weights up to rounding: exp(l - max over all E) / sums, against exp(l - max over the set)
+    assert np.allclose(a["topk_w"], b["topk_w"], rtol=1e-14) and np.allclose(a["y"], b["y"], rtol=1e-12, atol=1e-13)
+    bad = table.copy()
+    bad[2, 0] = s.E  # token 2 keeps one expert
+    c = O.layer(s, r["x"], r["Wr"], r["bias"], routed, sh, hash_routing=(ids, bad))
+    keep = int(bad[2, 1])
+    assert c["topk_idx"][2].tolist() == [keep, -1] and c["topk_w"][2].tolist() == [1.0, 0.0]
+    assert c["pair_slot"][2 * s.k + 1] == -1
+    u = L.act_to_f64(r["x"], "bf16")[2:3]
+    one = {kk: (None if v is None else v[keep]) for kk, v in routed.items()}
+    ref = O.expert_ffn(u, one, "bf16")[0] + O.expert_ffn(u, sh, "bf16")[0]
+    assert np.allclose(c["y"][2], ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.delete(c["y"], 2, axis=0), np.delete(b["y"], 2, axis=0))
+
+
 # ------------------------------------------------------------------ Int8 W8A8
 # 'CANN DeepSeek-V4推理优化', Int8 quantisation strategy: routed and shared experts' linear layers
 # run W8A8, weights int8 per output channel (static), activations int8 per token (dynamic).
