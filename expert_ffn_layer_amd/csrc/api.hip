@@ -226,9 +226,16 @@ moe_status check_weights(const moe_weights* w, moe_dtype fmt, const char* what) 
   return MOE_OK;
 }
 
-// moe_route without the argument checks.
+// Hash routing's inputs: the experts of token t are row ids[t] of table[vocab][k].
+struct HashRoute {
+  const int32_t* ids;
+  const int32_t* table;
+  int vocab;
+};
+
+// moe_route (or moe_route_hash, with `hash`) without the argument checks.
 moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const float* bias, int32_t* idx,
-                    float* w, void* ws, const Ws& L, hipStream_t st) {
+                    float* w, void* ws, const Ws& L, hipStream_t st, const HashRoute* hash = nullptr) {
   if (s.T == 0) return MOE_OK;
   const RouterPlan rp = router_plan(s);
   // scores of the padded experts: 256-wide MFMA tiles on the prefill kernel, 64 on the decode one
@@ -254,8 +261,9 @@ moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const flo
   hipError_t e = rp.prefill ? launch_prefill_scores(a, st)
                             : launch_grouped_decode(s.act, EPI_F32, s.act, s.act, a, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
   if (e != hipSuccess) return hip_status(e, "router scores");
-  e = launch_topk(at<float>(ws, L.logits), Ep, a.ksplit, bias, s.T, s.E, s.k, idx, w, st);
-  return hip_status(e, "router top-k");
+  e = launch_topk(at<float>(ws, L.logits), Ep, a.ksplit, bias, s.T, s.E, s.k, hash ? hash->ids : nullptr,
+                  hash ? hash->table : nullptr, hash ? hash->vocab : 0, idx, w, st);
+  return hip_status(e, hash ? "hash routing" : "router top-k");
 }
 
 // The LDS-tiled MFMA kernel when the experts average at least 64 rows (or when asked for and
@@ -450,7 +458,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
 
 moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
                     const moe_weights* routed, const moe_weights* shared, void* y, int32_t* topk_idx_out,
-                    float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t const* ev) {
+                    float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t const* ev,
+                    const HashRoute* hash = nullptr) {
   moe_status s = check_shape(shape);
   if (s != MOE_OK) return s;
   if ((s = check_weights(routed, shape->w_routed, "routed")) != MOE_OK) return s;
@@ -467,7 +476,7 @@ moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed
   void* y_perm = at<void>(ws, L.y_perm);
   void* y_sh = shape->I_shared ? at<void>(ws, L.y_shared) : nullptr;
   if (ev && (s = record(ev[0], st)) != MOE_OK) return s;
-  if ((s = do_route(*shape, x, Wr_packed, bias, idx, w, ws, L, st)) != MOE_OK) return s;
+  if ((s = do_route(*shape, x, Wr_packed, bias, idx, w, ws, L, st, hash)) != MOE_OK) return s;
   if (ev && (s = record(ev[1], st)) != MOE_OK) return s;
   bool planned = false;
   if ((s = do_permute(*shape, idx, off, slot_token, pair_slot, ws, L, st, true, &planned)) != MOE_OK) return s;
@@ -537,6 +546,20 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* Wr_packe
   return do_route(*shape, x, Wr_packed, bias, topk_idx, topk_w, ws, L, (hipStream_t)stream);
 }
 
+moe_status moe_route_hash(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
+                          const int32_t* token_ids, const int32_t* hash_table, int32_t vocab, int32_t* topk_idx,
+                          float* topk_w, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (vocab < 1) return fail(MOE_ERR_INVALID_ARG, "vocab=%d < 1", vocab);
+  if (shape->T && (!x || !Wr_packed || !token_ids || !hash_table || !topk_idx || !topk_w))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  Ws L;
+  if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
+  const HashRoute h{token_ids, hash_table, vocab};
+  return do_route(*shape, x, Wr_packed, bias, topk_idx, topk_w, ws, L, (hipStream_t)stream, &h);
+}
+
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* expert_offsets,
                        int32_t* slot_token, int32_t* pair_slot, void* ws, size_t ws_bytes, moe_stream_t stream) {
   moe_status s = check_shape(shape);
@@ -577,6 +600,18 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, ws_bytes,
                   (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_layer_forward_hash(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
+                                  const int32_t* token_ids, const int32_t* hash_table, int32_t vocab,
+                                  const moe_weights* routed, const moe_weights* shared, void* y,
+                                  int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                                  moe_stream_t stream) {
+  if (vocab < 1) return fail(MOE_ERR_INVALID_ARG, "vocab=%d < 1", vocab);
+  if (shape && shape->T && (!token_ids || !hash_table)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  const HashRoute h{token_ids, hash_table, vocab};
+  return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, ws_bytes,
+                  (hipStream_t)stream, nullptr, &h);
 }
 
 moe_status moe_layer_forward_timed(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,

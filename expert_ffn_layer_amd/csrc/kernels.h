@@ -87,7 +87,8 @@ hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int s
                        int32_t* group_range, int32_t* cum_blocks, int32_t* block_group, uint32_t* zero, int zero_words,
                        hipStream_t st);
 hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
-                       int32_t* idx, float* w, hipStream_t st);
+                       const int32_t* hash_ids, const int32_t* hash_table, int vocab, int32_t* idx, float* w,
+                       hipStream_t st);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* slot_token, int32_t* pair_slot, int32_t* ws_rank,
                           int32_t* ws_hist, hipStream_t st);

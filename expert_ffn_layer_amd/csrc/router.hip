@@ -6,6 +6,12 @@
 // partial scores, in a fixed order); k rounds of a wave-wide arg-max (ties to the lower index)
 // pick the experts; they are then listed in ascending expert index. The weights are exp(l - m) / sum over the chosen of exp(l - m) with
 // m the largest score, which equals the softmax over all E renormalised over the chosen k.
+//
+// Hash routing ('CANN DeepSeek-V4推理优化', MoE section: the first layers route by hash) replaces
+// the arg-max rounds: the experts are row token_ids[t] of a [vocab][k] table, each score fetched
+// from the lane that holds it, and the weights renormalise over that set in the same way. Entries
+// outside [0, E) (all k for an id outside [0, vocab)) are written as expert -1 with weight 0
+// after the valid ones; equal experts keep table order.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,9 +24,11 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-template <int PL>
+template <int PL, bool HASH>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int ldl, long long part_stride,
                                                    int nparts, const float* __restrict__ bias, int T, int E, int k,
+                                                   const int32_t* __restrict__ token_ids,
+                                                   const int32_t* __restrict__ table, int vocab,
                                                    int32_t* __restrict__ idx, float* __restrict__ wout) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -57,6 +65,54 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   }
   int sel[TOPK_MAX];
   float sv[TOPK_MAX];
+  if constexpr (HASH) {
+    const int id = token_ids[t];
+    const bool id_ok = id >= 0 && id < vocab;
+    int key[TOPK_MAX];
+    float m = NEG;
+#pragma unroll
+    for (int r = 0; r < TOPK_MAX; ++r) {
+      sel[r] = -1;
+      sv[r] = NEG;
+      key[r] = 0x7fffffff;
+      if (r < k) {
+        int e = id_ok ? table[(size_t)id * k + r] : -1;  // the same address in every lane
+        if (e < 0 || e >= E) e = -1;
+        float sc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < PL; ++j)
+          if (e >= 0 && (e >> 6) == j) sc = v[j];
+        sc = __shfl(sc, e >= 0 ? (e & 63) : 0, 64);  // the score of e lives in lane e % 64
+        sel[r] = e;
+        sv[r] = e >= 0 ? sc : NEG;
+        key[r] = (e >= 0 ? e : E + r) * TOPK_MAX + r;  // valid ones ascending, then table order
+        if (e >= 0) m = __builtin_fmaxf(m, sc);
+      }
+    }
+    float z = 0.0f, mine_p = 0.0f;
+    int mine_key = 0x7fffffff, mine = -1;
+#pragma unroll
+    for (int r = 0; r < TOPK_MAX; ++r) {
+      if (r < k) {
+        const float p = sel[r] >= 0 ? __expf(sv[r] - m) : 0.0f;
+        z += p;
+        if (r == lane) {
+          mine = sel[r];
+          mine_p = p;
+          mine_key = key[r];
+        }
+      }
+    }
+    if (lane < k) {
+      int rank = 0;
+#pragma unroll
+      for (int r = 0; r < TOPK_MAX; ++r)
+        if (r < k && key[r] < mine_key) ++rank;
+      idx[(size_t)t * k + rank] = mine;
+      wout[(size_t)t * k + rank] = mine >= 0 ? mine_p / z : 0.0f;
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < TOPK_MAX; ++r) {
     sel[r] = 0x7fffffff;
@@ -104,18 +160,30 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   }
 }
 
-hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
-                       int32_t* idx, float* w, hipStream_t st) {
-  const long long ps = (long long)T * ldl;
-  if (k > TOPK_MAX || E > 64 * PER_LANE_MAX) return hipErrorInvalidValue;
+template <bool HASH>
+static void launch_topk_t(const float* logits, int ldl, long long ps, int nparts, const float* bias, int T, int E,
+                          int k, const int32_t* ids, const int32_t* table, int vocab, int32_t* idx, float* w,
+                          hipStream_t st) {
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
   const int pl = (E + 63) / 64;
-  if (pl <= 1) topk_kernel<1><<<grid, block, 0, st>>>(logits, ldl, ps, nparts, bias, T, E, k, idx, w);
-  else if (pl <= 2) topk_kernel<2><<<grid, block, 0, st>>>(logits, ldl, ps, nparts, bias, T, E, k, idx, w);
-  else if (pl <= 4) topk_kernel<4><<<grid, block, 0, st>>>(logits, ldl, ps, nparts, bias, T, E, k, idx, w);
-  else if (pl <= 6) topk_kernel<6><<<grid, block, 0, st>>>(logits, ldl, ps, nparts, bias, T, E, k, idx, w);
-  else if (pl <= 8) topk_kernel<8><<<grid, block, 0, st>>>(logits, ldl, ps, nparts, bias, T, E, k, idx, w);
-  else topk_kernel<16><<<grid, block, 0, st>>>(logits, ldl, ps, nparts, bias, T, E, k, idx, w);
+#define MOE_TOPK(PL) topk_kernel<PL, HASH><<<grid, block, 0, st>>>(logits, ldl, ps, nparts, bias, T, E, k, ids, table, vocab, idx, w)
+  if (pl <= 1) MOE_TOPK(1);
+  else if (pl <= 2) MOE_TOPK(2);
+  else if (pl <= 4) MOE_TOPK(4);
+  else if (pl <= 6) MOE_TOPK(6);
+  else if (pl <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+}
+
+hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
+                       const int32_t* hash_ids, const int32_t* hash_table, int vocab, int32_t* idx, float* w,
+                       hipStream_t st) {
+  const long long ps = (long long)T * ldl;
+  if (k > TOPK_MAX || E > 64 * PER_LANE_MAX) return hipErrorInvalidValue;
+  if (T == 0) return hipSuccess;
+  if (hash_ids) launch_topk_t<true>(logits, ldl, ps, nparts, bias, T, E, k, hash_ids, hash_table, vocab, idx, w, st);
+  else launch_topk_t<false>(logits, ldl, ps, nparts, bias, T, E, k, nullptr, nullptr, 0, idx, w, st);
   return hipGetLastError();
 }
 

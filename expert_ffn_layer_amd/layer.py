@@ -46,6 +46,11 @@ class PackedLayer:
         if need > self.ws.numel():
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.ws.device)
 
+    def forward_hash(self, x, bias, token_ids, hash_table, y, topk_idx=None, topk_w=None, stream=None):
+        N.moe_layer_forward_hash(self.shape, x, self.Wr, bias, token_ids, hash_table, self.routed, self.shared, y,
+                                 topk_idx, topk_w, self.ws, stream)
+        return y
+
     def forward(self, x, bias, y, topk_idx=None, topk_w=None, stream=None):
         N.moe_layer_forward(self.shape, x, self.Wr, bias, self.routed, self.shared, y, topk_idx, topk_w,
                             self.ws, stream)

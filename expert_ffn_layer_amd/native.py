@@ -18,8 +18,8 @@ PATH = {"auto": 0, "decode": 1, "prefill": 2}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_pack_size", "moe_pack", "moe_workspace_size",
-           "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_forward_timed")
+           "moe_route", "moe_route_hash", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
+           "moe_layer_forward_hash", "moe_layer_forward_timed")
 TIMED_EVENTS = 7
 
 
@@ -62,10 +62,12 @@ def load() -> ctypes.CDLL:
         lib.moe_pack.argtypes = [ctypes.c_int, I32, I32, I32, P, P, P, P, P]
         lib.moe_workspace_size.argtypes = [PS, ctypes.POINTER(SZ)]
         lib.moe_route.argtypes = [PS, P, P, P, P, P, P, SZ, P]
+        lib.moe_route_hash.argtypes = [PS, P, P, P, P, P, I32, P, P, P, SZ, P]
         lib.moe_permute.argtypes = [PS, P, P, P, P, P, SZ, P]
         lib.moe_grouped_ffn.argtypes = [PS, P, P, P, PW, PW, P, P, P, SZ, P]
         lib.moe_combine.argtypes = [PS, P, P, P, P, P, P]
         lib.moe_layer_forward.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P]
+        lib.moe_layer_forward_hash.argtypes = [PS, P, P, P, P, P, I32, PW, PW, P, P, P, P, SZ, P]
         lib.moe_layer_forward_timed.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P,
                                                 ctypes.POINTER(ctypes.c_void_p)]
         for name in EXPORTS[2:]:
@@ -127,6 +129,12 @@ def moe_route(shape, x, Wr_packed, bias, topk_idx, topk_w, ws, stream=None):
                             _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def moe_route_hash(shape, x, Wr_packed, bias, token_ids, hash_table, topk_idx, topk_w, ws, stream=None):
+    _check(load().moe_route_hash(ctypes.byref(shape), _p(x), _p(Wr_packed), _p(bias), _p(token_ids),
+                                 _p(hash_table), hash_table.shape[0], _p(topk_idx), _p(topk_w), _p(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def moe_permute(shape, topk_idx, expert_offsets, slot_token, pair_slot, ws, stream=None):
     _check(load().moe_permute(ctypes.byref(shape), _p(topk_idx), _p(expert_offsets), _p(slot_token),
                               _p(pair_slot), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
@@ -154,6 +162,16 @@ def moe_layer_forward(shape, x, Wr_packed, bias, routed: dict, shared: dict | No
                                     None if s is None else ctypes.byref(s), _p(y), _p(topk_idx), _p(topk_w),
                                     _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def moe_layer_forward_hash(shape, x, Wr_packed, bias, token_ids, hash_table, routed: dict, shared: dict | None, y,
+                           topk_idx=None, topk_w=None, ws=None, stream=None):
+    r, s = weights(routed), weights(shared)
+    _check(load().moe_layer_forward_hash(ctypes.byref(shape), _p(x), _p(Wr_packed), _p(bias), _p(token_ids),
+                                         _p(hash_table), hash_table.shape[0], ctypes.byref(r),
+                                         None if s is None else ctypes.byref(s), _p(y), _p(topk_idx), _p(topk_w),
+                                         _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                         _stream(stream)))
 
 
 def moe_layer_forward_timed(shape, x, Wr_packed, bias, routed: dict, shared: dict | None, y, events,

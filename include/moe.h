@@ -169,6 +169,24 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* Wr_packe
                      size_t ws_bytes, moe_stream_t stream);
 
 /*
+ * moe_route_hash — hash routing ('CANN DeepSeek-V4推理优化', MoE section: the first layers pick
+ * their experts by hash, the later ones by the learned router). The experts of token t are row
+ * token_ids[t] of hash_table; the weights are moe_route's, renormalised over that set.
+ *   token_ids  int32[T], values in [0, vocab)
+ *   hash_table int32[vocab][k]: the k experts of each id, values in [0, E)
+ *   topk_idx   int32[T][k] out: the row's valid experts in ascending index (equal ones in table
+ *              order), then -1 for each entry outside [0, E) (all k for an id outside [0, vocab))
+ *   topk_w     float[T][k] out: exp(l - m) / sum of exp(l - m) over the row's valid experts,
+ *              m = their largest score (the router's scores, bias included); 0 for -1 entries
+ * Pairs with expert -1 are skipped by moe_permute and add nothing in moe_combine. Other
+ * arguments, ownership and errors as moe_route; MOE_ERR_INVALID_ARG for vocab < 1.
+ */
+moe_status moe_route_hash(const moe_shape* shape, const void* x, const void* Wr_packed,
+                          const float* bias, const int32_t* token_ids, const int32_t* hash_table,
+                          int32_t vocab, int32_t* topk_idx, float* topk_w, void* ws,
+                          size_t ws_bytes, moe_stream_t stream);
+
+/*
  * moe_permute — stable counting sort of the pairs q = t*k + j by expert [ch6 §6.2.6].
  *   topk_idx       int32[T*k] in: values in [0, E) (entries outside are skipped)
  *   expert_offsets int32[E+1] out: rows of expert e are [off[e], off[e+1]); off[E] = T*k
@@ -214,6 +232,17 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              const float* bias, const moe_weights* routed,
                              const moe_weights* shared, void* y, int32_t* topk_idx_out,
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_layer_forward_hash — moe_layer_forward with moe_route_hash in place of moe_route
+ * (arguments as those two).
+ */
+moe_status moe_layer_forward_hash(const moe_shape* shape, const void* x, const void* Wr_packed,
+                                  const float* bias, const int32_t* token_ids,
+                                  const int32_t* hash_table, int32_t vocab,
+                                  const moe_weights* routed, const moe_weights* shared, void* y,
+                                  int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                                  size_t ws_bytes, moe_stream_t stream);
 
 /*
  * moe_layer_forward_timed — moe_layer_forward that also records `events` (MOE_TIMED_EVENTS

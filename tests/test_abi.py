@@ -140,5 +140,10 @@ def test_entry_points_reject_null_and_small_workspace_before_launch():
     wf = N.MoeWeights(0x1000, 0x1000, 0x1000, None, None, None)
     assert lib.moe_layer_forward(ctypes.byref(sh), fake, fake, None, ctypes.byref(wf), None, fake, None, None,
                                  fake, 1 << 30, None) == 1  # shared weights missing
+    # hash routing: missing ids or table, vocab < 1
+    assert lib.moe_route_hash(ctypes.byref(s), fake, fake, None, None, fake, 10, fake, fake, fake, 1 << 30, None) == 1
+    assert lib.moe_route_hash(ctypes.byref(s), fake, fake, None, fake, fake, 0, fake, fake, fake, 1 << 30, None) == 1
+    assert lib.moe_layer_forward_hash(ctypes.byref(s), fake, fake, None, fake, None, 10, ctypes.byref(wf), None, fake,
+                                      None, None, fake, 1 << 30, None) == 1
     # misaligned workspace
     assert lib.moe_permute(ctypes.byref(s), fake, fake, fake, fake, P(0x1001), 1 << 30, None) == 1

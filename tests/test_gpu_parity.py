@@ -13,7 +13,7 @@ from inputgen import layers as L
 from inputgen import philox as px
 from oracle import oracle as O
 
-from _gpu import build, oracle_full, oracle_tokens, rel_fro, run, say, to_f64, tol_of
+from _gpu import build, host_weights, oracle_full, oracle_tokens, rel_fro, run, say, to_f64, tol_of
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -381,6 +381,49 @@ def test_layer_random_sweep(spec):
         err = rel_fro(to_f64(y), ref["y"])
         say("  %s: rel. Frobenius error %.3e (bound %.0e)" % (path, err, tol_of(spec)))
         assert err <= tol_of(spec)
+
+
+# ------------------------------------------------------------------ hash routing
+
+HASH_SPECS = [
+    ("decode-bf16-shared", L.LayerSpec("h1", T=45, H=512, E=12, k=3, I=256, shared=True, seed=71), 37),
+    ("prefill-fp8", L.LayerSpec("h2", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="fp8",
+                                w_shared="fp8", seed=72), 1000),
+    ("wide-E", L.LayerSpec("h3", T=9, H=256, E=300, k=7, I=128, seed=73), 5),
+]
+
+
+@pytest.mark.parametrize("name,spec,vocab", HASH_SPECS, ids=[h[0] for h in HASH_SPECS])
+def test_hash_routing_matches_oracle(name, spec, vocab):
+    """moe_route_hash against the oracle (indices bit-exact, weights within 1e-5), with some invalid
+    ids and table entries mixed in; then the whole hash-routed layer."""
+    say("hash", name, spec, vocab)
+    lay, pl = build(spec, DEV)
+    ids, table = L.hash_inputs(spec, vocab)
+    ids[::7] = vocab + 3  # ids outside the table: all k pairs dropped
+    table[1, 0] = spec.E  # an entry outside [0, E): that pair dropped
+    if spec.k > 1:
+        table[2, 1] = table[2, 0]  # a repeated expert: both pairs kept
+    d_ids, d_tab = torch.from_numpy(ids).to(DEV), torch.from_numpy(table).to(DEV)
+    x = lay["x"].view(torch.bfloat16)
+    idx = torch.empty((spec.T, spec.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((spec.T, spec.k), dtype=torch.float32, device=DEV)
+    N.moe_route_hash(pl.shape, x, pl.Wr, lay["bias"], d_ids, d_tab, idx, w, pl.ws)
+    torch.cuda.synchronize()
+    ridx, rw = O.route_hash(lay["x_host"], lay["Wr_host"], lay["bias_host"], ids, table, spec.k, spec.act)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-5
+    y = torch.empty((spec.T, spec.H), dtype=torch.bfloat16, device=DEV)
+    idx2 = torch.empty_like(idx)
+    pl.forward_hash(x, lay["bias"], d_ids, d_tab, y, idx2)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), ridx)
+    routed = host_weights(lay["routed"])
+    shared = {kk: (None if v is None else v[0]) for kk, v in host_weights(lay["shared"]).items()} if spec.shared else None
+    ref = O.layer(spec, lay["x_host"], lay["Wr_host"], lay["bias_host"], routed, shared, hash_routing=(ids, table))
+    err = rel_fro(to_f64(y), ref["y"])
+    say("  rel. Frobenius error %.3e (bound %.0e)" % (err, tol_of(spec)))
+    assert err <= tol_of(spec)
 
 
 # ------------------------------------------------------------------ graph capture
