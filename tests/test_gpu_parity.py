@@ -383,6 +383,49 @@ def test_layer_random_sweep(spec):
         assert err <= tol_of(spec)
 
 
+def _sweep_quantised_specs(n=12, seed=2025):
+    """Random small layers over the activation-quantising formats (prefill path): W4A8 routed with a
+    bf16 or W8A8 MXFP8 shared expert or none, Int8 W8A8 with or without a shared expert; group
+    sizes from empty to several 256-row items, T from 1 up."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ("w4a8", "hybrid", "int8")[i % 3]
+        shared = kind == "hybrid" or bool(rng.random() < 0.5)
+        wr = "int8" if kind == "int8" else "mxfp4a8"
+        ws = {"w4a8": "bf16", "hybrid": "mxfp8a8", "int8": "int8"}[kind]
+        H = int(rng.choice([512, 1024]))
+        I = int(rng.choice([256, 512]))
+        E = int(rng.choice([4, 8, 16, 40]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 7, 33, 150, 420]))
+        zipf = bool(rng.random() < 0.5) and E >= 8
+        out.append(L.LayerSpec("swq%d" % i, T=T, H=H, E=E, k=k, I=I, shared=shared, w_routed=wr, w_shared=ws,
+                               router="zipf" if zipf else "uniform", zipf_alpha=1.1 if zipf else 0.0,
+                               calib_tokens=256, seed=300 + i))
+    return out
+
+
+SWEEP_Q = _sweep_quantised_specs()
+
+
+@pytest.mark.parametrize("spec", SWEEP_Q, ids=[s.name for s in SWEEP_Q])
+def test_layer_random_sweep_quantised(spec):
+    """Each random quantised layer on its (prefill) path: routing identical to the oracle's, outputs
+    within the bound, and a second call bit-identical."""
+    say("sweep-q", spec)
+    lay, pl = build(spec, DEV)
+    y, idx, w = run(spec, lay, pl)
+    ref = oracle_full(spec, lay)
+    assert np.array_equal(idx.cpu().numpy(), ref["topk_idx"])
+    assert np.max(np.abs(w.cpu().numpy() - ref["topk_w"])) <= 1e-5
+    err = rel_fro(to_f64(y), ref["y"])
+    say("  rel. Frobenius error %.3e (bound %.0e)" % (err, tol_of(spec)))
+    assert err <= tol_of(spec)
+    y2, _, _ = run(spec, lay, pl)
+    assert torch.equal(y, y2)
+
+
 # ------------------------------------------------------------------ hash routing
 
 HASH_SPECS = [
