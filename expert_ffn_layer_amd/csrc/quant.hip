@@ -18,71 +18,76 @@ namespace moe {
 
 namespace {
 
-constexpr int QTHREADS = 256;  // 4 waves, one row each
+constexpr int QTHREADS = 256;  // int8: 4 waves, one row each
 
-// Wave w of workgroup b quantises row 4b + w. Each lane takes 8 consecutive elements per pass of
-// 512, so four lanes hold one 32-block and agree on its exponent by two xor shuffles.
-__global__ void __launch_bounds__(QTHREADS) quant_mxfp8_kernel(const uint16_t* __restrict__ src, int rows, int K,
+// MXFP8: thread i quantises elements 8i .. 8i + 7 of the row-major [rows][K] matrix (K a multiple
+// of 32, so a 32-block is four consecutive threads of one wave, which agree on its exponent by two
+// xor shuffles, and block b of the flat matrix is row b / (K / 32), block b % (K / 32)).
+__global__ void __launch_bounds__(QTHREADS) quant_mxfp8_kernel(const uint16_t* __restrict__ src, long long n8,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (QTHREADS / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint16_t* in = src + (size_t)row * K;
-  for (int c = 8 * lane; c < K; c += 512) {  // K is a multiple of 32: 4-lane groups stay whole
-    const u32x4 v = *(const u32x4*)(in + c);
-    float f[8];
+  const long long i = (long long)blockIdx.x * QTHREADS + threadIdx.x;
+  const bool live = i < n8;  // the whole wave takes part in the shuffles
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (live) v = *(const u32x4*)(src + 8 * i);
+  float f[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16lo(v[i]);
-      f[2 * i + 1] = bf16hi(v[i]);
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
-    const int X = mxfp8_exponent(amax);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= e4m3_rne_sat(__builtin_amdgcn_ldexpf(f[i], -X)) << (8 * i);
-      hi |= e4m3_rne_sat(__builtin_amdgcn_ldexpf(f[4 + i], -X)) << (8 * i);
-    }
-    *(u32x2*)(codes + (size_t)row * K + c) = u32x2{lo, hi};
-    if ((lane & 3) == 0) scales[(size_t)row * (K / 32) + (c >> 5)] = (uint8_t)(X + 127);
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = bf16lo(v[q]);
+    f[2 * q + 1] = bf16hi(v[q]);
   }
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[q]));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
+  const int X = mxfp8_exponent(amax);
+  if (!live) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lo |= e4m3_rne_sat(__builtin_amdgcn_ldexpf(f[q], -X)) << (8 * q);
+    hi |= e4m3_rne_sat(__builtin_amdgcn_ldexpf(f[4 + q], -X)) << (8 * q);
+  }
+  *(u32x2*)(codes + 8 * i) = u32x2{lo, hi};
+  if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(X + 127);
 }
 
-// Int8 W8A8: row `row` of src (bf16, K a multiple of 8) -> int8 codes and one fp32 scale per row.
-// One wave per row: the row's largest magnitude by a wave-wide xor reduction, then f = 127 / max and
-// s = max / 127 (IEEE fp32 divisions) and code = rint(v * f) (fp32 product, ties to even), clamped
-// to +-127; the row is read a second time for the codes (it is in cache). An all-zero row gets
-// s = 0 and zero codes.
+// Int8 W8A8: row `row` of src (bf16, K a multiple of 8, at most 8192) -> int8 codes and one fp32
+// scale per row. One wave per row, which holds the row in registers (at most 16 chunks of 8 per
+// lane): the largest magnitude by a wave-wide xor reduction, then f = 127 / max and s = max / 127
+// (IEEE fp32 divisions) and code = rint(v * f) (fp32 product, ties to even), clamped to +-127. An
+// all-zero row gets s = 0 and zero codes.
+constexpr int QI8_CHUNKS = 16;
 __global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __restrict__ src, int rows, int K,
                                                               int8_t* __restrict__ codes, float* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (QTHREADS / 64) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const uint16_t* in = src + (size_t)row * K;
+  u32x4 v[QI8_CHUNKS];
   float amax = 0.f;
-  for (int c = 8 * lane; c < K; c += 512) {
-    const u32x4 v = *(const u32x4*)(in + c);
+#pragma unroll
+  for (int q = 0; q < QI8_CHUNKS; ++q) {
+    const int c = 8 * lane + 512 * q;
+    v[q] = c < K ? *(const u32x4*)(in + c) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16lo(v[i])), __builtin_fabsf(bf16hi(v[i]))));
+      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16lo(v[q][i])), __builtin_fabsf(bf16hi(v[q][i]))));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
   const float f = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
-  for (int c = 8 * lane; c < K; c += 512) {
-    const u32x4 v = *(const u32x4*)(in + c);
+#pragma unroll
+  for (int q = 0; q < QI8_CHUNKS; ++q) {
+    const int c = 8 * lane + 512 * q;
+    if (c >= K) break;
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float x = (i & 1) ? bf16hi(v[i >> 1]) : bf16lo(v[i >> 1]);
-      const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fmul_rn(x, f)), -127.f), 127.f);
-      w[i >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (i & 3));
+      const float x = (i & 1) ? bf16hi(v[q][i >> 1]) : bf16lo(v[q][i >> 1]);
+      const float r = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fmul_rn(x, f)), -127.f), 127.f);
+      w[i >> 2] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (i & 3));
     }
     *(u32x2*)(codes + (size_t)row * K + c) = u32x2{w[0], w[1]};
   }
@@ -92,7 +97,7 @@ __global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __
 }  // namespace
 
 hipError_t launch_quant_int8(const void* src, int rows, int K, int8_t* codes, float* scales, hipStream_t st) {
-  if (K % 8) return hipErrorInvalidValue;
+  if (K % 8 || K > 8 * 64 * QI8_CHUNKS) return hipErrorInvalidValue;
   const int blocks = (rows + QTHREADS / 64 - 1) / (QTHREADS / 64);
   if (blocks == 0) return hipSuccess;
   quant_int8_kernel<<<blocks, QTHREADS, 0, st>>>((const uint16_t*)src, rows, K, codes, scales);
@@ -101,9 +106,10 @@ hipError_t launch_quant_int8(const void* src, int rows, int K, int8_t* codes, fl
 
 hipError_t launch_quant_mxfp8(const void* src, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   if (K % 32) return hipErrorInvalidValue;
-  const int blocks = (rows + QTHREADS / 64 - 1) / (QTHREADS / 64);
+  const long long n8 = (long long)rows * K / 8;
+  const long long blocks = (n8 + QTHREADS - 1) / QTHREADS;
   if (blocks == 0) return hipSuccess;
-  quant_mxfp8_kernel<<<blocks, QTHREADS, 0, st>>>((const uint16_t*)src, rows, K, codes, scales);
+  quant_mxfp8_kernel<<<(unsigned)blocks, QTHREADS, 0, st>>>((const uint16_t*)src, n8, codes, scales);
   return hipGetLastError();
 }
 
