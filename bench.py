@@ -27,10 +27,16 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "int8": 5000.0}
 # kernel of known size that --calib-copy appends. Keyed by workload; an entry holds only while
 # the kernel sources it was measured on are unchanged (sha256 of those files).
 TRAFFIC = {
-    "c2": {"sha": "d19114cde11b4a36", "bytes": 3176825079},  # gate/up decode kernel
-    "c5": {"sha": "1b2179f3108af01c", "bytes": 16404419934},  # gate/up prefill kernel
+    # gate/up decode kernel
+    "c2": {"sha": "ef9a531dead2c7bb", "bytes": 3176803352},
+    # gate/up prefill kernel
+    "c5": {"sha": "1db47f5b1dfbd3e8", "bytes": 16329218211},
     # the W4A8 gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared bf16 GEMM
-    "v4p-w4a8": {"sha": "92298b6e2cc2d506", "bytes": 10134626545},
+    "v4p-w4a8": {"sha": "c50a2a9c32bb9127", "bytes": 10136001064},
+    # the hybrid gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared W8A8 MXFP8 GEMM
+    "v4p-mx": {"sha": "c50a2a9c32bb9127", "bytes": 9792253077},
+    # the int8 gate/up stage: x to int8 + Int8 W8A8 GEMM
+    "v3-int8": {"sha": "c50a2a9c32bb9127", "bytes": 17148889740},
 }
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),

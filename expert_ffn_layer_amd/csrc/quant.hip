@@ -53,22 +53,24 @@ __global__ void __launch_bounds__(QTHREADS) quant_mxfp8_kernel(const uint16_t* _
   if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(X + 127);
 }
 
-// Int8 W8A8: row `row` of src (bf16, K a multiple of 8, at most 8192) -> int8 codes and one fp32
-// scale per row. One wave per row, which holds the row in registers (at most 16 chunks of 8 per
-// lane): the largest magnitude by a wave-wide xor reduction, then f = 127 / max and s = max / 127
-// (IEEE fp32 divisions) and code = rint(v * f) (fp32 product, ties to even), clamped to +-127. An
-// all-zero row gets s = 0 and zero codes.
-constexpr int QI8_CHUNKS = 16;
+// Int8 W8A8: row `row` of src (bf16, K a multiple of 8, at most 64 * 8 * CH) -> int8 codes and one
+// fp32 scale per row. One wave per row, which holds the row in registers (CH chunks of 8 per lane,
+// the fewest that cover K, so short rows keep the occupancy up): the largest magnitude by a
+// wave-wide xor reduction, then f = 127 / max and s = max / 127 (IEEE fp32 divisions) and
+// code = rint(v * f) (fp32 product, ties to even), clamped to +-127. An all-zero row gets s = 0 and
+// zero codes.
+constexpr int QI8_MAX_CHUNKS = 16;
+template <int CH>
 __global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __restrict__ src, int rows, int K,
                                                               int8_t* __restrict__ codes, float* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (QTHREADS / 64) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const uint16_t* in = src + (size_t)row * K;
-  u32x4 v[QI8_CHUNKS];
+  u32x4 v[CH];
   float amax = 0.f;
 #pragma unroll
-  for (int q = 0; q < QI8_CHUNKS; ++q) {
+  for (int q = 0; q < CH; ++q) {
     const int c = 8 * lane + 512 * q;
     v[q] = c < K ? *(const u32x4*)(in + c) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -79,7 +81,7 @@ __global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __
   for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
   const float f = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
 #pragma unroll
-  for (int q = 0; q < QI8_CHUNKS; ++q) {
+  for (int q = 0; q < CH; ++q) {
     const int c = 8 * lane + 512 * q;
     if (c >= K) break;
     uint32_t w[2] = {0u, 0u};
@@ -97,10 +99,13 @@ __global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __
 }  // namespace
 
 hipError_t launch_quant_int8(const void* src, int rows, int K, int8_t* codes, float* scales, hipStream_t st) {
-  if (K % 8 || K > 8 * 64 * QI8_CHUNKS) return hipErrorInvalidValue;
+  if (K % 8 || K > 8 * 64 * QI8_MAX_CHUNKS) return hipErrorInvalidValue;
   const int blocks = (rows + QTHREADS / 64 - 1) / (QTHREADS / 64);
   if (blocks == 0) return hipSuccess;
-  quant_int8_kernel<<<blocks, QTHREADS, 0, st>>>((const uint16_t*)src, rows, K, codes, scales);
+  const uint16_t* s16 = (const uint16_t*)src;
+  if (K <= 512 * 4) quant_int8_kernel<4><<<blocks, QTHREADS, 0, st>>>(s16, rows, K, codes, scales);
+  else if (K <= 512 * 8) quant_int8_kernel<8><<<blocks, QTHREADS, 0, st>>>(s16, rows, K, codes, scales);
+  else quant_int8_kernel<QI8_MAX_CHUNKS><<<blocks, QTHREADS, 0, st>>>(s16, rows, K, codes, scales);
   return hipGetLastError();
 }
 
