@@ -11,13 +11,18 @@
 // is n / 256 full items plus one full or half item for the rest, which wastes no more rows than
 // 128-row tiles would.
 //
-// Both operands reach LDS by direct global -> LDS DMA (global_load_lds_dwordx4) through a
-// 3-stage ring of reduction steps, so the loads of the next stages are in flight behind two
-// steps of MFMA work and hold no registers. Each 1 KiB DMA lands in MFMA fragment order (a
-// weight packet as stored; an activation fragment gathered from 16 rows), so every LDS read is a
-// conflict-free 16-byte read at lane * 16. Weights are the A operand of
-// v_mfma_f32_16x16x32_bf16, activations the B operand; fp8 packets are converted by the wave
-// that uses them (e4m3 -> fp32 exact, times the 128 x 128 block scale, -> bf16).
+// Both operands reach LDS by direct global -> LDS DMA (global_load_lds_dwordx4) through a ring of
+// reduction steps (3 stages, or 2 where a stage is too large), so the loads of the next stages are
+// in flight behind the current steps' MFMA work and hold no registers. Each 1 KiB DMA lands in MFMA
+// fragment order (a weight packet as stored; an activation fragment gathered from 16 rows), so
+// every LDS read is a conflict-free 16-byte read. Weights are the A operand, activations the B
+// operand. Per weight format (the PCodec specialisations below):
+//   bf16, fp8, MXFP4 with bf16 activations: v_mfma_f32_16x16x32_bf16; fp8 and fp4 packets are
+//     converted by the wave that uses them (exactly, with the block scale's exponent);
+//   W4A8 and W8A8 MXFP8 with MXFP8 activations: v_mfma_scale_f32_16x16x128_f8f6f4, operands and
+//     e8m0 exponents as stored;
+//   Int8 W8A8 with int8 activations: v_mfma_i32_16x16x64_i8, exact int32 sums scaled per row and
+//     per feature after the last step.
 //
 // Items are ordered so that a run of consecutive items covers up to 8 column tiles x all full
 // row tiles of one group, and the workgroup -> item map gives each XCD a contiguous run of the

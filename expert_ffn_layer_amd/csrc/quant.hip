@@ -10,7 +10,9 @@
 //
 // Each token row of x is quantised once, in token order: codes uint8[T][K] and exponents
 // uint8[T][K/32]; the routed experts' GEMM gathers both by slot_token, as the bf16 path gathers x.
-// (The second product's input, h, is quantised in the gate/up GEMM's epilogue instead.)
+// For the MXFP8 formats the second product's input, h, is quantised in the gate/up GEMM's epilogue
+// (a 32-block is one wave's 32 columns of a row); Int8 W8A8 scales a whole row of h, which spans
+// many workgroups, so h is written in bf16 and quantised here, row by row, before down.
 #include "common.h"
 #include "kernels.h"
 
