@@ -105,12 +105,10 @@ moe_status check_shape(const moe_shape* s) {
                 "INT8 W8A8 experts run on the prefill path only: BF16 activations, I a multiple of 256, "
                 "H a multiple of 512");
   if (s->w_routed == MOE_MXFP4_B32_A8 &&
-      (s->path == MOE_PATH_DECODE ||
-       !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
+      (!prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
        !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->I, s->I, s->H)))
     return fail(MOE_ERR_UNSUPPORTED,
-                "W4A8 routed experts run on the prefill path only: BF16 activations, I a multiple of 256, "
-                "H a multiple of 512");
+                "W4A8 routed experts need BF16 activations, I a multiple of 256 and H a multiple of 512");
   if (s->path == MOE_PATH_PREFILL &&
       (!prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
        !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->I, s->I, s->H)))
@@ -272,7 +270,7 @@ bool use_prefill(const moe_shape& s) {
   const int cs = s.I_shared ? s.w_shared : s.w_routed;
   if (!prefill_supported(s.act, s.w_routed, cs, s.H, s.I, s.H) || !prefill_supported(s.act, s.w_routed, cs, s.I, s.I, s.H))
     return false;
-  if (s.path == MOE_PATH_PREFILL || s.w_routed == MOE_MXFP4_B32_A8 || s.w_routed == MOE_INT8_W8A8) return true;
+  if (s.path == MOE_PATH_PREFILL || s.w_routed == MOE_INT8_W8A8) return true;
   if (s.path == MOE_PATH_DECODE) return false;
   return (long long)s.T * s.k >= 64LL * s.E;
 }
@@ -356,9 +354,9 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.out_s = nullptr;
   const int cs = S ? s.w_shared : s.w_routed;
   const bool a8 = s.w_routed == MOE_MXFP4_B32_A8;
-  // W4A8: the routed groups multiply MXFP8 codes of x (quantised once per token, gathered like x)
-  // and write h as MXFP8 for their down product; the shared expert keeps its own launch on the
-  // bf16 rows.
+  // W4A8: the routed groups multiply MXFP8 codes of x (quantised once per token, gathered like x).
+  // On the prefill kernel they write h as MXFP8 for their down product; on the decode kernel they
+  // write it in bf16 and it is quantised before down. The shared expert keeps its own launch.
   auto launch_a8 = [&](int epi, const GroupedArgs& base, const void* codes, const void* scales, int K,
                        int rows, const int32_t* gather) {
     GroupedArgs ra = base, sa = base;
@@ -369,21 +367,35 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
     ra.act_scale = scales;
     ra.g_begin = 0;
     ra.g_end = s.E;
-    if (epi == EPI_SWIGLU) {
-      ra.out = at<void>(ws, L.hq);
-      ra.ldo = s.I;
-      ra.out_scale = at<void>(ws, L.hs);
+    hipError_t r;
+    if (prefill) {
+      if (epi == EPI_SWIGLU) {
+        ra.out = at<void>(ws, L.hq);
+        ra.ldo = s.I;
+        ra.out_scale = at<void>(ws, L.hs);
+      }
+      r = launch_w4a8_prefill(epi == EPI_SWIGLU ? EPI_SWIGLU_Q8 : epi, ra, max_rb, st);
+    } else {
+      r = launch_grouped_decode(s.act, epi, MOE_MXFP4_B32_A8, MOE_MXFP4_B32_A8, ra, max_rb, st);
     }
-    hipError_t r = launch_w4a8_prefill(epi == EPI_SWIGLU ? EPI_SWIGLU_Q8 : epi, ra, max_rb, st);
     if (r != hipSuccess || !S) return r;
     sa.g_begin = s.E;
     sa.g_end = s.E + 1;
-    if (cs != MOE_MXFP8_B32_A8) return launch_grouped_prefill(s.act, epi, cs, cs, sa, max_rb, st);
+    if (cs != MOE_MXFP8_B32_A8)
+      return prefill ? launch_grouped_prefill(s.act, epi, cs, cs, sa, max_rb, st)
+                     : launch_grouped_decode(s.act, epi, cs, cs, sa, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
     // W8A8 MXFP8 shared expert: the same MXFP8 rows of x (token t is row P + t of the group)
     // and of h, whose shared rows follow the routed ones
     sa.act = codes;
     sa.lda = K;
     sa.act_scale = scales;
+    if (!prefill) {
+      // decode kernel: h in bf16 (quantised with the routed rows before down)
+      sa.gather = epi == EPI_SWIGLU ? gather : nullptr;
+      sa.act_rows = epi == EPI_SWIGLU ? rows : P + s.T;
+      return launch_grouped_decode(s.act, epi, MOE_MXFP8_B32_A8, MOE_MXFP8_B32_A8, sa,
+                                   (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
+    }
     if (epi == EPI_SWIGLU) {
       sa.gather = gather;
       sa.act_rows = rows;
@@ -416,6 +428,13 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   }
   if (e != hipSuccess) return hip_status(e, "gate/up grouped GEMM");
   if (ev && (rs = record(ev[1], st)) != MOE_OK) return rs;
+  if (a8 && !prefill) {
+    // W4A8 on the decode kernel: the routed rows of h (bf16), and those of a W8A8 MXFP8 shared
+    // expert after them, to MXFP8 for the down product
+    const int qrows = P + (S && cs == MOE_MXFP8_B32_A8 ? s.T : 0);
+    e = launch_quant_mxfp8(at<void>(ws, L.h), qrows, s.I, at<uint8_t>(ws, L.hq), at<uint8_t>(ws, L.hs), st);
+    if (e != hipSuccess) return hip_status(e, "MXFP8 quantisation of h");
+  }
   // down: y = h Wd
   a.gather = nullptr;
   a.act = at<void>(ws, L.h);

@@ -27,6 +27,8 @@ struct Codec;
 template <>
 struct Codec<MOE_F32> {
   static constexpr int KP = 16, ACT16 = 1;  // activation 16-byte chunks per packet per lane
+  static constexpr bool A8 = false;         // MXFP8 activations on the block-scaled MFMA
+  static constexpr int WPK = 1;             // 1 KiB weight packets per reduction step
   __device__ static void mma(const u32x4& w, const u32x4* x, float, f32x4& acc) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -37,6 +39,8 @@ struct Codec<MOE_F32> {
 template <>
 struct Codec<MOE_BF16> {
   static constexpr int KP = 32, ACT16 = 1;
+  static constexpr bool A8 = false;
+  static constexpr int WPK = 1;
   __device__ static void mma(const u32x4& w, const u32x4* x, float, f32x4& acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
                                                   __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
@@ -62,6 +66,8 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1, float 
 template <>
 struct Codec<MOE_FP8_E4M3_B128> {
   static constexpr int KP = 64, ACT16 = 2;
+  static constexpr bool A8 = false;
+  static constexpr int WPK = 1;
   __device__ static void mma(const u32x4& w, const u32x4* x, float s, f32x4& acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[0], w[1], s),
                                                   __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
@@ -84,12 +90,52 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
 template <>
 struct Codec<MOE_MXFP4_B32> {
   static constexpr int KP = 128, ACT16 = 4;
+  static constexpr bool A8 = false;
+  static constexpr int WPK = 1;
   __device__ static void mma(const u32x4& w, const u32x4* x, float s, f32x4& acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16(w[i], s),
                                                     __builtin_bit_cast(bf16x8, x[i]), acc, 0, 0, 0);
   }
+};
+
+// W4A8: an MXFP4 packet is the fp4 A operand of v_mfma_scale_f32_16x16x128_f8f6f4 as stored (lane
+// (f, g): 32 codes of feature f, elements 32g .. 32g + 31, in operand dwords 0-3, with the lane's
+// e8m0 byte as its scale). The B operand is the token's MXFP8 row: lane (j, g) holds elements
+// 16g .. + 15 and 64 + 16g .. + 15 of the packet's 128 (two 16-byte chunks, 64 bytes apart), and
+// its scale byte is the exponent of (token j, block g). One MFMA per packet and row tile.
+template <>
+struct Codec<MOE_MXFP4_B32_A8> {
+  static constexpr int KP = 128, ACT16 = 2;
+  static constexpr bool A8 = true;
+  static constexpr int WPK = 1;
+  __device__ static void mma8(const u32x4* w, const u32x4* x, int sw, int sx, f32x4& acc) {
+    const i32x8 a = {(int)w[0][0], (int)w[0][1], (int)w[0][2], (int)w[0][3], 0, 0, 0, 0};
+    const i32x8 b = {(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
+                     (int)x[1][0], (int)x[1][1], (int)x[1][2], (int)x[1][3]};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, 0, sw, 0, sx);
+  }
+  __device__ static void mma(const u32x4&, const u32x4*, float, f32x4&) {}  // not reached (mma8)
+};
+
+// W8A8 MXFP8 (the shared expert of the hybrid scheme): the same instruction with fp8 A. Measured on
+// the hardware, fp8 A takes the fp8 B layout, so the step's two fp8 packets (elements 0..63 and
+// 64..127, lane (f, g) holding run 16g of each) are the operand as stored, and the packed
+// exponents (one byte per lane per packet pair, at the MXFP4 scale layout's place) its scales.
+template <>
+struct Codec<MOE_MXFP8_B32_A8> {
+  static constexpr int KP = 128, ACT16 = 2;
+  static constexpr bool A8 = true;
+  static constexpr int WPK = 2;
+  __device__ static void mma8(const u32x4* w, const u32x4* x, int sw, int sx, f32x4& acc) {
+    const i32x8 a = {(int)w[0][0], (int)w[0][1], (int)w[0][2], (int)w[0][3],
+                     (int)w[1][0], (int)w[1][1], (int)w[1][2], (int)w[1][3]};
+    const i32x8 b = {(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
+                     (int)x[1][0], (int)x[1][1], (int)x[1][2], (int)x[1][3]};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, sw, 0, sx);
+  }
+  __device__ static void mma(const u32x4&, const u32x4*, float, f32x4&) {}  // not reached (mma8)
 };
 
 // Scale of the lane's packet (nt, kt).
@@ -101,6 +147,8 @@ __device__ __forceinline__ float packet_scale(const uint8_t* sc, int N, int KT, 
   } else if (C == MOE_MXFP4_B32) {
     const uint32_t E = sc[((size_t)nt * KT + kt) * 64 + lane];
     return __uint_as_float(E << 23);
+  } else if (C == MOE_MXFP4_B32_A8 || C == MOE_MXFP8_B32_A8) {
+    return __int_as_float((int)sc[((size_t)nt * KT + kt) * 64 + lane]);  // the raw e8m0 byte
   }
   return 1.0f;
 }
@@ -115,8 +163,9 @@ struct EpiTraits {
 template <int C, int NMAT, int NF, int MT, int U>
 struct Stage {
   u32x4 x[U][MT][Codec<C>::ACT16];
-  u32x4 w[U][NMAT][NF];
+  u32x4 w[U][NMAT][NF][Codec<C>::WPK];
   float s[U][NMAT][NF];
+  int xs[U][MT];  // W4A8: the lane's activation exponent byte per packet and row tile
 };
 
 // Issue the loads of packets kt .. kt+U-1 (indices past kt1-1 re-read packet kt1-1 and are
@@ -124,28 +173,34 @@ struct Stage {
 template <int C, int ACT, int NMAT, int NF, int MT, int U>
 __device__ __forceinline__ void load_stage(Stage<C, NMAT, NF, MT, U>& st, const uint8_t* __restrict__ w0,
                                            const uint8_t* __restrict__ w1, const uint8_t* __restrict__ s0,
-                                           const uint8_t* __restrict__ s1, const uint8_t* const (&xrow)[MT], int N,
-                                           int KT, int nt0, int kt, int kt1, int lane) {
+                                           const uint8_t* __restrict__ s1, const uint8_t* const (&xrow)[MT],
+                                           const uint8_t* const (&xsrow)[MT], int N, int KT, int nt0, int kt,
+                                           int kt1, int lane) {
   using Cd = Codec<C>;
-  constexpr int AB = ACT == MOE_F32 ? 4 : 2;
+  constexpr int AB = Cd::A8 ? 1 : (ACT == MOE_F32 ? 4 : 2);
+  constexpr int CHS = Cd::A8 ? 64 : 16;  // bytes between a lane's activation chunks
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int k = min(kt + u, kt1 - 1);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const size_t off = ((size_t)(nt0 + f) * KT + k) * PACKET_BYTES + (size_t)lane * 16;
-      st.w[u][0][f] = ld_nt((const u32x4*)(w0 + off));
-      st.s[u][0][f] = packet_scale<C>(s0, N, KT, nt0 + f, k, lane);
-      if (NMAT == 2) {
-        st.w[u][NMAT - 1][f] = ld_nt((const u32x4*)(w1 + off));
-        st.s[u][NMAT - 1][f] = packet_scale<C>(s1, N, KT, nt0 + f, k, lane);
+#pragma unroll
+      for (int p = 0; p < Cd::WPK; ++p) {
+        // WPK consecutive 1 KiB packets per step (the fp8 pair of a 128-deep MXFP8 step)
+        const size_t off = (((size_t)(nt0 + f) * KT + k) * Cd::WPK + p) * PACKET_BYTES + (size_t)lane * 16;
+        st.w[u][0][f][p] = ld_nt((const u32x4*)(w0 + off));
+        if (NMAT == 2) st.w[u][NMAT - 1][f][p] = ld_nt((const u32x4*)(w1 + off));
       }
+      st.s[u][0][f] = packet_scale<C>(s0, N, KT, nt0 + f, k, lane);
+      if (NMAT == 2) st.s[u][NMAT - 1][f] = packet_scale<C>(s1, N, KT, nt0 + f, k, lane);
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int i = 0; i < Cd::ACT16; ++i)
-        st.x[u][m][i] = *(const u32x4*)(xrow[m] + (size_t)k * Cd::KP * AB + i * 16);
+        st.x[u][m][i] = *(const u32x4*)(xrow[m] + (size_t)k * Cd::KP * AB + i * CHS);
+      if constexpr (Cd::A8) st.xs[u][m] = xsrow[m][k * 4];
+    }
   }
 }
 
@@ -158,7 +213,12 @@ __device__ __forceinline__ void mma_stage(const Stage<C, NMAT, NF, MT, U>& st, f
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) Codec<C>::mma(st.w[u][m][f], st.x[u][r], st.s[u][m][f], acc[r][m][f]);
+        for (int m = 0; m < NMAT; ++m) {
+          if constexpr (Codec<C>::A8)
+            Codec<C>::mma8(st.w[u][m][f], st.x[u][r], __float_as_int(st.s[u][m][f]), st.xs[u][r], acc[r][m][f]);
+          else
+            Codec<C>::mma(st.w[u][m][f][0], st.x[u][r], st.s[u][m][f], acc[r][m][f]);
+        }
 }
 
 // The same with the weight operand of packets kt + u >= kt1 replaced by zero codes (which
@@ -167,6 +227,7 @@ template <int C, int NMAT, int NF, int MT, int U>
 __device__ __forceinline__ void mma_stage_masked(const Stage<C, NMAT, NF, MT, U>& st, int kt, int kt1,
                                                  f32x4 (&acc)[MT][NMAT][NF]) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  const u32x4 zeros[2] = {zero, zero};
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const bool valid = kt + u < kt1;
@@ -175,8 +236,13 @@ __device__ __forceinline__ void mma_stage_masked(const Stage<C, NMAT, NF, MT, U>
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-          Codec<C>::mma(valid ? st.w[u][m][f] : zero, st.x[u][r], st.s[u][m][f], acc[r][m][f]);
+        for (int m = 0; m < NMAT; ++m) {
+          if constexpr (Codec<C>::A8)
+            Codec<C>::mma8(valid ? st.w[u][m][f] : zeros, st.x[u][r], __float_as_int(st.s[u][m][f]), st.xs[u][r],
+                           acc[r][m][f]);
+          else
+            Codec<C>::mma(valid ? st.w[u][m][f][0] : zero, st.x[u][r], st.s[u][m][f], acc[r][m][f]);
+        }
   }
 }
 
@@ -199,23 +265,23 @@ constexpr int stage_depth() {
 template <int C, int ACT, int NMAT, int NF, int MT>
 __device__ __forceinline__ void wave_mma(const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
                                          const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,
-                                         const uint8_t* const (&xrow)[MT], int N, int KT, int nt0, int kt0, int kt1,
-                                         int lane, f32x4 (&acc)[MT][NMAT][NF]) {
+                                         const uint8_t* const (&xrow)[MT], const uint8_t* const (&xsrow)[MT], int N,
+                                         int KT, int nt0, int kt0, int kt1, int lane, f32x4 (&acc)[MT][NMAT][NF]) {
   constexpr int U = stage_depth<C, NMAT, NF, MT>();
   if (kt0 >= kt1) return;
   Stage<C, NMAT, NF, MT, U> A, B;
-  load_stage<C, ACT, NMAT, NF, MT, U>(A, w0, w1, s0, s1, xrow, N, KT, nt0, kt0, kt1, lane);
+  load_stage<C, ACT, NMAT, NF, MT, U>(A, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt0, kt1, lane);
   int kt = kt0;
   // steady state: both stages entirely inside the range, so every load and MFMA is
   // unconditional and the wait counts stay exact (the next stage's loads remain in flight)
   for (; kt + 2 * U < kt1; kt += 2 * U) {
-    load_stage<C, ACT, NMAT, NF, MT, U>(B, w0, w1, s0, s1, xrow, N, KT, nt0, kt + U, kt1, lane);
+    load_stage<C, ACT, NMAT, NF, MT, U>(B, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + U, kt1, lane);
     mma_stage(A, acc);
-    load_stage<C, ACT, NMAT, NF, MT, U>(A, w0, w1, s0, s1, xrow, N, KT, nt0, kt + 2 * U, kt1, lane);
+    load_stage<C, ACT, NMAT, NF, MT, U>(A, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + 2 * U, kt1, lane);
     mma_stage(B, acc);
   }
   // remainder (1 .. 2U packets), branch-free: packets past the range are masked to zero
-  load_stage<C, ACT, NMAT, NF, MT, U>(B, w0, w1, s0, s1, xrow, N, KT, nt0, kt + U, kt1, lane);
+  load_stage<C, ACT, NMAT, NF, MT, U>(B, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + U, kt1, lane);
   mma_stage_masked(A, kt, kt1, acc);
   mma_stage_masked(B, kt + U, kt1, acc);
 }
@@ -255,13 +321,21 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
   const int rl = lane & 15;
   constexpr int AB = ACT == MOE_F32 ? 4 : 2;
   const uint8_t* xrow[MT];
+  const uint8_t* xsrow[MT];  // W4A8: the row's exponent of block (lane / 16) of packet 0
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int rr = 16 * m + rl;
     const int r = rr < wnr ? wrow0 + rr : row0;
     int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
     if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
-    xrow[m] = (const uint8_t*)a.act + ((size_t)src * a.lda + (lane >> 4) * (KP / 4)) * AB;
+    if constexpr (Codec<C>::A8) {
+      // MXFP8 rows of K bytes: the lane's chunks start at byte 16 (lane / 16) of each packet's 128
+      xrow[m] = (const uint8_t*)a.act + (size_t)src * a.lda + 16 * (lane >> 4);
+      xsrow[m] = (const uint8_t*)a.act_scale + (size_t)src * (a.K / 32) + (lane >> 4);
+    } else {
+      xrow[m] = (const uint8_t*)a.act + ((size_t)src * a.lda + (lane >> 4) * (KP / 4)) * AB;
+      xsrow[m] = nullptr;
+    }
   }
 
   f32x4 acc[MT][NMAT][NF];
@@ -272,7 +346,7 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[r][m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (wnr > 0) wave_mma<C, ACT, NMAT, NF, MT>(w0, w1, s0, s1, xrow, a.N, KT, nt0, kt0, kt1, lane, acc);
+  if (wnr > 0) wave_mma<C, ACT, NMAT, NF, MT>(w0, w1, s0, s1, xrow, xsrow, a.N, KT, nt0, kt0, kt1, lane, acc);
 
   // fixed-order reduction of the KS reduction parts, one row tile per round
   if constexpr (KS > 1) {
@@ -373,7 +447,13 @@ template <int CR, int CS, int ACT, int EPI, int NF>
 __global__ void __launch_bounds__(256) grouped_decode_kernel(GroupedArgs a) {
   constexpr int NMAT = EpiTraits<EPI>::NMAT;
   __shared__ float red[3 * NMAT * NF * 4 * 64];
-  const int rbi = blockIdx.x / a.NTW, ntw = blockIdx.x % a.NTW;
+  int rbi = blockIdx.x / a.NTW;
+  const int ntw = blockIdx.x % a.NTW;
+  if (a.cum_blocks && a.g_end > a.g_begin) {
+    // a launch over groups [g_begin, g_end) only: its row blocks follow those of earlier groups
+    rbi += a.cum_blocks[a.g_begin];
+    if (rbi >= a.cum_blocks[a.g_end]) return;
+  }
   int g = 0, blk = rbi;
   if (a.cum_blocks) {
     if (rbi >= a.cum_blocks[a.G]) return;
@@ -452,6 +532,8 @@ static hipError_t launch_codecs(int cr, int cs, int nf, const GroupedArgs& a, in
     MOE_CASE(MOE_MXFP4_B32, MOE_BF16)
     MOE_CASE(MOE_MXFP4_B32, MOE_FP8_E4M3_B128)
     MOE_CASE(MOE_MXFP4_B32, MOE_MXFP4_B32)
+    MOE_CASE(MOE_MXFP4_B32_A8, MOE_MXFP4_B32_A8)  // the routed groups of a W4A8 layer
+    MOE_CASE(MOE_MXFP8_B32_A8, MOE_MXFP8_B32_A8)  // its W8A8 MXFP8 shared expert
   }
 #undef MOE_CASE
   return hipErrorInvalidValue;

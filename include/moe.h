@@ -62,14 +62,16 @@ typedef enum {
                              MXFP8 (E4M3FN codes, round to nearest even, saturating at 448, with
                              one e8m0 exponent floor(log2 max|v|) - 8 per 32 reduction elements)
                              and multiplied by the block-scaled fp4 x fp8 matrix instruction.
-                             Only as w_routed, with BF16 activations, on the prefill path. */
+                             Only as w_routed, with BF16 activations, I a multiple of 256 and H of
+                             512; on either path (thin batches take the decode kernel). */
   MOE_MXFP8_B32_A8 = 5,   /* W8A8 MXFP8 shared expert of the hybrid MXFP8-MXFP4 scheme (same
                              passage: the shared expert's linear layers run W8A8, weights and
                              activations both MXFP8). Weights: OCP E4M3FN codes + one e8m0
                              exponent per 32 reduction elements, w = e4m3(c) * 2^(E-127). The
                              activations are quantised to MXFP8 as for MOE_MXFP4_B32_A8 and both
                              operands go to the block-scaled fp8 x fp8 matrix instruction. Only
-                             as w_shared, with w_routed = MOE_MXFP4_B32_A8. */
+                             as w_shared, with w_routed = MOE_MXFP4_B32_A8; it runs on the prefill
+                             kernel on either path. */
   MOE_INT8_W8A8 = 6       /* Int8 W8A8 experts (same page, Int8 quantisation strategy: the routed
                              and shared experts' linear layers run W8A8, weights statically
                              quantised per output channel, activations dynamically per token).
@@ -89,7 +91,7 @@ typedef enum {
   MOE_PATH_PREFILL = 2    /* LDS-tiled MFMA grouped GEMM (many rows per expert): BF16
                              activations, BF16 / FP8 / MXFP4 / W4A8 / W8A8 MXFP8 / INT8 weights, I
                              a multiple of 256, H a multiple of 512; MOE_ERR_UNSUPPORTED otherwise.
-                             W4A8 and INT8 routed experts always take this path (AUTO included). */
+                             INT8 experts always take this path (AUTO included). */
 } moe_path;
 
 typedef struct {

@@ -99,13 +99,17 @@ CONFIGS = {
 # prefill batch (T * k = 64 E, where the path switches to the MFMA kernel), with MXFP4 routed
 # experts and bf16 activations, with W4A8 routed experts (activations quantised to MXFP8), and in
 # the hybrid MXFP8-MXFP4 scheme: W4A8 routed experts and a W8A8 MXFP8 shared expert. The
-# DeepSeek-V3-shaped prefill layer with Int8 W8A8 routed and shared experts.
+# DeepSeek-V3-shaped prefill layer with Int8 W8A8 routed and shared experts. The V4-Pro decode layer
+# (T = 32) with W4A8 routed experts, and in the hybrid scheme.
 EXTRA = {
     "v4p": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096),
     "v4p-w4a8": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-w4a8", T=4096, w_routed="mxfp4a8"),
     "v4p-mx": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-hybrid-mxfp8-mxfp4", T=4096,
                                     w_routed="mxfp4a8", w_shared="mxfp8a8"),
     "v3-int8": CONFIGS["c5"].replace(name="deepseek-v3-moe-prefill-int8-w8a8", w_routed="int8", w_shared="int8"),
+    "c4-w4a8": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-decode-w4a8", w_routed="mxfp4a8"),
+    "c4-mx": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-decode-hybrid-mxfp8-mxfp4", w_routed="mxfp4a8",
+                                   w_shared="mxfp8a8"),
 }
 
 

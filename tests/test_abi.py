@@ -47,15 +47,13 @@ def _shape(**kw):
     (dict(T=-1), 1), (dict(H=100), 1), (dict(I=64), 1), (dict(E=0), 1), (dict(E=2000), 1),
     (dict(k=0), 1), (dict(k=9), 1), (dict(E=32, k=17), 1), (dict(I_shared=256), 2),
     (dict(act="fp8"), 1), (dict(act="f32"), 2), (dict(w_routed="f32"), 2),
-    # W4A8: routed experts only, prefill only (bf16 activations, I % 256, H % 512)
+    # W4A8: routed experts only (bf16 activations, I % 256, H % 512)
     (dict(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="mxfp4a8"), 2),
-    (dict(H=512, I=256, w_routed="mxfp4a8", path="decode"), 2),
     (dict(H=512, I=128, w_routed="mxfp4a8"), 2), (dict(H=256, I=256, w_routed="mxfp4a8"), 2),
     # W8A8 MXFP8: the shared expert only, beside W4A8 routed experts
     (dict(H=512, I=256, w_routed="mxfp8a8"), 2),
     (dict(H=512, I=256, I_shared=256, w_routed="bf16", w_shared="mxfp8a8"), 2),
     (dict(H=512, I=256, I_shared=256, w_routed="mxfp4", w_shared="mxfp8a8"), 2),
-    (dict(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="mxfp8a8", path="decode"), 2),
     (dict(act="f32", w_routed="f32", I_shared=128, w_shared="mxfp8a8"), 2),
     # Int8 W8A8: routed and shared both INT8 (or no shared expert), prefill only
     (dict(H=512, I=256, I_shared=256, w_routed="int8", w_shared="bf16"), 2),
@@ -74,6 +72,14 @@ def test_w4a8_shape_is_accepted_and_adds_quantised_activations():
     a8 = N.moe_workspace_size(_shape(H=512, I=256, w_routed="mxfp4a8"))
     assert a8 > base
     assert N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="bf16")) > a8
+
+
+def test_w4a8_accepts_both_paths():
+    for path in ("decode", "prefill", "auto"):
+        assert N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="bf16",
+                                           path=path)) > 0
+        assert N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="mxfp4a8", w_shared="mxfp8a8",
+                                           path=path)) > 0
 
 
 def test_hybrid_shape_is_accepted_and_quantises_the_shared_rows_of_h():

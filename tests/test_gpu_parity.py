@@ -175,8 +175,8 @@ def _prefill_ok(spec):
 def test_layer_small(name, spec, path):
     if path == "prefill" and not _prefill_ok(spec):
         pytest.skip("the prefill kernel takes bf16 activations, I % 256 == 0 and H % 512 == 0")
-    if path == "decode" and spec.w_routed in ("mxfp4a8", "int8"):
-        pytest.skip("W4A8 and Int8 W8A8 experts run on the prefill path only (the decode path is refused)")
+    if path == "decode" and spec.w_routed == "int8":
+        pytest.skip("Int8 W8A8 experts run on the prefill path only (the decode path is refused)")
     say("layer", name, path, spec)
     lay, pl = build(spec, DEV, path)
     y, idx, w = run(spec, lay, pl)
@@ -291,7 +291,7 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
 # kernel, the bf16 shared expert in a launch of its own; the same layer with W4A8 routed experts
 # (MXFP8 activations on the block-scaled MFMA); and the hybrid MXFP8-MXFP4 layer (W4A8 routed, W8A8
 # MXFP8 shared); the DeepSeek-V3-shaped prefill layer with Int8 W8A8 experts
-FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8"]
+FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8", "c4-w4a8", "c4-mx"]
 
 
 @pytest.mark.slow
@@ -362,10 +362,8 @@ SWEEP = _sweep_specs()
 def test_layer_random_sweep(spec):
     """Every random layer on the automatic path, and on both explicit paths where the shape allows
     them: routing identical to the oracle's, outputs within the format's bound."""
-    paths = ["auto"]
-    if spec.w_routed != "mxfp4a8":
-        paths.append("decode")
-    if _prefill_ok(spec) and spec.w_routed != "mxfp4a8":
+    paths = ["auto", "decode"]
+    if _prefill_ok(spec):
         paths.append("prefill")
     if spec.w_routed == "mxfp4a8" and not _prefill_ok(spec):
         pytest.skip("W4A8 needs the prefill shape constraints")
@@ -414,16 +412,20 @@ def test_layer_random_sweep_quantised(spec):
     """Each random quantised layer on its (prefill) path: routing identical to the oracle's, outputs
     within the bound, and a second call bit-identical."""
     say("sweep-q", spec)
-    lay, pl = build(spec, DEV)
-    y, idx, w = run(spec, lay, pl)
-    ref = oracle_full(spec, lay)
-    assert np.array_equal(idx.cpu().numpy(), ref["topk_idx"])
-    assert np.max(np.abs(w.cpu().numpy() - ref["topk_w"])) <= 1e-5
-    err = rel_fro(to_f64(y), ref["y"])
-    say("  rel. Frobenius error %.3e (bound %.0e)" % (err, tol_of(spec)))
-    assert err <= tol_of(spec)
-    y2, _, _ = run(spec, lay, pl)
-    assert torch.equal(y, y2)
+    ref = None
+    # W4A8 layers run on both kernels (the decode one at thin batches); Int8 on the prefill one
+    for path in (["auto", "decode", "prefill"] if spec.w_routed == "mxfp4a8" else ["auto"]):
+        lay, pl = build(spec, DEV, path)
+        y, idx, w = run(spec, lay, pl)
+        if ref is None:
+            ref = oracle_full(spec, lay)
+        assert np.array_equal(idx.cpu().numpy(), ref["topk_idx"])
+        assert np.max(np.abs(w.cpu().numpy() - ref["topk_w"])) <= 1e-5
+        err = rel_fro(to_f64(y), ref["y"])
+        say("  %s: rel. Frobenius error %.3e (bound %.0e)" % (path, err, tol_of(spec)))
+        assert err <= tol_of(spec)
+        y2, _, _ = run(spec, lay, pl)
+        assert torch.equal(y, y2)
 
 
 # ------------------------------------------------------------------ hash routing
