@@ -69,7 +69,7 @@ def measured_traffic(config: str, path: str):
 
 # bounded CPU-oracle samples (tokens): about 10-30 s of oracle work per config
 CPU_TOKENS = {"c1": 16, "c2": 64, "c3": 12, "c4": 32, "c5": 4, "v4p": 6, "v4p-w4a8": 6, "v4p-mx": 6, "v3-int8": 4,
-              "c4-w4a8": 32, "c4-mx": 32}
+              "c4-w4a8": 32, "c4-mx": 32, "c3-int8": 12}
 
 
 def log(*a):
@@ -82,11 +82,12 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8", "c4-w4a8", "c4-mx"],
+                    choices=["c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8", "c4-w4a8", "c4-mx", "c3-int8"],
                     help="c1-c5: the layer configurations; v4p, v4p-w4a8, v4p-mx: the V4-Pro-shaped layer at a "
                          "prefill batch with MXFP4 / W4A8 routed experts, and in the hybrid MXFP8-MXFP4 scheme "
                          "(W4A8 routed, W8A8 MXFP8 shared); v3-int8: the c5 layer with Int8 W8A8 experts; "
-                         "c4-w4a8, c4-mx: the c4 decode layer with W4A8 routed experts, and hybrid")
+                         "c4-w4a8, c4-mx: the c4 decode layer with W4A8 routed experts, and hybrid; c3-int8: the c3 "
+                         "decode layer with Int8 W8A8 experts")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=None)

@@ -99,11 +99,10 @@ moe_status check_shape(const moe_shape* s) {
   if ((ri8 && s->I_shared && !si8) || (si8 && !ri8))
     return fail(MOE_ERR_UNSUPPORTED, "INT8 W8A8 experts: routed and shared both INT8 (or no shared expert)");
   if (s->w_routed == MOE_INT8_W8A8 &&
-      (s->path == MOE_PATH_DECODE || !prefill_supported(s->act, s->w_routed, s->w_routed, s->H, s->I, s->H) ||
+      (!prefill_supported(s->act, s->w_routed, s->w_routed, s->H, s->I, s->H) ||
        !prefill_supported(s->act, s->w_routed, s->w_routed, s->I, s->I, s->H)))
     return fail(MOE_ERR_UNSUPPORTED,
-                "INT8 W8A8 experts run on the prefill path only: BF16 activations, I a multiple of 256, "
-                "H a multiple of 512");
+                "INT8 W8A8 experts need BF16 activations, I a multiple of 256 and H a multiple of 512");
   if (s->w_routed == MOE_MXFP4_B32_A8 &&
       (!prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->H, s->I, s->H) ||
        !prefill_supported(s->act, s->w_routed, s->I_shared ? s->w_shared : s->w_routed, s->I, s->I, s->H)))
@@ -270,7 +269,7 @@ bool use_prefill(const moe_shape& s) {
   const int cs = s.I_shared ? s.w_shared : s.w_routed;
   if (!prefill_supported(s.act, s.w_routed, cs, s.H, s.I, s.H) || !prefill_supported(s.act, s.w_routed, cs, s.I, s.I, s.H))
     return false;
-  if (s.path == MOE_PATH_PREFILL || s.w_routed == MOE_INT8_W8A8) return true;
+  if (s.path == MOE_PATH_PREFILL) return true;
   if (s.path == MOE_PATH_DECODE) return false;
   return (long long)s.T * s.k >= 64LL * s.E;
 }
@@ -421,7 +420,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
     GroupedArgs ia = a;
     ia.act = at<void>(ws, L.xq);
     ia.act_scale = at<void>(ws, L.xs);
-    e = launch_int8_prefill(EPI_SWIGLU, ia, max_rb, st);
+    e = prefill ? launch_int8_prefill(EPI_SWIGLU, ia, max_rb, st)
+                : launch_grouped_decode(s.act, EPI_SWIGLU, MOE_INT8_W8A8, MOE_INT8_W8A8, ia, max_rb, st);
   } else {
     e = prefill ? launch_grouped_prefill(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st)
                 : launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
@@ -466,7 +466,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
     GroupedArgs ia = a;
     ia.act = at<void>(ws, L.hq);
     ia.act_scale = at<void>(ws, L.hs);
-    e = launch_int8_prefill(EPI_PLAIN, ia, max_rb, st);
+    e = prefill ? launch_int8_prefill(EPI_PLAIN, ia, max_rb, st)
+                : launch_grouped_decode(s.act, EPI_PLAIN, MOE_INT8_W8A8, MOE_INT8_W8A8, ia, max_rb, st);
   } else {
     e = prefill ? launch_grouped_prefill(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st)
                 : launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);

@@ -29,6 +29,7 @@ struct Codec<MOE_F32> {
   static constexpr int KP = 16, ACT16 = 1;  // activation 16-byte chunks per packet per lane
   static constexpr bool A8 = false;         // MXFP8 activations on the block-scaled MFMA
   static constexpr int WPK = 1;             // 1 KiB weight packets per reduction step
+  static constexpr bool I8 = false;         // int8 x int8 with int32 sums, scaled per row and feature
   __device__ static void mma(const u32x4& w, const u32x4* x, float, f32x4& acc) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -41,6 +42,7 @@ struct Codec<MOE_BF16> {
   static constexpr int KP = 32, ACT16 = 1;
   static constexpr bool A8 = false;
   static constexpr int WPK = 1;
+  static constexpr bool I8 = false;
   __device__ static void mma(const u32x4& w, const u32x4* x, float, f32x4& acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
                                                   __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
@@ -68,6 +70,7 @@ struct Codec<MOE_FP8_E4M3_B128> {
   static constexpr int KP = 64, ACT16 = 2;
   static constexpr bool A8 = false;
   static constexpr int WPK = 1;
+  static constexpr bool I8 = false;
   __device__ static void mma(const u32x4& w, const u32x4* x, float s, f32x4& acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[0], w[1], s),
                                                   __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
@@ -92,6 +95,7 @@ struct Codec<MOE_MXFP4_B32> {
   static constexpr int KP = 128, ACT16 = 4;
   static constexpr bool A8 = false;
   static constexpr int WPK = 1;
+  static constexpr bool I8 = false;
   __device__ static void mma(const u32x4& w, const u32x4* x, float s, f32x4& acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -110,6 +114,7 @@ struct Codec<MOE_MXFP4_B32_A8> {
   static constexpr int KP = 128, ACT16 = 2;
   static constexpr bool A8 = true;
   static constexpr int WPK = 1;
+  static constexpr bool I8 = false;
   __device__ static void mma8(const u32x4* w, const u32x4* x, int sw, int sx, f32x4& acc) {
     const i32x8 a = {(int)w[0][0], (int)w[0][1], (int)w[0][2], (int)w[0][3], 0, 0, 0, 0};
     const i32x8 b = {(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
@@ -128,6 +133,7 @@ struct Codec<MOE_MXFP8_B32_A8> {
   static constexpr int KP = 128, ACT16 = 2;
   static constexpr bool A8 = true;
   static constexpr int WPK = 2;
+  static constexpr bool I8 = false;
   __device__ static void mma8(const u32x4* w, const u32x4* x, int sw, int sx, f32x4& acc) {
     const i32x8 a = {(int)w[0][0], (int)w[0][1], (int)w[0][2], (int)w[0][3],
                      (int)w[1][0], (int)w[1][1], (int)w[1][2], (int)w[1][3]};
@@ -136,6 +142,24 @@ struct Codec<MOE_MXFP8_B32_A8> {
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, sw, 0, sx);
   }
   __device__ static void mma(const u32x4&, const u32x4*, float, f32x4&) {}  // not reached (mma8)
+};
+
+// Int8 W8A8: an int8 packet (16 features x 64, laid out as an fp8 packet) and the gathered int8 token
+// rows (lane (j, g): 16 bytes of token j, run 16g of the packet's 64) go to v_mfma_i32_16x16x64_i8,
+// whose A and B operands share that lane layout, so the codes' products add exactly in int32. The
+// sums are scaled by the row's activation scale and the feature's weight scale after the wave's
+// reduction range, before the partial sums of the waves are added.
+template <>
+struct Codec<MOE_INT8_W8A8> {
+  static constexpr int KP = 64, ACT16 = 1;
+  static constexpr bool A8 = false;
+  static constexpr int WPK = 1;
+  static constexpr bool I8 = true;
+  __device__ static void mma(const u32x4& w, const u32x4* x, float, f32x4& acc) {
+    acc = __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, w),
+                                                                          __builtin_bit_cast(i32x4, x[0]),
+                                                                          __builtin_bit_cast(i32x4, acc), 0, 0, 0));
+  }
 };
 
 // Scale of the lane's packet (nt, kt).
@@ -177,7 +201,7 @@ __device__ __forceinline__ void load_stage(Stage<C, NMAT, NF, MT, U>& st, const 
                                            const uint8_t* const (&xsrow)[MT], int N, int KT, int nt0, int kt,
                                            int kt1, int lane) {
   using Cd = Codec<C>;
-  constexpr int AB = Cd::A8 ? 1 : (ACT == MOE_F32 ? 4 : 2);
+  constexpr int AB = (Cd::A8 || Cd::I8) ? 1 : (ACT == MOE_F32 ? 4 : 2);
   constexpr int CHS = Cd::A8 ? 64 : 16;  // bytes between a lane's activation chunks
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -322,13 +346,19 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
   constexpr int AB = ACT == MOE_F32 ? 4 : 2;
   const uint8_t* xrow[MT];
   const uint8_t* xsrow[MT];  // W4A8: the row's exponent of block (lane / 16) of packet 0
+  int srcs[MT];              // Int8: the activation row of each row tile (its scale index)
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int rr = 16 * m + rl;
     const int r = rr < wnr ? wrow0 + rr : row0;
     int src = a.gather ? (r < a.P ? a.gather[r] : r - a.P) : r;
     if ((unsigned)src >= (unsigned)a.act_rows) src = 0;
-    if constexpr (Codec<C>::A8) {
+    srcs[m] = src;
+    if constexpr (Codec<C>::I8) {
+      // int8 rows of K bytes: the lane's chunk starts at byte 16 (lane / 16) of each 64-byte packet
+      xrow[m] = (const uint8_t*)a.act + (size_t)src * a.lda + 16 * (lane >> 4);
+      xsrow[m] = nullptr;
+    } else if constexpr (Codec<C>::A8) {
       // MXFP8 rows of K bytes: the lane's chunks start at byte 16 (lane / 16) of each packet's 128
       xrow[m] = (const uint8_t*)a.act + (size_t)src * a.lda + 16 * (lane >> 4);
       xsrow[m] = (const uint8_t*)a.act_scale + (size_t)src * (a.K / 32) + (lane >> 4);
@@ -347,6 +377,28 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
       for (int f = 0; f < NF; ++f) acc[r][m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (wnr > 0) wave_mma<C, ACT, NMAT, NF, MT>(w0, w1, s0, s1, xrow, xsrow, a.N, KT, nt0, kt0, kt1, lane, acc);
+
+  if constexpr (Codec<C>::I8) {
+    // int32 sums -> fp32 times the row's activation scale and the feature's weight scale (features
+    // (nt0 + f) * 16 + 4 (lane / 16) + i of token row 16 r + lane % 16); the whole register
+    // vector is reinterpreted (a bit cast of one vector element reads element 0)
+    const float* asc = (const float*)a.act_scale;
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+      const float rs = asc[srcs[r]];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const f32x4 cs = *(const f32x4*)((const float*)(m == 0 ? s0 : s1) + (nt0 + f) * 16 + 4 * (lane >> 4));
+          const i32x4 iv = __builtin_bit_cast(i32x4, acc[r][m][f]);
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = (float)iv[i] * rs * cs[i];
+          acc[r][m][f] = v;
+        }
+    }
+  }
 
   // fixed-order reduction of the KS reduction parts, one row tile per round
   if constexpr (KS > 1) {
@@ -534,6 +586,7 @@ static hipError_t launch_codecs(int cr, int cs, int nf, const GroupedArgs& a, in
     MOE_CASE(MOE_MXFP4_B32, MOE_MXFP4_B32)
     MOE_CASE(MOE_MXFP4_B32_A8, MOE_MXFP4_B32_A8)  // the routed groups of a W4A8 layer
     MOE_CASE(MOE_MXFP8_B32_A8, MOE_MXFP8_B32_A8)  // its W8A8 MXFP8 shared expert
+    MOE_CASE(MOE_INT8_W8A8, MOE_INT8_W8A8)
   }
 #undef MOE_CASE
   return hipErrorInvalidValue;

@@ -57,7 +57,7 @@ struct GroupedArgs {
 // per-item setup and reduction stay negligible.
 inline int decode_nf(int codec, int epi, int K, int N) {
   if (epi == EPI_F32) return 1;
-  const double bpw = codec == 0 ? 4.0 : codec == 1 ? 2.0 : (codec == 2 || codec == 5) ? 1.03125 : 0.53125;
+  const double bpw = codec == 0 ? 4.0 : codec == 1 ? 2.0 : (codec == 2 || codec == 5 || codec == 6) ? 1.03125 : 0.53125;
   const int nmat = epi == EPI_SWIGLU ? 2 : 1;
   // converted formats (fp8, MXFP4) stop at 4 tiles for the plain epilogue: their conversion
   // temporaries make 8 tiles cost a wave of occupancy per SIMD, which streams slower

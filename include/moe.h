@@ -70,8 +70,7 @@ typedef enum {
                              exponent per 32 reduction elements, w = e4m3(c) * 2^(E-127). The
                              activations are quantised to MXFP8 as for MOE_MXFP4_B32_A8 and both
                              operands go to the block-scaled fp8 x fp8 matrix instruction. Only
-                             as w_shared, with w_routed = MOE_MXFP4_B32_A8; it runs on the prefill
-                             kernel on either path. */
+                             as w_shared, with w_routed = MOE_MXFP4_B32_A8; on either path. */
   MOE_INT8_W8A8 = 6       /* Int8 W8A8 experts (same page, Int8 quantisation strategy: the routed
                              and shared experts' linear layers run W8A8, weights statically
                              quantised per output channel, activations dynamically per token).
@@ -81,7 +80,7 @@ typedef enum {
                              clamped to +-127); an all-zero row has s = 0. The products accumulate
                              the codes exactly in int32 on the int8 matrix instruction, then scale
                              by s_row * s[n]. As w_routed, with no shared expert or an INT8 one;
-                             BF16 activations; on the prefill path. */
+                             BF16 activations, I a multiple of 256 and H of 512; on either path. */
 } moe_dtype;
 
 typedef enum {
@@ -91,7 +90,7 @@ typedef enum {
   MOE_PATH_PREFILL = 2    /* LDS-tiled MFMA grouped GEMM (many rows per expert): BF16
                              activations, BF16 / FP8 / MXFP4 / W4A8 / W8A8 MXFP8 / INT8 weights, I
                              a multiple of 256, H a multiple of 512; MOE_ERR_UNSUPPORTED otherwise.
-                             INT8 experts always take this path (AUTO included). */
+                             */
 } moe_path;
 
 typedef struct {

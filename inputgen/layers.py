@@ -100,7 +100,8 @@ CONFIGS = {
 # experts and bf16 activations, with W4A8 routed experts (activations quantised to MXFP8), and in
 # the hybrid MXFP8-MXFP4 scheme: W4A8 routed experts and a W8A8 MXFP8 shared expert. The
 # DeepSeek-V3-shaped prefill layer with Int8 W8A8 routed and shared experts. The V4-Pro decode layer
-# (T = 32) with W4A8 routed experts, and in the hybrid scheme.
+# (T = 32) with W4A8 routed experts, and in the hybrid scheme; the DeepSeek-V3 decode layer with Int8
+# W8A8 experts.
 EXTRA = {
     "v4p": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-mxfp4", T=4096),
     "v4p-w4a8": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-prefill-w4a8", T=4096, w_routed="mxfp4a8"),
@@ -110,6 +111,7 @@ EXTRA = {
     "c4-w4a8": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-decode-w4a8", w_routed="mxfp4a8"),
     "c4-mx": CONFIGS["c4"].replace(name="deepseek-v4-pro-moe-decode-hybrid-mxfp8-mxfp4", w_routed="mxfp4a8",
                                    w_shared="mxfp8a8"),
+    "c3-int8": CONFIGS["c3"].replace(name="deepseek-v3-moe-decode-int8-w8a8", w_routed="int8", w_shared="int8"),
 }
 
 

@@ -55,10 +55,9 @@ def _shape(**kw):
     (dict(H=512, I=256, I_shared=256, w_routed="bf16", w_shared="mxfp8a8"), 2),
     (dict(H=512, I=256, I_shared=256, w_routed="mxfp4", w_shared="mxfp8a8"), 2),
     (dict(act="f32", w_routed="f32", I_shared=128, w_shared="mxfp8a8"), 2),
-    # Int8 W8A8: routed and shared both INT8 (or no shared expert), prefill only
+    # Int8 W8A8: routed and shared both INT8 (or no shared expert)
     (dict(H=512, I=256, I_shared=256, w_routed="int8", w_shared="bf16"), 2),
     (dict(H=512, I=256, I_shared=256, w_routed="bf16", w_shared="int8"), 2),
-    (dict(H=512, I=256, w_routed="int8", path="decode"), 2),
     (dict(H=256, I=256, w_routed="int8"), 2),
 ])
 def test_shape_validation(kw, status):

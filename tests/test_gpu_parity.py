@@ -175,8 +175,6 @@ def _prefill_ok(spec):
 def test_layer_small(name, spec, path):
     if path == "prefill" and not _prefill_ok(spec):
         pytest.skip("the prefill kernel takes bf16 activations, I % 256 == 0 and H % 512 == 0")
-    if path == "decode" and spec.w_routed == "int8":
-        pytest.skip("Int8 W8A8 experts run on the prefill path only (the decode path is refused)")
     say("layer", name, path, spec)
     lay, pl = build(spec, DEV, path)
     y, idx, w = run(spec, lay, pl)
@@ -291,7 +289,7 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
 # kernel, the bf16 shared expert in a launch of its own; the same layer with W4A8 routed experts
 # (MXFP8 activations on the block-scaled MFMA); and the hybrid MXFP8-MXFP4 layer (W4A8 routed, W8A8
 # MXFP8 shared); the DeepSeek-V3-shaped prefill layer with Int8 W8A8 experts
-FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8", "c4-w4a8", "c4-mx"]
+FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8", "c4-w4a8", "c4-mx", "c3-int8"]
 
 
 @pytest.mark.slow
@@ -413,8 +411,8 @@ def test_layer_random_sweep_quantised(spec):
     within the bound, and a second call bit-identical."""
     say("sweep-q", spec)
     ref = None
-    # W4A8 layers run on both kernels (the decode one at thin batches); Int8 on the prefill one
-    for path in (["auto", "decode", "prefill"] if spec.w_routed == "mxfp4a8" else ["auto"]):
+    # each layer on both kernels (the automatic choice, then each one explicitly)
+    for path in ("auto", "decode", "prefill"):
         lay, pl = build(spec, DEV, path)
         y, idx, w = run(spec, lay, pl)
         if ref is None:
