@@ -28,15 +28,15 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "int8": 5000.0}
 # the kernel sources it was measured on are unchanged (sha256 of those files).
 TRAFFIC = {
     # gate/up decode kernel
-    "c2": {"sha": "26a8b501fdc3a48e", "bytes": 3176803352},
+    "c2": {"sha": "24c0fd2cc318dc45", "bytes": 3176791832},
     # gate/up prefill kernel
-    "c5": {"sha": "f7033a8b3c3e918e", "bytes": 16329218211},
+    "c5": {"sha": "e0463fd1be82c895", "bytes": 16306116370},
     # the W4A8 gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared bf16 GEMM
-    "v4p-w4a8": {"sha": "d4f86ea008d23925", "bytes": 10136001064},
+    "v4p-w4a8": {"sha": "f0710d12f35a6620", "bytes": 10135443620},
     # the hybrid gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared W8A8 MXFP8 GEMM
-    "v4p-mx": {"sha": "d4f86ea008d23925", "bytes": 9792253077},
+    "v4p-mx": {"sha": "f0710d12f35a6620", "bytes": 9792367135},
     # the int8 gate/up stage: x to int8 + Int8 W8A8 GEMM
-    "v3-int8": {"sha": "d4f86ea008d23925", "bytes": 17148889740},
+    "v3-int8": {"sha": "f0710d12f35a6620", "bytes": 17220118025},
 }
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
