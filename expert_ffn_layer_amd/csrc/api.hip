@@ -296,6 +296,110 @@ moe_status record(hipEvent_t ev, hipStream_t st) {
 }
 
 // ev (optional, 3 events): recorded after the plan, after gate/up and after down.
+// The launches of one FFN pass (gate/up, then down) on the kernel family the shape selects; the
+// per-format rules for the activation operand live here, the argument set-up in do_ffn.
+struct FfnPass {
+  const moe_shape& s;
+  void* ws;
+  const Ws& L;
+  hipStream_t st;
+  bool prefill;
+  int P, S;
+  int cs;      // the shared expert's format (the routed one when there is none)
+  int max_rb;  // row blocks the launch grid covers
+
+  // bf16 activations: one launch over the routed and shared groups
+  hipError_t plain(int epi, const GroupedArgs& a) const {
+    return prefill ? launch_grouped_prefill(s.act, epi, s.w_routed, cs, a, max_rb, st)
+                   : launch_grouped_decode(s.act, epi, s.w_routed, cs, a, max_rb, st);
+  }
+
+  // Int8 W8A8: int8 codes and per-row scales of the activations (rows and gather as in a), one
+  // launch over the routed and shared groups; h comes out in bf16
+  hipError_t int8(int epi, const GroupedArgs& a, const void* codes, const void* scales) const {
+    GroupedArgs ia = a;
+    ia.act = codes;
+    ia.act_scale = scales;
+    return prefill ? launch_int8_prefill(epi, ia, max_rb, st)
+                   : launch_grouped_decode(s.act, epi, MOE_INT8_W8A8, MOE_INT8_W8A8, ia, max_rb, st);
+  }
+
+  // W4A8: the routed groups multiply MXFP8 codes of the activations (rows of K, gathered through
+  // gather, or read in order when it is null). On the prefill kernel gate/up writes h as MXFP8 for
+  // the down product; on the decode kernel it writes h in bf16, quantised before down. The shared
+  // expert keeps its own launch, on the bf16 activations of base unless it is MXFP8 itself.
+  hipError_t w4a8(int epi, const GroupedArgs& base, const void* codes, const void* scales, int K, int rows,
+                  const int32_t* gather) const {
+    const bool swiglu = epi == EPI_SWIGLU;
+    GroupedArgs ra = base;
+    ra.gather = gather;
+    ra.act = codes;
+    ra.lda = K;
+    ra.act_rows = rows;
+    ra.act_scale = scales;
+    ra.g_begin = 0;
+    ra.g_end = s.E;
+    if (prefill && swiglu) to_mxfp8_h(ra);
+    hipError_t r = prefill ? launch_w4a8_prefill(swiglu ? EPI_SWIGLU_Q8 : epi, ra, max_rb, st)
+                           : launch_grouped_decode(s.act, epi, MOE_MXFP4_B32_A8, MOE_MXFP4_B32_A8, ra, max_rb, st);
+    if (r != hipSuccess || !S) return r;
+    GroupedArgs sa = base;
+    sa.g_begin = s.E;
+    sa.g_end = s.E + 1;
+    const int shared_rb = (s.T + ROW_BLOCK - 1) / ROW_BLOCK;
+    if (cs != MOE_MXFP8_B32_A8)
+      return prefill ? launch_grouped_prefill(s.act, epi, cs, cs, sa, max_rb, st)
+                     : launch_grouped_decode(s.act, epi, cs, cs, sa, shared_rb, st);
+    // W8A8 MXFP8 shared expert: the same MXFP8 rows of x (token t is row P + t of the group) and
+    // of h, whose shared rows follow the routed ones
+    sa.act = codes;
+    sa.lda = K;
+    sa.act_scale = scales;
+    sa.gather = swiglu ? gather : nullptr;
+    sa.act_rows = swiglu ? rows : P + s.T;
+    if (!prefill)
+      return launch_grouped_decode(s.act, epi, MOE_MXFP8_B32_A8, MOE_MXFP8_B32_A8, sa, shared_rb, st);
+    if (swiglu) to_mxfp8_h(sa);
+    return launch_w8a8_shared(swiglu ? EPI_SWIGLU_Q8 : epi, sa, s.T, st);
+  }
+
+  // the prefill kernels' gate/up epilogue writes h straight to MXFP8 codes and exponents
+  void to_mxfp8_h(GroupedArgs& a) const {
+    a.out = at<void>(ws, L.hq);
+    a.ldo = s.I;
+    a.out_scale = at<void>(ws, L.hs);
+  }
+
+  // h (bf16, rows 0..rows-1 of the workspace) to the activation format of the down product;
+  // nothing for the formats whose gate/up epilogue already wrote it there
+  hipError_t quantise_h(bool a8, bool i8) const {
+    if (a8 && !prefill) {
+      // the routed rows, and those of a W8A8 MXFP8 shared expert after them
+      const int rows = P + (S && cs == MOE_MXFP8_B32_A8 ? s.T : 0);
+      return launch_quant_mxfp8(at<void>(ws, L.h), rows, s.I, at<uint8_t>(ws, L.hq), at<uint8_t>(ws, L.hs), st);
+    }
+    if (i8) return launch_quant_int8(at<void>(ws, L.h), P + S * s.T, s.I, at<int8_t>(ws, L.hq), at<float>(ws, L.hs), st);
+    return hipSuccess;
+  }
+};
+
+// the weights of one product: gate and up (two matrices, the SwiGLU pair) or down (one)
+void set_weights(GroupedArgs& a, const moe_weights& r, const moe_weights* sh, bool gate_up, size_t mat_bytes,
+                 size_t scale_bytes) {
+  a.wa_r = (const uint8_t*)(gate_up ? r.gate : r.down);
+  a.wb_r = gate_up ? (const uint8_t*)r.up : nullptr;
+  a.sa_r = (const uint8_t*)(gate_up ? r.gate_scale : r.down_scale);
+  a.sb_r = gate_up ? (const uint8_t*)r.up_scale : nullptr;
+  if (sh) {
+    a.wa_s = (const uint8_t*)(gate_up ? sh->gate : sh->down);
+    a.wb_s = gate_up ? (const uint8_t*)sh->up : nullptr;
+    a.sa_s = (const uint8_t*)(gate_up ? sh->gate_scale : sh->down_scale);
+    a.sb_s = gate_up ? (const uint8_t*)sh->up_scale : nullptr;
+  }
+  a.mat_bytes = (long long)mat_bytes;
+  a.scale_bytes = (long long)scale_bytes;
+}
+
 moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const int32_t* slot_token,
                   const moe_weights& r, const moe_weights* sh, void* y_perm, void* y_shared, void* ws, const Ws& L,
                   hipStream_t st, hipEvent_t const* ev = nullptr, bool plan_ready = false) {
@@ -319,6 +423,8 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   moe_status rs;
   if (ev && (rs = record(ev[0], st)) != MOE_OK) return rs;
   const int max_rb = std::min(s.E, P) + (P + rb - 1) / rb + S * ((s.T + rb - 1) / rb);
+  const bool a8 = s.w_routed == MOE_MXFP4_B32_A8, i8 = s.w_routed == MOE_INT8_W8A8;
+  const FfnPass f{s, ws, L, st, prefill, P, S, S ? (int)s.w_shared : (int)s.w_routed, max_rb};
 
   GroupedArgs a{};
   a.zero_row = zero;
@@ -329,149 +435,50 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.shared_group = S ? s.E : -1;
   a.P = P;
   a.M = P + S * s.T;
-  // gate/up with the SwiGLU epilogue: h = SiLU(x Wg) * (x Wu)
+  // gate/up with the SwiGLU epilogue: h = SiLU(x Wg) * (x Wu), x gathered per slot
   a.gather = slot_token;
   a.act = x;
   a.lda = s.H;
   a.act_rows = s.T;
-  a.wa_r = (const uint8_t*)r.gate;
-  a.wb_r = (const uint8_t*)r.up;
-  a.sa_r = (const uint8_t*)r.gate_scale;
-  a.sb_r = (const uint8_t*)r.up_scale;
-  if (S) {
-    a.wa_s = (const uint8_t*)sh->gate;
-    a.wb_s = (const uint8_t*)sh->up;
-    a.sa_s = (const uint8_t*)sh->gate_scale;
-    a.sb_s = (const uint8_t*)sh->up_scale;
-  }
-  a.mat_bytes = (long long)mb1;
-  a.scale_bytes = (long long)sb1;
+  set_weights(a, r, S ? sh : nullptr, true, mb1, sb1);
   a.K = s.H;
   a.N = s.I;
   a.out = at<void>(ws, L.h);
   a.ldo = s.I;
   a.out_s = nullptr;
-  const int cs = S ? s.w_shared : s.w_routed;
-  const bool a8 = s.w_routed == MOE_MXFP4_B32_A8;
-  // W4A8: the routed groups multiply MXFP8 codes of x (quantised once per token, gathered like x).
-  // On the prefill kernel they write h as MXFP8 for their down product; on the decode kernel they
-  // write it in bf16 and it is quantised before down. The shared expert keeps its own launch.
-  auto launch_a8 = [&](int epi, const GroupedArgs& base, const void* codes, const void* scales, int K,
-                       int rows, const int32_t* gather) {
-    GroupedArgs ra = base, sa = base;
-    ra.gather = gather;
-    ra.act = codes;
-    ra.lda = K;
-    ra.act_rows = rows;
-    ra.act_scale = scales;
-    ra.g_begin = 0;
-    ra.g_end = s.E;
-    hipError_t r;
-    if (prefill) {
-      if (epi == EPI_SWIGLU) {
-        ra.out = at<void>(ws, L.hq);
-        ra.ldo = s.I;
-        ra.out_scale = at<void>(ws, L.hs);
-      }
-      r = launch_w4a8_prefill(epi == EPI_SWIGLU ? EPI_SWIGLU_Q8 : epi, ra, max_rb, st);
-    } else {
-      r = launch_grouped_decode(s.act, epi, MOE_MXFP4_B32_A8, MOE_MXFP4_B32_A8, ra, max_rb, st);
-    }
-    if (r != hipSuccess || !S) return r;
-    sa.g_begin = s.E;
-    sa.g_end = s.E + 1;
-    if (cs != MOE_MXFP8_B32_A8)
-      return prefill ? launch_grouped_prefill(s.act, epi, cs, cs, sa, max_rb, st)
-                     : launch_grouped_decode(s.act, epi, cs, cs, sa, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
-    // W8A8 MXFP8 shared expert: the same MXFP8 rows of x (token t is row P + t of the group)
-    // and of h, whose shared rows follow the routed ones
-    sa.act = codes;
-    sa.lda = K;
-    sa.act_scale = scales;
-    if (!prefill) {
-      // decode kernel: h in bf16 (quantised with the routed rows before down)
-      sa.gather = epi == EPI_SWIGLU ? gather : nullptr;
-      sa.act_rows = epi == EPI_SWIGLU ? rows : P + s.T;
-      return launch_grouped_decode(s.act, epi, MOE_MXFP8_B32_A8, MOE_MXFP8_B32_A8, sa,
-                                   (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
-    }
-    if (epi == EPI_SWIGLU) {
-      sa.gather = gather;
-      sa.act_rows = rows;
-      sa.out = at<void>(ws, L.hq);
-      sa.ldo = s.I;
-      sa.out_scale = at<void>(ws, L.hs);
-    } else {
-      sa.gather = nullptr;
-      sa.act_rows = P + s.T;
-    }
-    return launch_w8a8_shared(epi == EPI_SWIGLU ? EPI_SWIGLU_Q8 : epi, sa, s.T, st);
-  };
-  const bool i8 = s.w_routed == MOE_INT8_W8A8;
   if (a8) {
+    // x to MXFP8 once per token; the codes are gathered like x
     e = launch_quant_mxfp8(x, s.T, s.H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), st);
     if (e != hipSuccess) return hip_status(e, "MXFP8 quantisation of x");
-    e = launch_a8(EPI_SWIGLU, a, at<void>(ws, L.xq), at<void>(ws, L.xs), s.H, s.T, slot_token);
+    e = f.w4a8(EPI_SWIGLU, a, at<void>(ws, L.xq), at<void>(ws, L.xs), s.H, s.T, slot_token);
   } else if (i8) {
-    // Int8 W8A8: x to int8 per token, then one launch over the routed and shared groups, which
-    // writes h in bf16 (quantised per row before down)
+    // x to int8 per token
     e = launch_quant_int8(x, s.T, s.H, at<int8_t>(ws, L.xq), at<float>(ws, L.xs), st);
     if (e != hipSuccess) return hip_status(e, "int8 quantisation of x");
-    GroupedArgs ia = a;
-    ia.act = at<void>(ws, L.xq);
-    ia.act_scale = at<void>(ws, L.xs);
-    e = prefill ? launch_int8_prefill(EPI_SWIGLU, ia, max_rb, st)
-                : launch_grouped_decode(s.act, EPI_SWIGLU, MOE_INT8_W8A8, MOE_INT8_W8A8, ia, max_rb, st);
+    e = f.int8(EPI_SWIGLU, a, at<void>(ws, L.xq), at<void>(ws, L.xs));
   } else {
-    e = prefill ? launch_grouped_prefill(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st)
-                : launch_grouped_decode(s.act, EPI_SWIGLU, s.w_routed, cs, a, max_rb, st);
+    e = f.plain(EPI_SWIGLU, a);
   }
   if (e != hipSuccess) return hip_status(e, "gate/up grouped GEMM");
   if (ev && (rs = record(ev[1], st)) != MOE_OK) return rs;
-  if (a8 && !prefill) {
-    // W4A8 on the decode kernel: the routed rows of h (bf16), and those of a W8A8 MXFP8 shared
-    // expert after them, to MXFP8 for the down product
-    const int qrows = P + (S && cs == MOE_MXFP8_B32_A8 ? s.T : 0);
-    e = launch_quant_mxfp8(at<void>(ws, L.h), qrows, s.I, at<uint8_t>(ws, L.hq), at<uint8_t>(ws, L.hs), st);
-    if (e != hipSuccess) return hip_status(e, "MXFP8 quantisation of h");
-  }
-  // down: y = h Wd
+  e = f.quantise_h(a8, i8);
+  if (e != hipSuccess) return hip_status(e, "quantisation of h");
+
+  // down: y = h Wd, the routed rows to y_perm and the shared ones to y_shared
   a.gather = nullptr;
   a.act = at<void>(ws, L.h);
   a.lda = s.I;
   a.act_rows = P + S * s.T;
-  a.wa_r = (const uint8_t*)r.down;
-  a.wb_r = nullptr;
-  a.sa_r = (const uint8_t*)r.down_scale;
-  a.sb_r = nullptr;
-  if (S) {
-    a.wa_s = (const uint8_t*)sh->down;
-    a.wb_s = nullptr;
-    a.sa_s = (const uint8_t*)sh->down_scale;
-    a.sb_s = nullptr;
-  }
-  a.mat_bytes = (long long)mb2;
-  a.scale_bytes = (long long)sb2;
+  set_weights(a, r, S ? sh : nullptr, false, mb2, sb2);
   a.K = s.I;
   a.N = s.H;
   a.out = y_perm;
   a.ldo = s.H;
   a.out_s = S ? y_shared : nullptr;
   a.ldo_s = s.H;
-  if (a8) {
-    e = launch_a8(EPI_PLAIN, a, at<void>(ws, L.hq), at<void>(ws, L.hs), s.I, P, nullptr);
-  } else if (i8) {
-    e = launch_quant_int8(at<void>(ws, L.h), P + S * s.T, s.I, at<int8_t>(ws, L.hq), at<float>(ws, L.hs), st);
-    if (e != hipSuccess) return hip_status(e, "int8 quantisation of h");
-    GroupedArgs ia = a;
-    ia.act = at<void>(ws, L.hq);
-    ia.act_scale = at<void>(ws, L.hs);
-    e = prefill ? launch_int8_prefill(EPI_PLAIN, ia, max_rb, st)
-                : launch_grouped_decode(s.act, EPI_PLAIN, MOE_INT8_W8A8, MOE_INT8_W8A8, ia, max_rb, st);
-  } else {
-    e = prefill ? launch_grouped_prefill(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st)
-                : launch_grouped_decode(s.act, EPI_PLAIN, s.w_routed, cs, a, max_rb, st);
-  }
+  if (a8) e = f.w4a8(EPI_PLAIN, a, at<void>(ws, L.hq), at<void>(ws, L.hs), s.I, P, nullptr);
+  else if (i8) e = f.int8(EPI_PLAIN, a, at<void>(ws, L.hq), at<void>(ws, L.hs));
+  else e = f.plain(EPI_PLAIN, a);
   if (e != hipSuccess) return hip_status(e, "down grouped GEMM");
   return ev ? record(ev[2], st) : MOE_OK;
 }
