@@ -160,6 +160,12 @@ SMALL = [
     ("int8-small-groups", L.LayerSpec("s20", T=96, H=1024, E=24, k=4, I=512, w_routed="int8", seed=50)),
     ("int8-one-token", L.LayerSpec("s21", T=1, H=512, E=4, k=2, I=256, shared=True, w_routed="int8",
                                    w_shared="int8", seed=51)),
+    # the limits the ABI accepts: 1024 experts (16 scores per lane of the top-k wave) and k = 16,
+    # with a shared expert as group 1025 of the plan
+    ("max-E-and-k", L.LayerSpec("s22", T=40, H=512, E=1024, k=16, I=256, shared=True, seed=52)),
+    # the degenerate layer: one expert, k = 1, every token's weight 1 (a dense SwiGLU plus the
+    # shared expert)
+    ("single-expert", L.LayerSpec("s23", T=33, H=512, E=1, k=1, I=256, shared=True, seed=53)),
 ]
 
 
