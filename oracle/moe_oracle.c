@@ -353,6 +353,10 @@ static int mxfp8_roundtrip(int K, double* v) {
 /* largest magnitude a, the factor f = 127 / a and the scale s = a / 127 (fp32 divisions),    */
 /* and each code q = v * f (fp32 product) rounded to the nearest integer, ties to even,     */
 /* clamped to [-127, 127]; the row then stands for q * s. An all-zero row has s = 0, q = 0.  */
+/* f is formed with a's binary exponent taken out: a = m 2^e (m in [0.5, 1)), f = 127 / m   */
+/* and q = rint((v 2^-e) * f). Scaling by 2^-e is exact, so this is the same fp32 number as  */
+/* v * (127 / a) wherever 127 / a is finite, and it stays defined for rows whose maximum is  */
+/* so small (below about 2^-121) that 127 / a overflows fp32.                                 */
 /* The rows quantised here (bf16 values, or h after its bf16 rounding) are exact in fp32,    */
 /* so this decision is the same on any IEEE machine.                                        */
 /* ---------------------------------------------------------------------------------------- */
@@ -369,9 +373,11 @@ int oracle_int8_quantize(int K, const double* v, int8_t* codes, float* scale) {
     *scale = 0.0f;
     return 0;
   }
-  volatile float f = 127.0f / a, s = a / 127.0f; /* fp32 roundings, not extended precision */
+  int e;
+  const float m = frexpf(a, &e);                  /* a = m 2^e exactly */
+  volatile float f = 127.0f / m, s = a / 127.0f; /* fp32 roundings, not extended precision */
   for (int i = 0; i < K; ++i) {
-    volatile float p = (float)v[i] * f;
+    volatile float p = ldexpf((float)v[i], -e) * f;
     float q = rintf(p);
     if (q > 127.0f) q = 127.0f;
     if (q < -127.0f) q = -127.0f;

@@ -635,6 +635,31 @@ def test_int8_quantize_hand_values():
         O.int8_quantize(np.array([1.0 + 2.0 ** -40]))
 
 
+def test_int8_quantize_tiny_rows_closed_form():
+    """A row of integers j 2^-133 (bf16 subnormals, maximum 127 2^-133) stands for exactly j times
+    s = 2^-133: codes j, although 127 / max overflows fp32 there (the factor is formed from the
+    maximum's significand, 127 / (127/128) = 128, applied to v 2^126 = j / 128)."""
+    j = np.array([127, -127, 0, 1, -1, 64, -3, 100, 0, 5], np.float64)
+    c, sc = O.int8_quantize(j * 2.0 ** -133)
+    assert c.tolist() == j.astype(int).tolist()
+    assert sc == np.float32(2.0 ** -133)
+
+
+def test_int8_quantize_codes_are_invariant_under_power_of_two_scaling():
+    """Scaling a row by 2^p leaves its codes unchanged and scales s by 2^p exactly, for p from deep
+    below the range where 127 / max is finite in fp32 up to the largest bf16 maxima."""
+    v = L.act_to_f64(L.store_act(px.normal_f32(5, 11, 0, 0, 4 * 256).reshape(4, 256), "bf16"), "bf16")
+    c0, s0 = O.int8_quantize(v)
+    for p in (-140, -125, -121, -60, 0, 60, 124):
+        vp = v * 2.0 ** p
+        if np.abs(vp).max() >= 2.0 ** 128 or np.abs(vp[vp != 0]).min() < 2.0 ** -149:
+            continue  # keep every entry exact in fp32
+        c, sc = O.int8_quantize(vp)
+        assert np.array_equal(c, c0), p
+        if np.all(s0.astype(np.float64) * 2.0 ** p >= 2.0 ** -126):  # s normal: exact scaling
+            assert np.array_equal(sc.astype(np.float64), s0.astype(np.float64) * 2.0 ** p), p
+
+
 def test_int8_quantize_error_bound_on_random_rows():
     """Every code within [-127, 127], the row maximum at +-127, and q s within half a step of v."""
     v = L.act_to_f64(L.store_act(px.normal_f32(5, 9, 0, 0, 8 * 512).reshape(8, 512), "bf16"), "bf16")
