@@ -652,4 +652,28 @@ moe_status moe_layer_forward_timed(const moe_shape* shape, const void* x, const 
                   (hipStream_t)stream, (hipEvent_t const*)events);
 }
 
+moe_status moe_quantize_mxfp8(const void* x, int32_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              moe_stream_t stream) {
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows=%d < 0", rows);
+  if (K < 32 || K % 32) return fail(MOE_ERR_INVALID_ARG, "K=%d must be a positive multiple of 32", K);
+  if ((long long)rows * K > (1LL << 40)) return fail(MOE_ERR_INVALID_ARG, "rows * K too large");
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if ((uintptr_t)x % 16 || (uintptr_t)codes % 8)
+    return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte and codes 8-byte aligned");
+  return hip_status(launch_quant_mxfp8(x, rows, K, codes, scales, (hipStream_t)stream), "MXFP8 quantisation");
+}
+
+moe_status moe_quantize_int8(const void* x, int32_t rows, int32_t K, int8_t* codes, float* scales,
+                             moe_stream_t stream) {
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows=%d < 0", rows);
+  if (K < 8 || K % 8 || K > 8192)
+    return fail(MOE_ERR_INVALID_ARG, "K=%d must be a positive multiple of 8, at most 8192", K);
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if ((uintptr_t)x % 16 || (uintptr_t)codes % 8 || (uintptr_t)scales % 4)
+    return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte, codes 8-byte and scales 4-byte aligned");
+  return hip_status(launch_quant_int8(x, rows, K, codes, scales, (hipStream_t)stream), "int8 quantisation");
+}
+
 }  // extern "C"

@@ -60,7 +60,9 @@ __global__ void __launch_bounds__(QTHREADS) quant_mxfp8_kernel(const uint16_t* _
 // the fewest that cover K, so short rows keep the occupancy up): the largest magnitude by a
 // wave-wide xor reduction, then f = 127 / max and s = max / 127 (IEEE fp32 divisions) and
 // code = rint(v * f) (fp32 product, ties to even), clamped to +-127. An all-zero row gets s = 0 and
-// zero codes.
+// zero codes. f is formed from the maximum's significand, max = m 2^e, f = 127 / m, and multiplies
+// v 2^-e: the exact power-of-two scaling gives the same fp32 value as v * (127 / max) wherever that
+// factor is finite, and keeps it finite for rows whose maximum is below about 2^-121.
 constexpr int QI8_MAX_CHUNKS = 16;
 template <int CH>
 __global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __restrict__ src, int rows, int K,
@@ -81,7 +83,8 @@ __global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
-  const float f = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
+  const int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;  // amax = m 2^e, m in [0.5, 1)
+  const float f = amax > 0.f ? __fdiv_rn(127.0f, __builtin_amdgcn_ldexpf(amax, -e)) : 0.f;
 #pragma unroll
   for (int q = 0; q < CH; ++q) {
     const int c = 8 * lane + 512 * q;
@@ -90,7 +93,8 @@ __global__ void __launch_bounds__(QTHREADS) quant_int8_kernel(const uint16_t* __
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float x = (i & 1) ? bf16hi(v[q][i >> 1]) : bf16lo(v[q][i >> 1]);
-      const float r = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fmul_rn(x, f)), -127.f), 127.f);
+      const float r =
+          __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fmul_rn(__builtin_amdgcn_ldexpf(x, -e), f)), -127.f), 127.f);
       w[i >> 2] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (i & 3));
     }
     *(u32x2*)(codes + (size_t)row * K + c) = u32x2{w[0], w[1]};

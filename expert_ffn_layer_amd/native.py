@@ -19,7 +19,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_pack_size", "moe_pack", "moe_workspace_size",
            "moe_route", "moe_route_hash", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_forward_hash", "moe_layer_forward_timed")
+           "moe_layer_forward_hash", "moe_layer_forward_timed", "moe_quantize_mxfp8", "moe_quantize_int8")
 TIMED_EVENTS = 7
 
 
@@ -70,6 +70,8 @@ def load() -> ctypes.CDLL:
         lib.moe_layer_forward_hash.argtypes = [PS, P, P, P, P, P, I32, PW, PW, P, P, P, P, SZ, P]
         lib.moe_layer_forward_timed.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P,
                                                 ctypes.POINTER(ctypes.c_void_p)]
+        lib.moe_quantize_mxfp8.argtypes = [P, I32, I32, P, P, P]
+        lib.moe_quantize_int8.argtypes = [P, I32, I32, P, P, P]
         for name in EXPORTS[2:]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -183,3 +185,15 @@ def moe_layer_forward_timed(shape, x, Wr_packed, bias, routed: dict, shared: dic
                                           None if s is None else ctypes.byref(s), _p(y), _p(topk_idx),
                                           _p(topk_w), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                           _stream(stream), arr))
+
+
+def moe_quantize_mxfp8(x, codes, scales, stream=None):
+    """x bf16 [rows, K] -> codes uint8 [rows, K], scales uint8 [rows, K / 32] (e8m0)."""
+    rows, K = (x.shape[0], x.shape[1]) if x is not None else (0, 32)
+    _check(load().moe_quantize_mxfp8(_p(x), rows, K, _p(codes), _p(scales), _stream(stream)))
+
+
+def moe_quantize_int8(x, codes, scales, stream=None):
+    """x bf16 [rows, K] -> codes int8 [rows, K], scales float32 [rows]."""
+    rows, K = (x.shape[0], x.shape[1]) if x is not None else (0, 8)
+    _check(load().moe_quantize_int8(_p(x), rows, K, _p(codes), _p(scales), _stream(stream)))

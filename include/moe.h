@@ -77,7 +77,8 @@ typedef enum {
                              Weights: int8 codes + one fp32 scale per output feature, w = c * s[n].
                              Each row of x and of h (after its bf16 rounding) is quantised in fp32:
                              f = 127 / max|v|, s = max|v| / 127, code = rint(v * f) (ties to even,
-                             clamped to +-127); an all-zero row has s = 0. The products accumulate
+                             clamped to +-127; f taken from max|v|'s significand, as
+                             moe_quantize_int8 states); an all-zero row has s = 0. The products accumulate
                              the codes exactly in int32 on the int8 matrix instruction, then scale
                              by s_row * s[n]. As w_routed, with no shared expert or an INT8 one;
                              BF16 activations, I a multiple of 256 and H of 512; on either path. */
@@ -94,16 +95,18 @@ typedef enum {
 } moe_path;
 
 typedef struct {
-  int32_t T;          /* tokens, >= 1 */
+  int32_t T;          /* tokens, >= 0 (0: the calls enqueue nothing) */
   int32_t H;          /* hidden size, multiple of 128 */
   int32_t E;          /* routed experts, 1..1024 */
   int32_t k;          /* experts per token, 1..min(E, 16) */
   int32_t I;          /* expert intermediate size, multiple of 128 */
   int32_t I_shared;   /* shared expert intermediate size: 0 = no shared expert, else == I */
   moe_dtype act;      /* MOE_F32 or MOE_BF16: x, Wr, y and the intermediates */
-  moe_dtype w_routed; /* MOE_F32 (with act MOE_F32) or BF16 / FP8 / MXFP4 / MXFP4_B32_A8 (with
-                         act BF16) */
-  moe_dtype w_shared; /* same rule, without MXFP4_B32_A8 */
+  moe_dtype w_routed; /* MOE_F32 (with act MOE_F32) or BF16 / FP8 / MXFP4 / MXFP4_B32_A8 /
+                         INT8_W8A8 (with act BF16) */
+  moe_dtype w_shared; /* MOE_F32 (with act MOE_F32) or BF16 / FP8 / MXFP4 (with act BF16);
+                         MXFP8_B32_A8 beside MXFP4_B32_A8 routed experts; INT8_W8A8 beside
+                         INT8_W8A8 routed experts (the only shared format they take) */
   moe_path path;
 } moe_shape;
 
@@ -258,6 +261,38 @@ moe_status moe_layer_forward_timed(const moe_shape* shape, const void* x, const 
                                    const moe_weights* shared, void* y, int32_t* topk_idx_out,
                                    float* topk_w_out, void* ws, size_t ws_bytes,
                                    moe_stream_t stream, moe_event_t* events);
+
+/*
+ * moe_quantize_mxfp8 — the activation quantisation of the MXFP8 formats (MOE_MXFP4_B32_A8,
+ * MOE_MXFP8_B32_A8; 'CANN DeepSeek-V4推理优化', quantisation strategy: 8-bit activations of the
+ * W4A8 and W8A8 linear layers), as the layer applies it to each row of x before gate/up.
+ *   x        bf16 [rows][K], row-major; K a multiple of 32
+ *   codes    uint8 [rows][K] out: E4M3FN(x * 2^-X), round to nearest even, saturating at +-448,
+ *            the sign of zero kept
+ *   scales   uint8 [rows][K/32] out: X + 127 for each run of 32 consecutive elements of a row,
+ *            X = floor(log2 max|v|) - 8 clamped to [-127, 127], and -127 for an all-zero run
+ * x is 16-byte aligned and codes 8-byte aligned. rows == 0 enqueues nothing. MOE_ERR_INVALID_ARG
+ * for rows < 0, K < 32 or not a multiple of 32, rows * K above 2^40, a NULL pointer or a
+ * misaligned one.
+ */
+moe_status moe_quantize_mxfp8(const void* x, int32_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              moe_stream_t stream);
+
+/*
+ * moe_quantize_int8 — the per-token activation quantisation of MOE_INT8_W8A8 (same page, Int8
+ * quantisation strategy: activations quantised dynamically per token), as the layer applies it to
+ * each row of x before gate/up and of h before down.
+ *   x        bf16 [rows][K], row-major; K a multiple of 8, at most 8192
+ *   codes    int8 [rows][K] out: rint(v * f) with f = 127 / max|v| (fp32 division and product,
+ *            ties to even), clamped to +-127; zero for an all-zero row. f is formed from the
+ *            maximum's significand (max|v| = m 2^e: f = 127 / m applied to v 2^-e), the same fp32
+ *            value wherever 127 / max|v| is finite, and finite for any row
+ *   scales   float [rows] out: max|v| / 127 (fp32 division); 0 for an all-zero row
+ * x is 16-byte, codes 8-byte and scales 4-byte aligned. rows == 0 enqueues nothing.
+ * MOE_ERR_INVALID_ARG for rows < 0, K outside those limits, a NULL pointer or a misaligned one.
+ */
+moe_status moe_quantize_int8(const void* x, int32_t rows, int32_t K, int8_t* codes, float* scales,
+                             moe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     txt = open(os.path.join(ROOT, "include", "moe.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_and_binding_agree():
@@ -152,3 +152,24 @@ def test_entry_points_reject_null_and_small_workspace_before_launch():
                                       None, None, fake, 1 << 30, None) == 1
     # misaligned workspace
     assert lib.moe_permute(ctypes.byref(s), fake, fake, fake, fake, P(0x1001), 1 << 30, None) == 1
+
+
+def test_quantisers_validate_before_launch():
+    lib = N.load()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first (or rows == 0 returns)
+    for fn, k_ok in ((lib.moe_quantize_mxfp8, 64), (lib.moe_quantize_int8, 64)):
+        assert fn(fake, 0, k_ok, fake, fake, None) == 0        # no rows: nothing to do
+        assert fn(fake, -1, k_ok, fake, fake, None) == 1       # negative rows
+        assert fn(None, 4, k_ok, fake, fake, None) == 1        # NULL input
+        assert fn(fake, 4, k_ok, None, fake, None) == 1        # NULL codes
+        assert fn(fake, 4, k_ok, fake, None, None) == 1        # NULL scales
+        assert fn(P(0x1008), 4, k_ok, fake, fake, None) == 1   # x not 16-byte aligned
+        assert fn(fake, 4, k_ok, P(0x1004), fake, None) == 1   # codes not 8-byte aligned
+    assert lib.moe_quantize_mxfp8(fake, 4, 48, fake, fake, None) == 1    # K not a multiple of 32
+    assert lib.moe_quantize_mxfp8(fake, 4, 0, fake, fake, None) == 1
+    assert lib.moe_quantize_mxfp8(fake, 1 << 30, 1 << 12, fake, fake, None) == 1  # rows * K > 2^40
+    assert lib.moe_quantize_int8(fake, 4, 12, fake, fake, None) == 1     # K not a multiple of 8
+    assert lib.moe_quantize_int8(fake, 4, 8200, fake, fake, None) == 1   # K above 8192
+    assert lib.moe_quantize_int8(fake, 4, 64, fake, P(0x1002), None) == 1  # scales not 4-byte aligned
+    assert "aligned" in lib.moe_last_error().decode()

@@ -432,6 +432,99 @@ def test_layer_random_sweep_quantised(spec):
         assert torch.equal(y, y2)
 
 
+# ------------------------------------------------------------------ activation quantisers, bit for bit
+
+def _bf16_rows(rows):
+    """float rows -> (their bf16 rounding as exact float64 values, the bf16 tensor on the device)."""
+    bits = px.f32_to_bf16_bits(np.asarray(rows, np.float32))
+    exact = px.bf16_bits_to_f32(bits).astype(np.float64)
+    return exact, torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _mxfp8_probe_rows(K, seed):
+    """Rows whose 32-blocks reach every branch of the MXFP8 rule: normal rows over a wide range of
+    scales, an all-zero row, -0.0 and entries far below their block maximum (the E4M3 subnormal grid
+    after scaling), block maxima whose scaled value reaches [448, 512) (saturation) or sits just
+    below it, exact E4M3 rounding ties, and bf16 subnormals (the exponent clamped at -127)."""
+    rng = np.random.default_rng(seed)
+    out = [rng.standard_normal(K) * 2.0 ** rng.uniform(-60, 60) for _ in range(24)]
+    out.append(np.zeros(K))
+    r = rng.standard_normal(K)
+    r[::7] = -0.0
+    r[1::5] *= 2.0 ** -rng.integers(8, 20, size=len(r[1::5]))
+    out.append(r)
+    # one block per maximum: 1.6875 (scaled 432, a tie between 416 and 448), 1.71875 (440, rounds up
+    # to 448), 1.75 (448), 1.8125 (464), 1.96875 (504), each with a random sign
+    r = rng.standard_normal(K) * 0.25
+    for b, m in enumerate((1.6875, 1.71875, 1.75, 1.8125, 1.96875)):
+        r[32 * (b % (K // 32)) + int(rng.integers(32))] = m * (1 if rng.random() < 0.5 else -1)
+    out.append(r)
+    # block maximum 1 (exponent -8), the other entries exact midpoints of the E4M3 grid at several
+    # binades: (1 + (2j + 1) / 16) * 2^-m
+    r = np.zeros(K)
+    for b in range(K // 32):
+        blk = [(1.0 + (2 * int(rng.integers(8)) + 1) / 16.0) * 2.0 ** -int(rng.integers(1, 12)) for _ in range(31)]
+        r[32 * b:32 * b + 31] = np.array(blk) * np.where(rng.random(31) < 0.5, -1.0, 1.0)
+        r[32 * b + 31] = 1.0
+    out.append(r)
+    out.append(rng.integers(-127, 128, size=K) * 2.0 ** -133)  # bf16 subnormals
+    out.append(rng.standard_normal(K) * 2.0 ** 120)
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("K", [32, 256, 7168])
+def test_mxfp8_quantiser_matches_oracle_bit_for_bit(K):
+    """The GPU's MXFP8 activation quantiser (the W4A8 layer's x) gives the oracle's codes and
+    exponents exactly: both take each decision from exact values with the same rounding rule."""
+    x, xd = _bf16_rows(_mxfp8_probe_rows(K, seed=900 + K))
+    codes = torch.empty(xd.shape, dtype=torch.uint8, device=DEV)
+    scales = torch.empty((xd.shape[0], K // 32), dtype=torch.uint8, device=DEV)
+    N.moe_quantize_mxfp8(xd, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = O.mxfp8_quantize(x)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    # the probes reached saturation, the subnormal grid and signed zero
+    assert (rc & 0x7F == 0x7E).any() and ((rc & 0x7F) > 0).any() and ((rc & 0x78) == 0).any()
+    assert (rc == 0x80).any()
+
+
+def _int8_probe_rows(K, seed):
+    """Normal rows over a wide range of scales, an all-zero row, -0.0 entries, rows with maximum 127
+    and 254 (factors 1 and 1/2, so half-integer and odd entries are exact rounding ties), a row with
+    one dominant entry, bf16 subnormals."""
+    rng = np.random.default_rng(seed)
+    out = [rng.standard_normal(K) * 2.0 ** rng.uniform(-60, 60) for _ in range(12)]
+    out.append(np.zeros(K))
+    r = rng.standard_normal(K)
+    r[::3] = -0.0
+    out.append(r)
+    for amax, ties in ((127.0, rng.integers(-40, 40, size=K) + 0.5), (254.0, 2.0 * rng.integers(-60, 60, size=K) + 1.0)):
+        r = ties.astype(np.float64)
+        r[int(rng.integers(K))] = amax if rng.random() < 0.5 else -amax
+        out.append(r)
+    r = rng.standard_normal(K) * 1e-3
+    r[int(rng.integers(K))] = 1e3
+    out.append(r)
+    out.append(rng.integers(-127, 128, size=K) * 2.0 ** -133)
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("K", [8, 520, 2048, 7168, 8192])
+def test_int8_quantiser_matches_oracle_bit_for_bit(K):
+    """The GPU's per-token int8 quantiser (the Int8 W8A8 layer's x and h) gives the oracle's codes
+    and fp32 scales exactly, for each row-length variant of the kernel."""
+    x, xd = _bf16_rows(_int8_probe_rows(K, seed=950 + K))
+    codes = torch.empty(xd.shape, dtype=torch.int8, device=DEV)
+    scales = torch.empty(xd.shape[0], dtype=torch.float32, device=DEV)
+    N.moe_quantize_int8(xd, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = O.int8_quantize(x)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert (np.abs(rc) == 127).any() and (rs == 0).any()
+
+
 # ------------------------------------------------------------------ hash routing
 
 HASH_SPECS = [
