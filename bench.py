@@ -32,11 +32,11 @@ TRAFFIC = {
     # gate/up prefill kernel
     "c5": {"sha": "e0463fd1be82c895", "bytes": 16306116370},
     # the W4A8 gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared bf16 GEMM
-    "v4p-w4a8": {"sha": "f0710d12f35a6620", "bytes": 10135443620},
+    "v4p-w4a8": {"sha": "176a8dd7ef59aeac", "bytes": 10131416530},
     # the hybrid gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared W8A8 MXFP8 GEMM
-    "v4p-mx": {"sha": "f0710d12f35a6620", "bytes": 9792367135},
+    "v4p-mx": {"sha": "176a8dd7ef59aeac", "bytes": 9795198467},
     # the int8 gate/up stage: x to int8 + Int8 W8A8 GEMM
-    "v3-int8": {"sha": "f0710d12f35a6620", "bytes": 17220118025},
+    "v3-int8": {"sha": "176a8dd7ef59aeac", "bytes": 17225696545},
 }
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
