@@ -88,7 +88,7 @@ moe_status check_shape(const moe_shape* s) {
   const bool f32 = s->act == MOE_F32;
   auto ok = [&](moe_dtype w) { return f32 ? w == MOE_F32 : w != MOE_F32; };
   if (!ok(s->w_routed) || (s->I_shared && !ok(s->w_shared)))
-    return fail(MOE_ERR_UNSUPPORTED, "weights must be F32 with F32 activations and BF16/FP8/MXFP4 with BF16 ones");
+    return fail(MOE_ERR_UNSUPPORTED, "F32 weights go with F32 activations, every other format with BF16 ones");
   if (s->I_shared && s->w_shared == MOE_MXFP4_B32_A8)
     return fail(MOE_ERR_UNSUPPORTED, "W4A8 (MOE_MXFP4_B32_A8) applies to the routed experts only");
   if (s->w_routed == MOE_MXFP8_B32_A8)
@@ -213,6 +213,15 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
+// The kernels move activations, outputs and packed matrices with 16-byte vector loads and DMA to
+// LDS, and scales, index and weight arrays with 4-byte ones: such pointers must be aligned to that
+// (every PyTorch allocation is), or the call is refused before any launch.
+bool al16(const void* p) { return (uintptr_t)p % 16 == 0; }
+bool al4(const void* p) { return (uintptr_t)p % 4 == 0; }
+moe_status misaligned(const char* what, int bytes) {
+  return fail(MOE_ERR_INVALID_ARG, "%s must be %d-byte aligned", what, bytes);
+}
+
 moe_status check_weights(const moe_weights* w, moe_dtype fmt, const char* what) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "%s weights are NULL", what);
   if (!w->gate || !w->up || !w->down) return fail(MOE_ERR_INVALID_ARG, "%s weight pointer is NULL", what);
@@ -220,6 +229,8 @@ moe_status check_weights(const moe_weights* w, moe_dtype fmt, const char* what) 
        fmt == MOE_INT8_W8A8) &&
       (!w->gate_scale || !w->up_scale || !w->down_scale))
     return fail(MOE_ERR_INVALID_ARG, "%s scales are NULL", what);
+  if (!al16(w->gate) || !al16(w->up) || !al16(w->down)) return misaligned("packed weights", 16);
+  if (!al4(w->gate_scale) || !al4(w->up_scale) || !al4(w->down_scale)) return misaligned("packed scales", 4);
   return MOE_OK;
 }
 
@@ -492,6 +503,9 @@ moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed
   if ((s = check_weights(routed, shape->w_routed, "routed")) != MOE_OK) return s;
   if (shape->I_shared && (s = check_weights(shared, shape->w_shared, "shared")) != MOE_OK) return s;
   if (shape->T && (!x || !Wr_packed || !y)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!al16(x) || !al16(Wr_packed) || !al16(y)) return misaligned("x, Wr_packed and y", 16);
+  if (!al4(bias) || !al4(topk_idx_out) || !al4(topk_w_out)) return misaligned("bias and the routing outputs", 4);
+  if (hash && (!al4(hash->ids) || !al4(hash->table))) return misaligned("token_ids and hash_table", 4);
   Ws L;
   if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
   if (shape->T == 0) return MOE_OK;
@@ -551,6 +565,11 @@ moe_status moe_pack(moe_dtype fmt, int32_t count, int32_t K, int32_t N, const vo
   if (count == 0) return MOE_OK;
   if (!w || !packed) return fail(MOE_ERR_INVALID_ARG, "NULL matrix pointer");
   if (sb && (!scale || !packed_scale)) return fail(MOE_ERR_INVALID_ARG, "NULL scale pointer");
+  if (!al16(packed)) return misaligned("packed", 16);
+  if (!al4(packed_scale)) return misaligned("packed_scale", 4);
+  const int wal = fmt == MOE_F32 ? 4 : fmt == MOE_BF16 ? 2 : 1;  // the source's element size
+  if ((uintptr_t)w % wal) return misaligned("w", wal);
+  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_INT8_W8A8) && !al4(scale)) return misaligned("scale", 4);
   return hip_status(moe_launch_pack(stored_fmt(fmt), count, K, N, w, scale, packed, packed_scale, (hipStream_t)stream),
                     "pack");
 }
@@ -568,6 +587,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* Wr_packe
   moe_status s = check_shape(shape);
   if (s != MOE_OK) return s;
   if (shape->T && (!x || !Wr_packed || !topk_idx || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!al16(x) || !al16(Wr_packed)) return misaligned("x and Wr_packed", 16);
+  if (!al4(bias) || !al4(topk_idx) || !al4(topk_w)) return misaligned("bias, topk_idx and topk_w", 4);
   Ws L;
   if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
   return do_route(*shape, x, Wr_packed, bias, topk_idx, topk_w, ws, L, (hipStream_t)stream);
@@ -581,6 +602,9 @@ moe_status moe_route_hash(const moe_shape* shape, const void* x, const void* Wr_
   if (vocab < 1) return fail(MOE_ERR_INVALID_ARG, "vocab=%d < 1", vocab);
   if (shape->T && (!x || !Wr_packed || !token_ids || !hash_table || !topk_idx || !topk_w))
     return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!al16(x) || !al16(Wr_packed)) return misaligned("x and Wr_packed", 16);
+  if (!al4(bias) || !al4(token_ids) || !al4(hash_table) || !al4(topk_idx) || !al4(topk_w))
+    return misaligned("bias, token_ids, hash_table, topk_idx and topk_w", 4);
   Ws L;
   if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
   const HashRoute h{token_ids, hash_table, vocab};
@@ -593,6 +617,8 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
   if (s != MOE_OK) return s;
   if (!expert_offsets || (shape->T && (!topk_idx || !slot_token || !pair_slot)))
     return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!al4(topk_idx) || !al4(expert_offsets) || !al4(slot_token) || !al4(pair_slot))
+    return misaligned("the index arrays", 4);
   Ws L;
   if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
   return do_permute(*shape, topk_idx, expert_offsets, slot_token, pair_slot, ws, L, (hipStream_t)stream);
@@ -607,6 +633,8 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t*
   if (shape->I_shared && (s = check_weights(shared, shape->w_shared, "shared")) != MOE_OK) return s;
   if (shape->T && (!x || !expert_offsets || !slot_token || !y_perm || (shape->I_shared && !y_shared)))
     return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!al16(x) || !al16(y_perm) || !al16(y_shared)) return misaligned("x, y_perm and y_shared", 16);
+  if (!al4(expert_offsets) || !al4(slot_token)) return misaligned("expert_offsets and slot_token", 4);
   Ws L;
   if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
   return do_ffn(*shape, x, expert_offsets, slot_token, *routed, shared, y_perm, y_shared, ws, L, (hipStream_t)stream);
@@ -617,6 +645,8 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
   moe_status s = check_shape(shape);
   if (s != MOE_OK) return s;
   if (shape->T && (!y_perm || !pair_slot || !topk_w || !y)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!al16(y_perm) || !al16(y_shared) || !al16(y)) return misaligned("y_perm, y_shared and y", 16);
+  if (!al4(pair_slot) || !al4(topk_w)) return misaligned("pair_slot and topk_w", 4);
   return hip_status(launch_combine(shape->act, y_perm, pair_slot, topk_w, y_shared, y, shape->T, shape->H, shape->k,
                                    (hipStream_t)stream),
                     "combine");

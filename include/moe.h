@@ -25,6 +25,9 @@
  *   - Errors are returned as codes, never thrown; on an error nothing has been enqueued,
  *     except MOE_ERR_HIP (a launch failed; moe_last_error() has the runtime's message).
  *   - Row-major everywhere. Activations x, y are [T][H] in the `act` type.
+ *   - Alignment: activations, outputs (x, y, y_perm, y_shared), the packed router and packed
+ *     weight matrices are 16-byte aligned; packed scales, bias, index and routing-weight arrays
+ *     4-byte aligned (any PyTorch allocation is). A misaligned pointer is MOE_ERR_INVALID_ARG.
  *
  * Weights are read in the packed layout written by moe_pack (once, at weight-load time): see
  * moe_pack for the layout and for which logical matrix each argument is.

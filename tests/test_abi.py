@@ -173,3 +173,35 @@ def test_quantisers_validate_before_launch():
     assert lib.moe_quantize_int8(fake, 4, 8200, fake, fake, None) == 1   # K above 8192
     assert lib.moe_quantize_int8(fake, 4, 64, fake, P(0x1002), None) == 1  # scales not 4-byte aligned
     assert "aligned" in lib.moe_last_error().decode()
+
+
+def test_misaligned_pointers_are_refused_before_launch():
+    """Activations, outputs and packed matrices need 16-byte alignment (vector loads, DMA to LDS),
+    scales, index and routing-weight arrays 4-byte alignment."""
+    lib = N.load()
+    s = _shape()
+    P = ctypes.c_void_p
+    a, m8, m2 = P(0x10000), P(0x10008), P(0x10002)  # aligned, 8 off a 16-byte boundary, 2 off
+    ws = 1 << 30
+    w = N.MoeWeights(0x10000, 0x10000, 0x10000, None, None, None)
+    wm = N.MoeWeights(0x10000, 0x10008, 0x10000, None, None, None)
+    assert lib.moe_route(ctypes.byref(s), m8, a, None, a, a, a, ws, None) == 1          # x
+    assert lib.moe_route(ctypes.byref(s), a, a, m2, a, a, a, ws, None) == 1             # bias
+    assert lib.moe_permute(ctypes.byref(s), a, a, m2, a, a, ws, None) == 1              # slot_token
+    assert lib.moe_grouped_ffn(ctypes.byref(s), a, a, a, ctypes.byref(wm), None, a, None, a, ws, None) == 1
+    assert "packed weights" in lib.moe_last_error().decode()
+    assert lib.moe_grouped_ffn(ctypes.byref(s), a, a, a, ctypes.byref(w), None, m8, None, a, ws, None) == 1
+    assert lib.moe_combine(ctypes.byref(s), a, a, a, None, m8, None) == 1               # y
+    assert lib.moe_combine(ctypes.byref(s), a, m2, a, None, a, None) == 1               # pair_slot
+    assert lib.moe_layer_forward(ctypes.byref(s), a, a, None, ctypes.byref(w), None, m8, None, None,
+                                 a, ws, None) == 1                                      # y
+    assert lib.moe_layer_forward(ctypes.byref(s), a, m8, None, ctypes.byref(w), None, a, None, None,
+                                 a, ws, None) == 1                                      # Wr_packed
+    s8 = _shape(w_routed="fp8")
+    w8 = N.MoeWeights(0x10000, 0x10000, 0x10000, 0x10000, 0x10002, 0x10000)
+    assert lib.moe_layer_forward(ctypes.byref(s8), a, a, None, ctypes.byref(w8), None, a, None, None,
+                                 a, ws, None) == 1
+    assert "packed scales" in lib.moe_last_error().decode()
+    assert lib.moe_pack(N.DTYPE["bf16"], 1, 256, 128, a, None, m8, None, None) == 1     # packed
+    assert lib.moe_pack(N.DTYPE["f32"], 1, 256, 128, m2, None, a, None, None) == 1      # f32 source
+    assert lib.moe_pack(N.DTYPE["fp8"], 1, 256, 256, a, m2, a, a, None) == 1            # fp32 scales
