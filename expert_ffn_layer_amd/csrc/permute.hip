@@ -44,7 +44,7 @@ __global__ void __launch_bounds__(PTHR) perm_rank_kernel(const int32_t* __restri
     int r_in_wave = 0;
     while (pending) {
       const int leader = __ffsll((long long)pending) - 1;
-      const int ek = __shfl(e, leader, 64);
+      const int ek = __builtin_amdgcn_readlane(e, leader);  // leader is wave-uniform
       const uint64_t same = __ballot(e == ek) & pending;
       if (e == ek) r_in_wave = __popcll(same & lanemask_lt(lane));
       if (lane == leader) wcnt[wave * E + ek] = __popcll(same);
@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(SMALL_THR) permute_small_kernel(
       int r_in_wave = 0;
       while (pending) {
         const int leader = __ffsll((long long)pending) - 1;
-        const int ek = __shfl(e, leader, 64);
+        const int ek = __builtin_amdgcn_readlane(e, leader);  // leader is wave-uniform
         const uint64_t same = __ballot(e == ek) & pending;
         if (e == ek) r_in_wave = __popcll(same & lanemask_lt(lane));
         if (lane == leader) wcnt[wave * E + ek] = __popcll(same);
