@@ -616,3 +616,38 @@ def test_layer_forward_captures_into_a_graph(name, spec):
         assert torch.equal(y, y_ref), rep
         # eager work between the replays, on the same workspace
         run(spec, lay, pl)
+
+
+def test_hash_routed_forward_captures_into_a_graph():
+    """moe_layer_forward_hash captures like moe_layer_forward: every replay (with eager calls and
+    synchronisations between them) equals the eager hash-routed forward bit for bit."""
+    spec = L.LayerSpec("g6", T=45, H=512, E=12, k=3, I=256, shared=True, seed=66)
+    lay, pl = build(spec, DEV)
+    ids, table = L.hash_inputs(spec, 37)
+    ids[::9] = 40  # some ids outside the table
+    d_ids, d_tab = torch.from_numpy(ids).to(DEV), torch.from_numpy(table).to(DEV)
+    x = lay["x"].view(torch.bfloat16)
+    y_ref = torch.empty((spec.T, spec.H), dtype=torch.bfloat16, device=DEV)
+    idx_ref = torch.empty((spec.T, spec.k), dtype=torch.int32, device=DEV)
+    w_ref = torch.empty((spec.T, spec.k), dtype=torch.float32, device=DEV)
+    pl.forward_hash(x, lay["bias"], d_ids, d_tab, y_ref, idx_ref, w_ref)
+    torch.cuda.synchronize()
+    y, idx, w = torch.empty_like(y_ref), torch.empty_like(idx_ref), torch.empty_like(w_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pl.forward_hash(x, lay["bias"], d_ids, d_tab, y, idx, w)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pl.forward_hash(x, lay["bias"], d_ids, d_tab, y, idx, w)
+    for rep in range(4):
+        y.fill_(0)
+        idx.fill_(-2)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx_ref), rep
+        assert torch.equal(w, w_ref), rep
+        assert torch.equal(y, y_ref), rep
+        run(spec, lay, pl)  # eager score-routed work between the replays, on the same workspace
