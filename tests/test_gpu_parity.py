@@ -651,3 +651,31 @@ def test_hash_routed_forward_captures_into_a_graph():
         assert torch.equal(w, w_ref), rep
         assert torch.equal(y, y_ref), rep
         run(spec, lay, pl)  # eager score-routed work between the replays, on the same workspace
+
+
+# ------------------------------------------------------------------ exact ties in the router
+
+@pytest.mark.parametrize("T", [33, 2304])
+def test_router_ties_go_to_the_lower_expert_index(T):
+    """With the router matrix zeroed every score is exactly its bias, so a bias drawn from {0, 1, 2}
+    ties many experts at the k-th / (k+1)-th boundary: the k chosen are the largest scores with ties
+    to the lower index, listed in ascending index, weighted by exp(b - max) renormalised; with no
+    bias, experts 0..k-1 at 1/k each. T = 2304 takes the prefill kernel's split-K scores."""
+    spec = L.LayerSpec("tie", T=T, H=512, E=40, k=6, I=256, seed=77)
+    lay, pl = build(spec, DEV)
+    pl.Wr.zero_()
+    x = lay["x"].view(torch.bfloat16)
+    rng = np.random.default_rng(5)
+    bias = rng.integers(0, 3, size=spec.E).astype(np.float32)
+    for b in (bias, None):
+        idx = torch.empty((T, spec.k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, spec.k), dtype=torch.float32, device=DEV)
+        N.moe_route(pl.shape, x, pl.Wr, None if b is None else torch.from_numpy(b).to(DEV), idx, w, pl.ws)
+        torch.cuda.synchronize()
+        bb = np.zeros(spec.E) if b is None else b.astype(np.float64)
+        chosen = sorted(sorted(range(spec.E), key=lambda e: (-bb[e], e))[:spec.k])
+        p = np.exp(bb[chosen] - bb[chosen].max())
+        assert (idx.cpu().numpy() == np.array(chosen, np.int32)).all()
+        assert np.abs(w.cpu().numpy() - p / p.sum()).max() <= 1e-6
+        ridx, rw, _ = O.route(lay["x_host"], np.zeros_like(lay["Wr_host"]), b, spec.k, spec.act)
+        assert np.array_equal(idx.cpu().numpy(), ridx) and np.abs(w.cpu().numpy() - rw).max() <= 1e-6
