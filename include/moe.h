@@ -196,9 +196,11 @@ moe_status moe_route_hash(const moe_shape* shape, const void* x, const void* Wr_
 /*
  * moe_permute — stable counting sort of the pairs q = t*k + j by expert [ch6 §6.2.6].
  *   topk_idx       int32[T*k] in: values in [0, E) (entries outside are skipped)
- *   expert_offsets int32[E+1] out: rows of expert e are [off[e], off[e+1]); off[E] = T*k
- *   slot_token     int32[T*k] out: token of each row (slot)
- *   pair_slot      int32[T*k] out: row of each pair
+ *   expert_offsets int32[E+1] out: rows of expert e are [off[e], off[e+1]); off[E] = the number
+ *                  of pairs with a valid expert (T*k when none is skipped)
+ *   slot_token     int32[T*k] out: token of each row (slot); entries from off[E] on are not
+ *                  written
+ *   pair_slot      int32[T*k] out: row of each pair, -1 for a skipped pair
  * Deterministic: no atomics decide an order.
  */
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx,
@@ -212,9 +214,11 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx,
  *   expert_offsets, slot_token: from moe_permute
  *   routed         packed routed weights (E experts)
  *   shared         packed shared weights, or NULL when I_shared == 0
- *   y_perm         [T*k][H] act out: row r = FFN_e(x[slot_token[r]]) for the e owning r
+ *   y_perm         [T*k][H] act out: row r = FFN_e(x[slot_token[r]]) for the e owning r (rows
+ *                  from expert_offsets[E] on, those of skipped pairs, are not written)
  *   y_shared       [T][H] act out (NULL when I_shared == 0)
- * The intermediate SiLU(x Wg) (.) (x Wu) is kept in `ws` in the act type; accumulation fp32.
+ * The intermediate h = SiLU(x Wg) (.) (x Wu) is kept in `ws` in the act type (for the MXFP8 and
+ * INT8 formats also, or only, as the codes and scales the down product reads); accumulation fp32.
  */
 moe_status moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
                            const int32_t* slot_token, const moe_weights* routed,
@@ -224,7 +228,10 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t*
 /*
  * moe_combine — y[t] = sum_{j<k} topk_w[t][j] * y_perm[pair_slot[t*k+j]] + y_shared[t], summed
  * in ascending j in fp32, one gather per output row, no atomics [ch6 §6.2.6, §6.4.1].
- *   y_shared may be NULL.
+ *   y_perm     [T*k][H] act, pair_slot int32[T*k], topk_w float[T][k] (from moe_grouped_ffn,
+ *              moe_permute and moe_route); a pair whose pair_slot is outside [0, T*k) adds nothing
+ *   y_shared   [T][H] act, or NULL
+ *   y          [T][H] act out
  */
 moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* pair_slot,
                        const float* topk_w, const void* y_shared, void* y, moe_stream_t stream);
