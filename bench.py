@@ -29,6 +29,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "int8": 5000.0}
 TRAFFIC = {
     # gate/up decode kernel
     "c2": {"sha": "24c0fd2cc318dc45", "bytes": 3176791832},
+    "c3": {"sha": "24c0fd2cc318dc45", "bytes": 14695798301},
+    "c4": {"sha": "24c0fd2cc318dc45", "bytes": 3676200475},
     # gate/up prefill kernel
     "c5": {"sha": "e0463fd1be82c895", "bytes": 16306116370},
     # the W4A8 gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared bf16 GEMM
