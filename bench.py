@@ -372,7 +372,13 @@ def cpu_baseline(spec, lay, S):
     for tkn in range(S):
         O.combine_token(wts[tkn], yperm[ps[tkn * spec.k:(tkn + 1) * spec.k]], None if ysh is None else ysh[tkn])
     dt = time.perf_counter() - t
-    return {"value": round(S / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": round(S / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu,
             "sample": "first %d of %d tokens of the same layer (route, permute, %d active experts' SwiGLU%s, "
                       "combine), fp64 C oracle, %.1f s" % (S, spec.T, len(need),
                                                            " + shared expert" if spec.shared else "", dt)}
