@@ -26,6 +26,8 @@
  *   1. router scores l[t][e] = sum_h x[t][h] Wr[h][e] (+ b[e])       [ch6 §6.2.6; V4 step D4]
  *   2. the k largest scores per token, ties to the lower expert index, listed in ascending
  *      expert index                                                  [V4 step D4 "top-6"]
+ *   2'. or, with hash routing, the k experts are row token_id[t] of a [vocab][k] table; entries
+ *      outside [0, E) are dropped                          [CANN DeepSeek-V4 page, MoE section]
  *   3. weights: softmax over all E scores, renormalised over the k selected
  *      (a1, a6 of the token-A example)                               [ch6 §6.2.6]
  *   4. permutation: rows regrouped by expert, stable in token order  [ch6 §6.2.6, receiver side]
