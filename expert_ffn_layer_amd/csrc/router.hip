@@ -3,9 +3,11 @@
 // Chapter 6 'Supernodes' section 6.2.6: the routing weights a_e of the combine).
 //
 // One wave per token. Each lane holds scores e = lane, lane + 64, ... (the sum of the split-K
-// partial scores, in a fixed order); k rounds of a wave-wide arg-max (ties to the lower index)
-// pick the experts; they are then listed in ascending expert index. The weights are exp(l - m) / sum over the chosen of exp(l - m) with
-// m the largest score, which equals the softmax over all E renormalised over the chosen k.
+// partial scores, in a fixed order). The k-th largest score is found by a bitwise search over
+// order keys with wave ballot counts; the experts above it, and the lowest-indexed ones equal to
+// it, are chosen (ties to the lower index) and listed in ascending expert index. The weights are
+// exp(l - m) / sum over the chosen of exp(l - m) with m the largest score, which equals the
+// softmax over all E renormalised over the chosen k.
 //
 // Hash routing ('CANN DeepSeek-V4推理优化', MoE section: the first layers route by hash) replaces
 // the arg-max rounds: the experts are row token_ids[t] of a [vocab][k] table, each score fetched
@@ -19,10 +21,6 @@ namespace moe {
 
 constexpr int TOPK_MAX = 16;
 constexpr int PER_LANE_MAX = 16;  // E <= 1024
-
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
 
 template <int PL, bool HASH>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int ldl, long long part_stride,
@@ -113,50 +111,64 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     }
     return;
   }
+  // Selection without moving data between lanes. Each score gets an order key (a monotone map of
+  // the float to uint32; padding experts get 0, below every real score). The k-th largest key K
+  // is built bit by bit from the top: a candidate bit stays when at least k keys reach the
+  // candidate, counted with wave ballots. The experts above K are chosen, and the lowest-indexed
+  // experts equal to K fill the remaining places (ties to the lower index).
+  uint32_t key[PL];
 #pragma unroll
-  for (int r = 0; r < TOPK_MAX; ++r) {
-    sel[r] = 0x7fffffff;
-    sv[r] = NEG;
-    if (r < k) {
-      // lane-local best, then a butterfly arg-max across the wave (uniform result)
-      float bv = NEG;
-      int bi = 0x7fffffff;
+  for (int j = 0; j < PL; ++j) {
+    const uint32_t u = __float_as_uint(v[j] + 0.0f);  // -0 -> +0: equal scores, equal keys
+    key[j] = lane + 64 * j < E ? ((u >> 31) ? ~u : (u | 0x80000000u)) : 0u;
+  }
+  uint32_t K = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = K | (1u << b);
+    int n = 0;
 #pragma unroll
-      for (int j = 0; j < PL; ++j) {
-        const int e = lane + 64 * j;
-        if (e < E && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
-      }
+    for (int j = 0; j < PL; ++j) n += __popcll(__ballot(key[j] >= c));
+    if (n >= k) K = c;
+  }
+  uint64_t pick[PL];
+  int need = k;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      sel[r] = bi;
-      sv[r] = bv;
+  for (int j = 0; j < PL; ++j) {
+    pick[j] = __ballot(key[j] > K);
+    need -= __popcll(pick[j]);
+  }
 #pragma unroll
-      for (int j = 0; j < PL; ++j)
-        if (bi == lane + 64 * j) v[j] = NEG;
+  for (int j = 0; j < PL; ++j) {
+    uint64_t eq = __ballot(key[j] == K);
+    while (need > 0 && eq) {  // wave-uniform
+      const uint64_t low = eq & (~eq + 1);
+      pick[j] |= low;
+      eq ^= low;
+      --need;
     }
   }
-  // weights relative to the largest score sv[0]; lane r < k writes pick r at its rank by index
-  float z = 0.0f, mine_p = 0.0f;
-  int mine = 0x7fffffff;
+  // the largest chosen score, then the weights' sum, both over the chosen in ascending expert
+  // index (each score read from the lane that holds it)
+  float m = NEG;
 #pragma unroll
-  for (int r = 0; r < TOPK_MAX; ++r) {
-    if (r < k) {
-      const float p = __expf(sv[r] - sv[0]);
-      z += p;
-      if (r == lane) { mine = sel[r]; mine_p = p; }
+  for (int j = 0; j < PL; ++j)
+    for (uint64_t bits = pick[j]; bits; bits &= bits - 1)
+      m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), __ffsll((long long)bits) - 1)));
+  float z = 0.0f;
+#pragma unroll
+  for (int j = 0; j < PL; ++j)
+    for (uint64_t bits = pick[j]; bits; bits &= bits - 1)
+      z += __expf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), __ffsll((long long)bits) - 1)) - m);
+  // each chosen expert's lane writes it at its rank among the chosen (ascending index)
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    if ((pick[j] >> lane) & 1ull) {
+      const int rank = base + __popcll(pick[j] & (lane ? (~0ull >> (64 - lane)) : 0ull));
+      idx[(size_t)t * k + rank] = lane + 64 * j;
+      wout[(size_t)t * k + rank] = __expf(v[j] - m) / z;
     }
-  }
-  if (lane < k) {
-    int rank = 0;
-#pragma unroll
-    for (int r = 0; r < TOPK_MAX; ++r)
-      if (r < k && sel[r] < mine) ++rank;
-    idx[(size_t)t * k + rank] = mine;
-    wout[(size_t)t * k + rank] = mine_p / z;
+    base += __popcll(pick[j]);
   }
 }
 
