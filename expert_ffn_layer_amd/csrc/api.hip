@@ -79,6 +79,12 @@ moe_status check_shape(const moe_shape* s) {
   if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", s->E);
   if (s->k < 1 || s->k > s->E || s->k > 16) return fail(MOE_ERR_INVALID_ARG, "k=%d outside [1, min(E, 16)]", s->k);
   if ((long long)s->T * s->k + s->T > 0x7fffffffLL / 2) return fail(MOE_ERR_INVALID_ARG, "T*k too large");
+  // The plan's block table keeps a row block's place in its group in 16 bits. A group holds at
+  // most T*k rows (hash routing may repeat an expert within a token; the shared group holds T),
+  // cut into 64-row blocks on the decode kernel (128 on the prefill one).
+  if ((long long)s->T * s->k > 65535LL * ROW_BLOCK)
+    return fail(MOE_ERR_UNSUPPORTED, "T*k=%lld: a group of more than %lld rows overflows the plan's block index",
+                (long long)s->T * s->k, 65535LL * ROW_BLOCK);
   if (s->I_shared != 0 && s->I_shared != s->I)
     return fail(MOE_ERR_UNSUPPORTED, "I_shared=%d: only 0 or I (=%d) is supported", s->I_shared, s->I);
   if (s->act != MOE_F32 && s->act != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "act must be F32 or BF16");

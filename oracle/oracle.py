@@ -14,7 +14,13 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "moe_oracle.c")
-LIB = os.path.join(HERE, "libmoe_oracle.so")
+# MOE_ORACLE_SANITIZE=1 selects a separate build with AddressSanitizer and UndefinedBehaviorSanitizer
+# (CPU only; any finding aborts), loaded in a process that preloads the sanitizer runtimes
+SANITIZE = os.environ.get("MOE_ORACLE_SANITIZE") == "1"
+LIB = os.path.join(HERE, "libmoe_oracle_san.so" if SANITIZE else "libmoe_oracle.so")
+CFLAGS = ["-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall"]
+SAN_CFLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+              "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall"]
 
 FMT = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "mxfp4a8": 4, "mxfp8a8": 5, "int8": 6}
 
@@ -22,11 +28,10 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (plain C, OpenMP)."""
+    """Compile the oracle with gcc (plain C, OpenMP; the sanitizer build when SANITIZE)."""
     if force or not os.path.exists(LIB):
         tmp = LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99",
-                               "-Wall", "-o", tmp, SRC, "-lm"])
+        subprocess.check_call(["gcc", *(SAN_CFLAGS if SANITIZE else CFLAGS), "-o", tmp, SRC, "-lm"])
         os.replace(tmp, LIB)
     return LIB
 

@@ -14,9 +14,16 @@ from inputgen import gpu as G
 from inputgen import layers as L
 from oracle import oracle as O
 
-# W4A8 is held to the bf16 bar: its oracle performs the same MXFP8 quantisation, so only
-# accumulation order and rounding of h / y differ
-TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 4e-2, "mxfp4": 4e-2, "mxfp4a8": 1e-2, "mxfp8a8": 1e-2, "int8": 1e-2}
+# The bounds the layer is specified to: relative Frobenius error 1e-2 for bf16 (and the fp32
+# layer), 4e-2 for the fp8 and MXFP4 weight formats.
+SPEC_TOL = {"f32": 1e-2, "bf16": 1e-2, "fp8": 4e-2, "mxfp4": 4e-2, "mxfp4a8": 4e-2, "mxfp8a8": 4e-2, "int8": 4e-2}
+# The bounds the tests hold the GPU path to. Every format is held to the bf16 bar or tighter: the
+# fp8 and MXFP4 weights are converted exactly (prefill) or each rounded once to bf16 (fp8 on the
+# decode kernel), W4A8, W8A8 MXFP8 and Int8 W8A8 quantise their activations exactly as their
+# oracle does, so what differs is accumulation order and the bf16 rounding of h and y. The
+# observed errors are 2e-3 to 4e-3; a mis-indexed block scale or exponent byte moves them far
+# past 1e-2. The fp32 layer is fp32 end to end.
+TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2, "mxfp4": 1e-2, "mxfp4a8": 1e-2, "mxfp8a8": 1e-2, "int8": 1e-2}
 
 
 def say(*a):
@@ -29,6 +36,11 @@ def tol_of(spec):
     if spec.act == "f32":
         return TOL["f32"]
     return max(TOL[f] for f in fmts)
+
+
+def spec_tol_of(spec):
+    fmts = [spec.w_routed] + ([spec.w_shared] if spec.shared else [])
+    return max(SPEC_TOL[f] for f in fmts)
 
 
 def rel_fro(a, b):
@@ -83,13 +95,15 @@ def oracle_full(spec, lay):
     return O.layer(spec, lay["x_host"], lay["Wr_host"], lay["bias_host"], routed, shared)
 
 
-def oracle_tokens(spec, lay, idx, w, tokens, threads=16):
-    """Oracle output rows for the listed tokens, given the oracle's routing (idx, w)."""
-    need = sorted({int(e) for t in tokens for e in idx[t]})
-    routed = host_weights(lay["routed"], need)
+def oracle_ffn_rows(spec, lay, jobs, threads=16):
+    """The oracle's expert FFN of single token rows: jobs is a list of (token, expert), expert -1
+    naming the shared expert; returns {job: output row (float64[H])}. Each row is computed alone
+    (one row's FFN does not depend on the others), the jobs spread over host threads."""
+    need = sorted({e for _, e in jobs if e >= 0})
+    routed = host_weights(lay["routed"], need) if need else None
     pos = {e: i for i, e in enumerate(need)}
     shared = None
-    if spec.shared:
+    if spec.shared and any(e < 0 for _, e in jobs):
         shared = {k: (None if v is None else v[0]) for k, v in host_weights(lay["shared"]).items()}
     u = L.act_to_f64(lay["x_host"], spec.act)
 
@@ -99,9 +113,15 @@ def oracle_tokens(spec, lay, idx, w, tokens, threads=16):
         one = {k: (None if v is None else v[pos[e]]) for k, v in routed.items()}
         return O.expert_ffn(u[t:t + 1], one, spec.w_routed)[0]
 
-    jobs = [(t, int(e)) for t in tokens for e in idx[t]] + ([(t, -1) for t in tokens] if spec.shared else [])
+    jobs = list(dict.fromkeys(jobs))
     with ThreadPoolExecutor(threads) as ex:
-        res = dict(zip(jobs, ex.map(lambda j: ffn(*j), jobs)))
+        return dict(zip(jobs, ex.map(lambda j: ffn(*j), jobs)))
+
+
+def oracle_tokens(spec, lay, idx, w, tokens, threads=16):
+    """Oracle output rows for the listed tokens, given the oracle's routing (idx, w)."""
+    jobs = [(t, int(e)) for t in tokens for e in idx[t]] + ([(t, -1) for t in tokens] if spec.shared else [])
+    res = oracle_ffn_rows(spec, lay, jobs, threads)
     out = []
     for t in tokens:
         yk = np.stack([res[(t, int(e))] for e in idx[t]])

@@ -59,6 +59,8 @@ def _shape(**kw):
     (dict(H=512, I=256, I_shared=256, w_routed="int8", w_shared="bf16"), 2),
     (dict(H=512, I=256, I_shared=256, w_routed="bf16", w_shared="int8"), 2),
     (dict(H=256, I=256, w_routed="int8"), 2),
+    # a group of more than 65535 64-row blocks (the plan's block index): T*k above 4194240
+    (dict(T=524281, k=8), 2),
 ])
 def test_shape_validation(kw, status):
     with pytest.raises(N.MoeError) as e:
@@ -93,6 +95,11 @@ def test_int8_shape_is_accepted_with_and_without_a_shared_expert():
     assert N.moe_workspace_size(_shape(H=512, I=256, w_routed="int8")) > 0
     assert N.moe_workspace_size(_shape(H=512, I=256, I_shared=256, w_routed="int8", w_shared="int8")) > \
         N.moe_workspace_size(_shape(H=512, I=256, w_routed="int8"))
+
+
+def test_largest_plannable_routing_is_accepted():
+    # T*k = 65535 * 64 exactly: every group's blocks fit the plan's 16-bit index
+    assert N.moe_workspace_size(_shape(T=65535 * 8, k=8)) > 0
 
 
 def test_workspace_grows_with_tokens_and_shared_expert():

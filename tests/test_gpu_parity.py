@@ -13,7 +13,8 @@ from inputgen import layers as L
 from inputgen import philox as px
 from oracle import oracle as O
 
-from _gpu import build, host_weights, oracle_full, oracle_tokens, rel_fro, run, say, to_f64, tol_of
+from _gpu import (build, host_weights, oracle_ffn_rows, oracle_full, oracle_tokens, rel_fro, run, say, spec_tol_of,
+                  to_f64, tol_of)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -296,13 +297,36 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
 # (MXFP8 activations on the block-scaled MFMA); and the hybrid MXFP8-MXFP4 layer (W4A8 routed, W8A8
 # MXFP8 shared); the DeepSeek-V3-shaped prefill layer with Int8 W8A8 experts
 FULL = ["c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8", "c4-w4a8", "c4-mx", "c3-int8"]
+# decode layers whose every output token is compared (the kernel widths the benchmark runs: bf16
+# gate/up with 16-feature tiles and down with 64 at H = 4096; MXFP4, W4A8 and the hybrid scheme at
+# H = 7168)
+ALL_TOKENS = {"c2", "c4", "c4-w4a8", "c4-mx"}
+
+
+def boundary_tokens(spec, roff, rst, block, groups=None):
+    """Tokens of the first and last row of every `block`-row block of the listed groups (all
+    routed groups when None), and of the shared group's blocks (rows in token order)."""
+    E = spec.E
+    out = set()
+    for g in (range(E) if groups is None else groups):
+        r0, r1 = int(roff[g]), int(roff[g + 1])
+        for b0 in range(r0, r1, block):
+            out.add(int(rst[b0]))
+            out.add(int(rst[min(b0 + block, r1) - 1]))
+    if spec.shared:
+        for b0 in range(0, spec.T, block):
+            out.add(b0)
+            out.add(min(b0 + block, spec.T) - 1)
+    return out
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("cfg", FULL)
 def test_full_size_layer(cfg):
     """The bench's launch configuration at full size: routing and permutation identical for
-    every token, outputs against the oracle on sampled tokens."""
+    every token; outputs against the oracle on every token of the Qwen3 and V4-Pro decode layers,
+    on the block boundaries of every group of more than one 64-row block of the V3 decode layers,
+    and on a sample of the prefill layers (whose row tiles the next test covers group by group)."""
     spec = L.workload(cfg)
     say("full-size", cfg, spec)
     lay, pl = build(spec, DEV)
@@ -324,12 +348,94 @@ def test_full_size_layer(cfg):
     counts = np.diff(roff)
     hot = int(np.argmax(counts))
     rng = np.random.default_rng(7)
-    tokens = sorted({0, spec.T - 1, int(rst[roff[hot]]), *rng.choice(spec.T, 5, replace=False).tolist()})
-    say("  active experts %d, max rows %d; oracle on tokens %s" % ((counts > 0).sum(), counts.max(), tokens))
+    if cfg in ALL_TOKENS:
+        tokens = list(range(spec.T))
+    elif spec.T <= 256:
+        thick = [g for g in range(spec.E) if counts[g] > 64]
+        tokens = sorted(boundary_tokens(spec, roff, rst, 64, thick) | set(rng.choice(spec.T, 8, replace=False).tolist()))
+    else:
+        tokens = sorted({0, spec.T - 1, int(rst[roff[hot]]), int(rst[roff[hot + 1] - 1]),
+                         *rng.choice(spec.T, 8, replace=False).tolist()})
+    say("  active experts %d, max rows %d; oracle on %d tokens" % ((counts > 0).sum(), counts.max(), len(tokens)))
     ref = oracle_tokens(spec, lay, ridx, rw, tokens)
     err = rel_fro(to_f64(y)[tokens], ref)
-    say("  rel. Frobenius error on sampled tokens %.3e (bound %.0e)" % (err, tol_of(spec)))
+    say("  rel. Frobenius error on %d tokens %.3e (bound %.0e; specified %.0e)"
+        % (len(tokens), err, tol_of(spec), spec_tol_of(spec)))
     assert err <= tol_of(spec)
+    # no token far off either: the worst token's own error within the bound
+    worst = max(rel_fro(to_f64(y)[t], r) for t, r in zip(tokens, ref))
+    say("  worst single-token error %.3e" % worst)
+    assert worst <= 2 * tol_of(spec)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", ["c5"])
+def test_full_size_prefill_rows_group_by_group(cfg):
+    """The prefill layer's grouped FFN at full size, row tile by row tile: with the oracle's
+    routing and permutation, the first and last row of every group, the first row of its last
+    128-row block (the ragged tile: a half item or the last full item) and the same rows of the
+    shared group are compared with the oracle's FFN of that row alone."""
+    spec = L.workload(cfg)
+    say("prefill rows", cfg, spec)
+    lay, pl = build(spec, DEV)
+    ridx, rw, _ = O.route(lay["x_host"], lay["Wr_host"], lay["bias_host"], spec.k, spec.act)
+    roff, rst, rps = O.permute(ridx, spec.E)
+    T, k, H = spec.T, spec.k, spec.H
+    x = lay["x"].view(torch.bfloat16)
+    yp = torch.empty((T * k, H), dtype=torch.bfloat16, device=DEV)
+    ysh = torch.empty((T, H), dtype=torch.bfloat16, device=DEV) if spec.shared else None
+    N.moe_grouped_ffn(pl.shape, x, torch.from_numpy(roff).to(DEV), torch.from_numpy(rst).to(DEV), pl.routed,
+                      pl.shared, yp, ysh, pl.ws)
+    torch.cuda.synchronize()
+    rows = []  # (slot or -1 - token for the shared rows, token, expert)
+    for g in range(spec.E):
+        r0, r1 = int(roff[g]), int(roff[g + 1])
+        if r1 > r0:
+            for r in sorted({r0, r0 + 128 * ((r1 - r0 - 1) // 128), r1 - 1}):
+                rows.append((r, int(rst[r]), g))
+    if spec.shared:
+        for t in sorted({0, 128 * ((T - 1) // 128), T - 1}):
+            rows.append((-1 - t, t, -1))
+    say("  %d rows over %d groups" % (len(rows), int((np.diff(roff) > 0).sum()) + (1 if spec.shared else 0)))
+    res = oracle_ffn_rows(spec, lay, [(t, e) for _, t, e in rows])
+    got = np.stack([to_f64(yp[r]) if r >= 0 else to_f64(ysh[-1 - r]) for r, _, _ in rows])
+    ref = np.stack([res[(t, e)] for _, t, e in rows])
+    err = rel_fro(got, ref)
+    worst = max(rel_fro(a, b) for a, b in zip(got, ref))
+    say("  rel. Frobenius error %.3e, worst row %.3e (bound %.0e)" % (err, worst, tol_of(spec)))
+    assert err <= tol_of(spec) and worst <= 2 * tol_of(spec)
+
+
+# layers at the V3 decode layer's width (H = 7168, I = 2048) on the decode kernel with a few
+# experts, so every group spans several 64-row blocks with a ragged last one: the gate/up widths
+# of the V3 decode layers (16 features, bf16 and int8), down at 32 (bf16) and 64 (int8) features,
+# four row tiles per block; every token compared
+MID = [
+    ("mid-bf16", L.LayerSpec("m1", T=200, H=7168, E=6, k=2, I=2048, shared=True, router="zipf", zipf_alpha=1.0,
+                             calib_tokens=512, seed=81)),
+    ("mid-int8", L.LayerSpec("m2", T=200, H=7168, E=6, k=2, I=2048, shared=True, w_routed="int8", w_shared="int8",
+                             router="zipf", zipf_alpha=1.0, calib_tokens=512, seed=82)),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,spec", MID, ids=[m[0] for m in MID])
+def test_decode_widths_every_token(name, spec):
+    say("mid", name, spec)
+    lay, pl = build(spec, DEV, "decode")
+    y, idx, w = run(spec, lay, pl)
+    ridx, rw, _ = O.route(lay["x_host"], lay["Wr_host"], lay["bias_host"], spec.k, spec.act)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-5
+    counts = np.bincount(ridx.reshape(-1), minlength=spec.E)
+    say("  group rows %s" % counts.tolist())
+    assert counts.max() > 128  # several 64-row blocks in one group
+    tokens = list(range(spec.T))
+    ref = oracle_tokens(spec, lay, ridx, rw, tokens)
+    err = rel_fro(to_f64(y), ref)
+    worst = max(rel_fro(to_f64(y)[t], ref[t]) for t in tokens)
+    say("  rel. Frobenius error %.3e, worst token %.3e (bound %.0e)" % (err, worst, tol_of(spec)))
+    assert err <= tol_of(spec) and worst <= 2 * tol_of(spec)
 
 
 # ------------------------------------------------------------------ seeded sweep of random small layers
@@ -655,18 +761,41 @@ def test_hash_routed_forward_captures_into_a_graph():
 
 # ------------------------------------------------------------------ exact ties in the router
 
+def _tie_bias(E, k, rng):
+    """Bias levels for a zeroed router: a few experts (fewer than k) at level 2, in the upper
+    64-expert slices; a tied level-1 set spread over every slice, larger than the places left;
+    the rest 0. The k-th place then falls inside the level-1 tie, and the lowest-indexed tied
+    experts that fill it lie in more than one slice (scores e, e + 64, ... share a lane)."""
+    b = np.zeros(E, np.float32)
+    if E <= 64:
+        b[:] = rng.integers(0, 3, size=E)
+        return b
+    n2 = max(1, k // 3)
+    top = rng.choice(np.arange(E // 2, E), n2, replace=False)
+    b[top] = 2.0
+    stride = max(1, (E - 20) // (3 * k))
+    tied = [e for e in range(20, E, stride) if b[e] == 0][:3 * k]
+    b[tied] = 1.0
+    need = k - n2
+    assert len(tied) > need and tied[need - 1] >= 64  # the chosen tied experts straddle a slice boundary
+    return b
+
+
 @pytest.mark.parametrize("T", [33, 2304])
-def test_router_ties_go_to_the_lower_expert_index(T):
-    """With the router matrix zeroed every score is exactly its bias, so a bias drawn from {0, 1, 2}
-    ties many experts at the k-th / (k+1)-th boundary: the k chosen are the largest scores with ties
-    to the lower index, listed in ascending index, weighted by exp(b - max) renormalised; with no
-    bias, experts 0..k-1 at 1/k each. T = 2304 takes the prefill kernel's split-K scores."""
-    spec = L.LayerSpec("tie", T=T, H=512, E=40, k=6, I=256, seed=77)
+@pytest.mark.parametrize("E,k", [(40, 6), (300, 7), (1024, 16)])
+def test_router_ties_go_to_the_lower_expert_index(T, E, k):
+    """With the router matrix zeroed every score is exactly its bias, so tied biases put many
+    experts at the k-th / (k+1)-th boundary: the k chosen are the largest scores with ties to the
+    lower index, listed in ascending index, weighted by exp(b - max) renormalised; with no bias,
+    experts 0..k-1 at 1/k each. The tied experts that fill the last places straddle the 64-expert
+    slices a lane's scores come in (E = 300, 1024). T = 2304 takes the prefill kernel's split-K
+    scores."""
+    spec = L.LayerSpec("tie", T=T, H=512, E=E, k=k, I=256, seed=77)
     lay, pl = build(spec, DEV)
     pl.Wr.zero_()
     x = lay["x"].view(torch.bfloat16)
-    rng = np.random.default_rng(5)
-    bias = rng.integers(0, 3, size=spec.E).astype(np.float32)
+    rng = np.random.default_rng(5 + E)
+    bias = _tie_bias(E, k, rng)
     for b in (bias, None):
         idx = torch.empty((T, spec.k), dtype=torch.int32, device=DEV)
         w = torch.empty((T, spec.k), dtype=torch.float32, device=DEV)
