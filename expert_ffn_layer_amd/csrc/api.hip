@@ -155,9 +155,13 @@ RouterPlan router_plan(const moe_shape& s) {
 }
 
 struct Ws {
-  size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, group_range, cum_blocks, block_group, zero, h,
-      y_perm, y_shared, xq, xs, hq, hs, total;
+  size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, fhist, done, group_range, cum_blocks,
+      block_group, zero, h, y_perm, y_shared, xq, xs, hq, hs, total;
 };
+
+// Decode batches route, permute and plan in one launch after the router scores (on the decode
+// kernel, which clears the launch's completion count).
+bool use_fused_route(const moe_shape& s) { return !router_plan(s).prefill && topk_permute_ok(s.T, s.k, s.E); }
 
 Ws ws_layout(const moe_shape& s) {
   const size_t P = (size_t)s.T * s.k, S = s.I_shared ? 1 : 0, R = P + S * s.T;
@@ -177,6 +181,9 @@ Ws ws_layout(const moe_shape& s) {
   w.pair_slot = take(P * 4);
   w.rank = take(P * 4);
   w.hist = take((size_t)permute_blocks((int)P) * s.E * 4);
+  // the fused route-permute launch: per workgroup of 16 tokens an expert histogram, and its count
+  w.fhist = take(use_fused_route(s) ? (size_t)((s.T + 15) / 16) * s.E * 4 : 0);
+  w.done = take(4);
   w.group_range = take(((size_t)s.E + 1) * 8);
   w.cum_blocks = take(((size_t)s.E + 2) * 4);
   // one entry per row block: at most one partial block per group plus the full ones (64-row
@@ -247,10 +254,10 @@ struct HashRoute {
   int vocab;
 };
 
-// moe_route (or moe_route_hash, with `hash`) without the argument checks.
-moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const float* bias, int32_t* idx,
-                    float* w, void* ws, const Ws& L, hipStream_t st, const HashRoute* hash = nullptr) {
-  if (s.T == 0) return MOE_OK;
+// The router scores into the workspace (split-K fp32 partials of the padded experts); `clear`:
+// a word the decode score kernel sets to 0. Returns the row stride of the partials in *ldl.
+moe_status do_scores(const moe_shape& s, const void* x, const void* Wr, void* ws, const Ws& L, hipStream_t st,
+                     int* ldl, uint32_t* clear = nullptr) {
   const RouterPlan rp = router_plan(s);
   // scores of the padded experts: 256-wide MFMA tiles on the prefill kernel, 64 on the decode one
   const int Ep = rp.prefill ? pad256(s.E) : pad64(s.E);
@@ -272,11 +279,23 @@ moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const flo
   a.out = at<float>(ws, L.logits);
   a.ldo = Ep;
   a.ksplit = rp.ksplit;
-  hipError_t e = rp.prefill ? launch_prefill_scores(a, st)
-                            : launch_grouped_decode(s.act, EPI_F32, s.act, s.act, a, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st);
-  if (e != hipSuccess) return hip_status(e, "router scores");
-  e = launch_topk(at<float>(ws, L.logits), Ep, a.ksplit, bias, s.T, s.E, s.k, hash ? hash->ids : nullptr,
-                  hash ? hash->table : nullptr, hash ? hash->vocab : 0, idx, w, st);
+  a.clear_word = clear;
+  if (clear && rp.prefill) return fail(MOE_ERR_HIP, "internal: the prefill score kernel clears no word");
+  *ldl = Ep;
+  return hip_status(rp.prefill ? launch_prefill_scores(a, st)
+                               : launch_grouped_decode(s.act, EPI_F32, s.act, s.act, a, (s.T + ROW_BLOCK - 1) / ROW_BLOCK, st),
+                    "router scores");
+}
+
+// moe_route (or moe_route_hash, with `hash`) without the argument checks.
+moe_status do_route(const moe_shape& s, const void* x, const void* Wr, const float* bias, int32_t* idx,
+                    float* w, void* ws, const Ws& L, hipStream_t st, const HashRoute* hash = nullptr) {
+  if (s.T == 0) return MOE_OK;
+  int ldl;
+  moe_status rs = do_scores(s, x, Wr, ws, L, st, &ldl);
+  if (rs != MOE_OK) return rs;
+  hipError_t e = launch_topk(at<float>(ws, L.logits), ldl, router_plan(s).ksplit, bias, s.T, s.E, s.k,
+                             hash ? hash->ids : nullptr, hash ? hash->table : nullptr, hash ? hash->vocab : 0, idx, w, st);
   return hip_status(e, hash ? "hash routing" : "router top-k");
 }
 
@@ -310,6 +329,34 @@ moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int3
 
 moe_status record(hipEvent_t ev, hipStream_t st) {
   return ev ? hip_status(hipEventRecord(ev, st), "event record") : MOE_OK;
+}
+
+// Route and permute (and, for the layer, the decode plan). Decode batches run the scores, then the
+// selection, permutation and plan in one launch; other shapes route and permute as moe_route and
+// moe_permute do. ev (optional): ev[1] is recorded after the scores (fused) or the routing.
+moe_status do_route_permute(const moe_shape& s, const void* x, const void* Wr, const float* bias, int32_t* idx,
+                            float* w, int32_t* off, int32_t* slot_token, int32_t* pair_slot, void* ws, const Ws& L,
+                            hipStream_t st, hipEvent_t const* ev, const HashRoute* hash, bool* planned) {
+  moe_status rs;
+  *planned = false;
+  if (s.T == 0) return do_permute(s, idx, off, slot_token, pair_slot, ws, L, st);
+  if (!use_fused_route(s)) {
+    if ((rs = do_route(s, x, Wr, bias, idx, w, ws, L, st, hash)) != MOE_OK) return rs;
+    if (ev && (rs = record(ev[1], st)) != MOE_OK) return rs;
+    return do_permute(s, idx, off, slot_token, pair_slot, ws, L, st, true, planned);
+  }
+  int ldl;
+  uint32_t* done = at<uint32_t>(ws, L.done);
+  if ((rs = do_scores(s, x, Wr, ws, L, st, &ldl, done)) != MOE_OK) return rs;
+  if (ev && (rs = record(ev[1], st)) != MOE_OK) return rs;
+  const hipError_t e = launch_topk_permute(
+      at<float>(ws, L.logits), ldl, router_plan(s).ksplit, bias, s.T, s.E, s.k, hash ? hash->ids : nullptr,
+      hash ? hash->table : nullptr, hash ? hash->vocab : 0, idx, w, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.fhist),
+      done, s.I_shared ? 1 : 0, ROW_BLOCK, off, slot_token, pair_slot, at<int32_t>(ws, L.group_range),
+      at<int32_t>(ws, L.cum_blocks), at<int32_t>(ws, L.block_group), st);
+  if ((rs = hip_status(e, hash ? "hash routing and permutation" : "router top-k and permutation")) != MOE_OK) return rs;
+  *planned = true;
+  return MOE_OK;
 }
 
 // ev (optional, 3 events): recorded after the plan, after gate/up and after down.
@@ -523,10 +570,10 @@ moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed
   void* y_perm = at<void>(ws, L.y_perm);
   void* y_sh = shape->I_shared ? at<void>(ws, L.y_shared) : nullptr;
   if (ev && (s = record(ev[0], st)) != MOE_OK) return s;
-  if ((s = do_route(*shape, x, Wr_packed, bias, idx, w, ws, L, st, hash)) != MOE_OK) return s;
-  if (ev && (s = record(ev[1], st)) != MOE_OK) return s;
   bool planned = false;
-  if ((s = do_permute(*shape, idx, off, slot_token, pair_slot, ws, L, st, true, &planned)) != MOE_OK) return s;
+  if ((s = do_route_permute(*shape, x, Wr_packed, bias, idx, w, off, slot_token, pair_slot, ws, L, st, ev, hash,
+                            &planned)) != MOE_OK)
+    return s;
   if (ev && (s = record(ev[2], st)) != MOE_OK) return s;
   if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, st, ev ? ev + 3 : nullptr,
                   planned)) != MOE_OK)
@@ -628,6 +675,23 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
   Ws L;
   if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
   return do_permute(*shape, topk_idx, expert_offsets, slot_token, pair_slot, ws, L, (hipStream_t)stream);
+}
+
+moe_status moe_route_permute(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
+                             int32_t* topk_idx, float* topk_w, int32_t* expert_offsets, int32_t* slot_token,
+                             int32_t* pair_slot, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (!expert_offsets || (shape->T && (!x || !Wr_packed || !topk_idx || !topk_w || !slot_token || !pair_slot)))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!al16(x) || !al16(Wr_packed)) return misaligned("x and Wr_packed", 16);
+  if (!al4(bias) || !al4(topk_idx) || !al4(topk_w) || !al4(expert_offsets) || !al4(slot_token) || !al4(pair_slot))
+    return misaligned("bias, the routing outputs and the index arrays", 4);
+  Ws L;
+  if ((s = check_ws(*shape, ws, ws_bytes, &L)) != MOE_OK) return s;
+  bool planned;
+  return do_route_permute(*shape, x, Wr_packed, bias, topk_idx, topk_w, expert_offsets, slot_token, pair_slot, ws, L,
+                          (hipStream_t)stream, nullptr, nullptr, &planned);
 }
 
 moe_status moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t* expert_offsets,

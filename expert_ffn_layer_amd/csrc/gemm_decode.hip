@@ -499,6 +499,7 @@ template <int CR, int CS, int ACT, int EPI, int NF>
 __global__ void __launch_bounds__(256) grouped_decode_kernel(GroupedArgs a) {
   constexpr int NMAT = EpiTraits<EPI>::NMAT;
   __shared__ float red[3 * NMAT * NF * 4 * 64];
+  if (a.clear_word && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.clear_word = 0u;
   int rbi = blockIdx.x / a.NTW;
   const int ntw = blockIdx.x % a.NTW;
   if (a.cum_blocks && a.g_end > a.g_begin) {

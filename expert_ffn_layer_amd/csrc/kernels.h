@@ -49,6 +49,7 @@ struct GroupedArgs {
   const void* act_scale; // W4A8: e8m0 exponents of the MXFP8 activations, [row][K/32], gathered as act;
                          // Int8 W8A8: fp32 scale per activation row
   void* out_scale;       // EPI_SWIGLU_Q8: e8m0 exponents of the output, [row][N/64] (N = 2 I)
+  uint32_t* clear_word;  // decode kernel: a word set to 0 by the launch (the next kernel's completion count)
 };
 
 // Output features (in units of 16) per decode work item, chosen from the instantiated set so an
@@ -97,6 +98,15 @@ bool permute_small_ok(int P, int E);
 hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int shared, int rb, int32_t* offsets,
                                 int32_t* slot_token, int32_t* pair_slot, int32_t* group_range, int32_t* cum_blocks,
                                 int32_t* block_group, hipStream_t st);
+// Decode batches: selection (or hash routing), permutation and plan in one launch. `done` is a
+// word of the workspace that must read 0 when the kernel starts (the router-score launch before it
+// clears it); ws_hist holds ceil(T / 16) x E ints.
+bool topk_permute_ok(int T, int k, int E);
+hipError_t launch_topk_permute(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
+                               const int32_t* hash_ids, const int32_t* hash_table, int vocab, int32_t* idx, float* w,
+                               int32_t* ws_rank, int32_t* ws_hist, uint32_t* done, int shared, int rb,
+                               int32_t* offsets, int32_t* slot_token, int32_t* pair_slot, int32_t* group_range,
+                               int32_t* cum_blocks, int32_t* block_group, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t st);
 // W4A8: bf16 rows [rows][K] -> MXFP8 codes uint8[rows][K] + e8m0 exponents uint8[rows][K/32].
 hipError_t launch_quant_mxfp8(const void* src, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t st);

@@ -12,6 +12,7 @@
 // Every result is a pure function of topk_idx: the map is the same on every run.
 #include "common.h"
 #include "kernels.h"
+#include "wave_topk.h"
 
 namespace moe {
 
@@ -87,6 +88,35 @@ __device__ int block_exclusive_scan(int32_t* lds, int32_t* tmp, int n) {
     for (int i = tid; i < n; i += nt) lds[i] = dst[i];
   __syncthreads();
   return total;
+}
+
+// Exclusive scan of one value per thread over the workgroup (up to 16 waves): each wave scans its
+// 64 values with lane shuffles, the first wave scans the waves' totals; `wsum` is 16 ints of LDS.
+// Returns the thread's exclusive prefix and sets *total to the sum of all values.
+__device__ int block_scan_one(int v, int32_t* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < nw ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_up(w, off, 64);
+      if (lane >= off) w += y;
+    }
+    if (lane < nw) wsum[lane] = w;
+  }
+  __syncthreads();
+  const int before = wave ? wsum[wave - 1] : 0;
+  *total = wsum[nw - 1];
+  __syncthreads();  // wsum free for the next scan
+  return before + x - v;
 }
 
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ hist, int NB, int E,
@@ -302,6 +332,176 @@ hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int sha
   if (!permute_small_ok(P, E)) return hipErrorInvalidValue;
   permute_small_kernel<<<1, SMALL_THR, 0, st>>>(idx, P, k, E, T, shared, rb, offsets, slot_token, pair_slot,
                                                 group_range, cum_blocks, block_group);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode batches in one launch: the router's selection, the permutation and the plan.
+// Workgroup b selects tokens 16b .. 16b + 15 (one wave each, wave_topk), then ranks its own pairs
+// in pair order among its pairs of the same expert (the wave-ballot ranks above) and writes the
+// ranks and its expert histogram. The last workgroup to finish -- a completion count in the
+// workspace, cleared by the router-score kernel of the same call -- forms the offsets (per expert
+// over the workgroups, then over the experts), places every pair at offsets[e] + its workgroup's
+// base + its rank, and writes the plan. The map is the same stable counting sort as the other
+// paths; only the workgroup that finishes last depends on scheduling, not the result.
+// ------------------------------------------------------------------------------------------
+constexpr int FTHR = 1024, FTOK = 16;  // threads and tokens per workgroup
+constexpr int FPAIRS = FTOK * TOPK_MAX;  // pairs per workgroup at most (4 waves)
+constexpr int FUSED_E = 512;
+constexpr int FUSED_CELLS = 16384;  // workgroups x experts of the histogram the last workgroup holds
+
+bool topk_permute_ok(int T, int k, int E) {
+  return T >= 1 && (long long)T * k <= SMALL_P && E <= FUSED_E && k <= TOPK_MAX &&
+         (long long)((T + FTOK - 1) / FTOK) * E <= FUSED_CELLS;
+}
+
+template <int PL, bool HASH>
+__global__ void __launch_bounds__(FTHR) topk_permute_kernel(
+    const float* __restrict__ logits, int ldl, long long part_stride, int nparts, const float* __restrict__ bias,
+    int T, int E, int k, const int32_t* __restrict__ token_ids, const int32_t* __restrict__ table, int vocab,
+    int32_t* __restrict__ idx, float* __restrict__ wout, int32_t* __restrict__ rank, int32_t* __restrict__ hist,
+    uint32_t* __restrict__ done, int shared, int rb, int32_t* __restrict__ offsets, int32_t* __restrict__ slot_token,
+    int32_t* __restrict__ pair_slot, int32_t* __restrict__ group_range, int32_t* __restrict__ cum_blocks,
+    int32_t* __restrict__ block_group) {
+  __shared__ int32_t kept[FPAIRS];            // this workgroup's experts, pair order
+  __shared__ int32_t wcnt[4 * FUSED_E];       // per-wave counts of this workgroup's pairs
+  __shared__ int32_t cell[FUSED_CELLS];       // last workgroup: base of (workgroup, expert)
+  __shared__ int32_t soff[FUSED_E + 2];       // last workgroup: offsets; then the plan's block prefix
+  __shared__ int32_t wsum[16];
+  __shared__ int last;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = blockIdx.x, t0 = b * FTOK;
+  const int ntok = min(FTOK, T - t0), np = ntok * k;
+  const int P = T * k;
+
+  // 1. selection: wave w routes token t0 + w
+  if (wave < ntok)
+    wave_topk<PL, HASH>(logits, ldl, part_stride, nparts, bias, t0 + wave, E, k, token_ids, table, vocab, idx, wout,
+                        kept + wave * k);
+  for (int i = tid; i < 4 * E; i += FTHR) wcnt[i] = 0;
+  __syncthreads();
+
+  // 2. ranks among this workgroup's pairs of the same expert, in pair order, and its histogram
+  int e = -1;
+  if (tid < np) {
+    e = kept[tid];
+    if (e < 0 || e >= E) e = -1;
+  }
+  int r_in_wave = 0;
+  if (wave < 4) {  // wave-uniform: the pairs sit in the first 4 waves
+    uint64_t pending = __ballot(e >= 0);
+    while (pending) {
+      const int leader = __ffsll((long long)pending) - 1;
+      const int ek = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t same = __ballot(e == ek) & pending;
+      if (e == ek) r_in_wave = __popcll(same & lanemask_lt(lane));
+      if (lane == leader) wcnt[wave * E + ek] = __popcll(same);
+      pending &= ~same;
+    }
+  }
+  __syncthreads();
+  if (e >= 0) {
+    int r = r_in_wave;
+    for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
+    rank[(size_t)t0 * k + tid] = r;
+  }
+  for (int ee = tid; ee < E; ee += FTHR)
+    hist[(size_t)b * E + ee] = wcnt[ee] + wcnt[E + ee] + wcnt[2 * E + ee] + wcnt[3 * E + ee];
+
+  // 3. completion count: this workgroup's selection, ranks and histogram are released device-wide
+  // before its increment; the workgroup that counts last acquires everyone's
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(done, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+
+  // 4. offsets: per expert, exclusive prefix over the workgroups, then over the experts
+  const int nb = gridDim.x;
+  for (int i = tid; i < nb * E; i += FTHR) cell[i] = hist[i];
+  __syncthreads();
+  int tot = 0;
+  if (tid < E) {
+    for (int bb = 0; bb < nb; ++bb) {
+      const int c = cell[bb * E + tid];
+      cell[bb * E + tid] = tot;
+      tot += c;
+    }
+  }
+  int grand;
+  const int off = block_scan_one(tid < E ? tot : 0, wsum, &grand);
+  if (tid < E) {
+    offsets[tid] = off;
+    soff[tid] = off;
+  }
+  if (tid == 0) {
+    offsets[E] = grand;
+    soff[E] = grand;
+  }
+  __syncthreads();
+
+  // 5. every pair to its slot
+  for (int q = tid; q < P; q += FTHR) {
+    const int eq = idx[q];
+    if (eq < 0 || eq >= E) {
+      pair_slot[q] = -1;
+      continue;
+    }
+    const int slot = soff[eq] + cell[(q / k / FTOK) * E + eq] + rank[q];
+    pair_slot[q] = slot;
+    slot_token[slot] = q / k;
+  }
+
+  // 6. plan: row range and row-block count of each group (routed experts, then the shared one)
+  const int G = E + (shared ? 1 : 0);
+  int b0 = 0, b1 = 0;
+  if (tid < G) {
+    b0 = tid < E ? soff[tid] : P;
+    b1 = tid < E ? soff[tid + 1] : P + T;
+    group_range[2 * tid] = b0;
+    group_range[2 * tid + 1] = b1;
+  }
+  int nblk;
+  const int cum = block_scan_one(tid < G ? (b1 - b0 + rb - 1) / rb : 0, wsum, &nblk);
+  if (tid < G) {
+    cum_blocks[tid] = cum;
+    cell[tid] = cum;
+  }
+  if (tid == 0) {
+    cum_blocks[G] = nblk;
+    cell[G] = nblk;
+  }
+  __syncthreads();
+  write_block_group(cell, G, block_group, tid, FTHR);
+}
+
+hipError_t launch_topk_permute(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
+                               const int32_t* hash_ids, const int32_t* hash_table, int vocab, int32_t* idx, float* w,
+                               int32_t* ws_rank, int32_t* ws_hist, uint32_t* done, int shared, int rb,
+                               int32_t* offsets, int32_t* slot_token, int32_t* pair_slot, int32_t* group_range,
+                               int32_t* cum_blocks, int32_t* block_group, hipStream_t st) {
+  if (!topk_permute_ok(T, k, E)) return hipErrorInvalidValue;
+  const long long ps = (long long)T * ldl;
+  const dim3 grid((unsigned)((T + FTOK - 1) / FTOK)), block(FTHR);
+  const int pl = (E + 63) / 64;
+#define MOE_TP(PL, HASH)                                                                                         \
+  topk_permute_kernel<PL, HASH><<<grid, block, 0, st>>>(logits, ldl, ps, nparts, bias, T, E, k, hash_ids,       \
+                                                        hash_table, vocab, idx, w, ws_rank, ws_hist, done, shared, \
+                                                        rb, offsets, slot_token, pair_slot, group_range,         \
+                                                        cum_blocks, block_group)
+  if (hash_ids) {
+    if (pl <= 2) MOE_TP(2, true);
+    else if (pl <= 4) MOE_TP(4, true);
+    else MOE_TP(8, true);
+  } else {
+    if (pl <= 1) MOE_TP(1, false);
+    else if (pl <= 2) MOE_TP(2, false);
+    else if (pl <= 4) MOE_TP(4, false);
+    else if (pl <= 6) MOE_TP(6, false);
+    else MOE_TP(8, false);
+  }
+#undef MOE_TP
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ PATH = {"auto": 0, "decode": 1, "prefill": 2}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_pack_size", "moe_pack", "moe_workspace_size",
-           "moe_route", "moe_route_hash", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
+           "moe_route", "moe_route_hash", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_hash", "moe_layer_forward_timed", "moe_quantize_mxfp8", "moe_quantize_int8")
 TIMED_EVENTS = 7
 
@@ -64,6 +64,7 @@ def load() -> ctypes.CDLL:
         lib.moe_route.argtypes = [PS, P, P, P, P, P, P, SZ, P]
         lib.moe_route_hash.argtypes = [PS, P, P, P, P, P, I32, P, P, P, SZ, P]
         lib.moe_permute.argtypes = [PS, P, P, P, P, P, SZ, P]
+        lib.moe_route_permute.argtypes = [PS, P, P, P, P, P, P, P, P, P, SZ, P]
         lib.moe_grouped_ffn.argtypes = [PS, P, P, P, PW, PW, P, P, P, SZ, P]
         lib.moe_combine.argtypes = [PS, P, P, P, P, P, P]
         lib.moe_layer_forward.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P]
@@ -141,6 +142,13 @@ def moe_permute(shape, topk_idx, expert_offsets, slot_token, pair_slot, ws, stre
     _check(load().moe_permute(ctypes.byref(shape), _p(topk_idx), _p(expert_offsets), _p(slot_token),
                               _p(pair_slot), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                               _stream(stream)))
+
+
+def moe_route_permute(shape, x, Wr_packed, bias, topk_idx, topk_w, expert_offsets, slot_token, pair_slot, ws,
+                      stream=None):
+    _check(load().moe_route_permute(ctypes.byref(shape), _p(x), _p(Wr_packed), _p(bias), _p(topk_idx), _p(topk_w),
+                                    _p(expert_offsets), _p(slot_token), _p(pair_slot), _p(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_grouped_ffn(shape, x, expert_offsets, slot_token, routed: dict, shared: dict | None, y_perm, y_shared,

@@ -208,6 +208,23 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx,
                        void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
+ * moe_route_permute — moe_route followed by moe_permute, with the same outputs bit for bit
+ * ('DeepSeek-V4-Pro on NVIDIA H200' §9.2: launch and synchronisation cost eats the gain of small
+ * kernels; 'CANN DeepSeek-V4推理优化', fused-kernel section: a fused gating top-k). Decode
+ * batches (T*k <= 8192, E <= 512, fewer than 2048 tokens) run as the router-score kernel and one
+ * more launch: its workgroups select 16 tokens each and rank their own pairs by expert, and the
+ * last workgroup to finish (a completion count in ws, cleared by the score kernel) forms the
+ * offsets and places every pair. Other shapes run moe_route's and moe_permute's kernels.
+ *   topk_idx, topk_w               out, as moe_route
+ *   expert_offsets, slot_token, pair_slot   out, as moe_permute
+ * Arguments, ownership and errors as moe_route and moe_permute.
+ */
+moe_status moe_route_permute(const moe_shape* shape, const void* x, const void* Wr_packed,
+                             const float* bias, int32_t* topk_idx, float* topk_w,
+                             int32_t* expert_offsets, int32_t* slot_token, int32_t* pair_slot,
+                             void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
  * moe_grouped_ffn — every expert's SwiGLU on its rows, plus the shared expert on all tokens
  * [ch6 §6.2.2; V4 D6].
  *   x              [T][H] act
@@ -241,6 +258,8 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
  * top-k, grouped expert weight reads, Linear-1/activation/Linear-2, combine).
  *   y              [T][H] act out
  *   topk_idx_out   int32[T][k] or NULL; topk_w_out float[T][k] or NULL (copies of the routing)
+ * Routing and permutation run as moe_route_permute; for decode batches its second launch also
+ * writes the grouped GEMMs' plan.
  */
 moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* Wr_packed,
                              const float* bias, const moe_weights* routed,
@@ -263,7 +282,9 @@ moe_status moe_layer_forward_hash(const moe_shape* shape, const void* x, const v
  * caller-created HIP events) on `stream` around its kernels, for per-stage timing:
  *   [0] start   [1] after route   [2] after permute   [3] after the grouped-GEMM plan
  *   [4] after the gate/up grouped GEMM   [5] after the down grouped GEMM   [6] after combine
- * Same results as moe_layer_forward. With T == 0 nothing is recorded.
+ * Decode batches (T*k <= 8192, E <= 512, fewer than 2048 tokens) run the top-k selection, the
+ * permutation and the plan as one kernel after the router scores: there [1] follows the scores
+ * and [2] that kernel. Same results as moe_layer_forward. With T == 0 nothing is recorded.
  */
 #define MOE_TIMED_EVENTS 7
 moe_status moe_layer_forward_timed(const moe_shape* shape, const void* x, const void* Wr_packed,

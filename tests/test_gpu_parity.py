@@ -290,6 +290,48 @@ def test_stages_match_oracle_stage_by_stage(name, spec):
     assert rel_fro(to_f64(y), ref_y) <= 4e-3  # only the final bf16 rounding differs
 
 
+# ------------------------------------------------------------------ fused routing + permutation
+
+ROUTE_PERMUTE = [
+    # (T, E, k): one token; a workgroup's 16 tokens exactly and one more; several workgroups with a
+    # ragged last one; the largest fused sizes (T*k = 8192, 32 workgroups x 512 experts of histogram);
+    # one expert; 125 workgroups; Zipf-skewed groups; past the fused limits (T*k > 8192; E > 512;
+    # 2048 tokens or more, whose scores run on the prefill kernel): the separate kernels
+    (1, 8, 2), (16, 128, 8), (17, 128, 8), (45, 300, 7), (255, 64, 6), (512, 512, 16), (64, 1, 1),
+    (1024, 40, 8), (2000, 16, 4), (600, 256, 8), (1100, 64, 8), (40, 1024, 16), (2304, 8, 2),
+]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_PERMUTE, ids=["T%d-E%d-k%d" % r for r in ROUTE_PERMUTE])
+def test_route_permute_matches_oracle(T, E, k):
+    """moe_route_permute against the oracle's route and permute, bit for bit (weights within
+    1e-5), with the workspace filled with 0xFF first: the completion count the fused launch relies
+    on is cleared by the score kernel of the same call. A second call gives the same bits."""
+    zipf = T >= 600
+    spec = L.LayerSpec("rp", T=T, H=256, E=E, k=k, I=128, router="zipf" if zipf else "uniform",
+                       zipf_alpha=1.1 if zipf else 0.0, calib_tokens=512, seed=90 + T + E)
+    lay, pl = build(spec, DEV)
+    pl.ws.fill_(255)
+    x = lay["x"].view(torch.bfloat16)
+    ridx, rw, _ = O.route(lay["x_host"], lay["Wr_host"], lay["bias_host"], k, spec.act)
+    roff, rst, rps = O.permute(ridx, E)
+    outs = []
+    for _ in range(2):
+        idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        off = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+        st = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+        ps = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+        N.moe_route_permute(pl.shape, x, pl.Wr, lay["bias"], idx, w, off, st, ps, pl.ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-5
+        assert np.array_equal(off.cpu().numpy(), roff)
+        assert np.array_equal(st.cpu().numpy(), rst) and np.array_equal(ps.cpu().numpy(), rps)
+        outs.append((idx, w, off, st, ps))
+    assert all(torch.equal(a, b) for a, b in zip(*outs))
+
+
 # ------------------------------------------------------------------ full-size layers
 
 # the DeepSeek-V4-Pro-shaped layer at a prefill batch: MXFP4 routed experts in the prefill
@@ -343,6 +385,14 @@ def test_full_size_layer(cfg):
     ps = torch.empty(spec.T * spec.k, dtype=torch.int32, device=DEV)
     N.moe_permute(s, idx, off, st, ps, pl.ws)
     torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(st.cpu().numpy(), rst) and np.array_equal(ps.cpu().numpy(), rps)
+    # routing and permutation as the layer runs them (one launch after the scores at decode sizes)
+    x = lay["x"] if spec.act == "f32" else lay["x"].view(torch.bfloat16)
+    idx2, w2 = torch.empty_like(idx), torch.empty_like(w)
+    N.moe_route_permute(s, x, pl.Wr, lay["bias"], idx2, w2, off, st, ps, pl.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), ridx) and np.max(np.abs(w2.cpu().numpy() - rw)) <= 1e-5
     assert np.array_equal(off.cpu().numpy(), roff)
     assert np.array_equal(st.cpu().numpy(), rst) and np.array_equal(ps.cpu().numpy(), rps)
     counts = np.diff(roff)
