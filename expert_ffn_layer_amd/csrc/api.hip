@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -584,6 +585,45 @@ moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed
   return s;
 }
 
+// ------------------------------------------------------------------------------------------
+// The library's own scratch memory, for callers that cannot allocate: moe_layer_forward_noalloc
+// runs the layer with this array as its workspace. Each GPU holds its own copy for the life of the
+// process; the host side finds that copy's address once per device and passes it to the kernels.
+// ------------------------------------------------------------------------------------------
+constexpr size_t SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[MAX_DEVICES];
+
+// The device address of the current device's scratch array (found on the first call per device,
+// with that device current), or null with the error set.
+void* scratch_of_current_device(moe_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_status(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    *st = fail(MOE_ERR_UNSUPPORTED, "device %d: the library's scratch covers devices 0..%d", dev, MAX_DEVICES - 1);
+    return nullptr;
+  }
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] { slot.err = hipGetSymbolAddress((void**)&slot.ptr, HIP_SYMBOL(scratch)); });
+  if (slot.err != hipSuccess || !slot.ptr) {
+    *st = hip_status(slot.err != hipSuccess ? slot.err : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    return nullptr;
+  }
+  *st = MOE_OK;
+  return slot.ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -726,6 +766,23 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              const moe_weights* routed, const moe_weights* shared, void* y, int32_t* topk_idx_out,
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, ws_bytes,
+                  (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
+                                     const moe_weights* routed, const moe_weights* shared, void* y,
+                                     int32_t* topk_idx_out, float* topk_w_out, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  const size_t need = ws_layout(*shape).total;
+  if (need > SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "this shape needs %zu bytes of workspace; the library's own scratch holds %zu "
+                "(use moe_layer_forward with a workspace)",
+                need, SCRATCH_BYTES);
+  void* ws = scratch_of_current_device(&s);
+  if (!ws) return s;
+  return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, SCRATCH_BYTES,
                   (hipStream_t)stream, nullptr);
 }
 

@@ -18,8 +18,11 @@ PATH = {"auto": 0, "decode": 1, "prefill": 2}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_pack_size", "moe_pack", "moe_workspace_size",
-           "moe_route", "moe_route_hash", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_forward_hash", "moe_layer_forward_timed", "moe_quantize_mxfp8", "moe_quantize_int8")
+           "moe_route", "moe_route_hash", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_combine",
+           "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_hash", "moe_layer_forward_timed",
+           "moe_quantize_mxfp8", "moe_quantize_int8")
+# the library's own scratch, the workspace of moe_layer_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 TIMED_EVENTS = 7
 
 
@@ -68,6 +71,7 @@ def load() -> ctypes.CDLL:
         lib.moe_grouped_ffn.argtypes = [PS, P, P, P, PW, PW, P, P, P, SZ, P]
         lib.moe_combine.argtypes = [PS, P, P, P, P, P, P]
         lib.moe_layer_forward.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P]
+        lib.moe_layer_forward_noalloc.argtypes = [PS, P, P, P, PW, PW, P, P, P, P]
         lib.moe_layer_forward_hash.argtypes = [PS, P, P, P, P, P, I32, PW, PW, P, P, P, P, SZ, P]
         lib.moe_layer_forward_timed.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P,
                                                 ctypes.POINTER(ctypes.c_void_p)]
@@ -172,6 +176,14 @@ def moe_layer_forward(shape, x, Wr_packed, bias, routed: dict, shared: dict | No
                                     None if s is None else ctypes.byref(s), _p(y), _p(topk_idx), _p(topk_w),
                                     _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def moe_layer_forward_noalloc(shape, x, Wr_packed, bias, routed: dict, shared: dict | None, y, topk_idx=None,
+                              topk_w=None, stream=None):
+    r, s = weights(routed), weights(shared)
+    _check(load().moe_layer_forward_noalloc(ctypes.byref(shape), _p(x), _p(Wr_packed), _p(bias), ctypes.byref(r),
+                                            None if s is None else ctypes.byref(s), _p(y), _p(topk_idx), _p(topk_w),
+                                            _stream(stream)))
 
 
 def moe_layer_forward_hash(shape, x, Wr_packed, bias, token_ids, hash_table, routed: dict, shared: dict | None, y,

@@ -267,6 +267,25 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
+ * moe_layer_forward_noalloc — moe_layer_forward with the library's own scratch memory as the
+ * workspace, for callers that cannot allocate device memory (code under HIP graph capture that
+ * owns no workspace, tight serving loops, harnesses that forbid hipMalloc). It allocates nothing
+ * and calls no allocating routine: the scratch is a 64 MiB array in the library's device code,
+ * one copy per GPU, held until the process ends; its address is looked up on the first call on
+ * each device (with that device current).
+ *   Arguments, ownership, results and errors as moe_layer_forward (bit-identical outputs), with
+ *   `stream` belonging to the current device. A shape whose moe_workspace_size exceeds 64 MiB
+ *   (e.g. prefill batches) is refused with MOE_ERR_WORKSPACE_TOO_SMALL before any launch.
+ *   Every call on a GPU uses that GPU's one scratch array: calls that overlap in time on one GPU
+ *   (other streams, other threads) race and give undefined results; calls in one stream are
+ *   ordered. Nothing in the scratch needs to start at zero: each call rewrites what it reads.
+ */
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* Wr_packed,
+                                     const float* bias, const moe_weights* routed,
+                                     const moe_weights* shared, void* y, int32_t* topk_idx_out,
+                                     float* topk_w_out, moe_stream_t stream);
+
+/*
  * moe_layer_forward_hash — moe_layer_forward with moe_route_hash in place of moe_route
  * (arguments as those two).
  */
