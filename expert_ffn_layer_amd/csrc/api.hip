@@ -157,7 +157,7 @@ RouterPlan router_plan(const moe_shape& s) {
 
 struct Ws {
   size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, fhist, done, group_range, cum_blocks,
-      block_group, zero, h, y_perm, y_shared, xq, xs, hq, hs, total;
+      block_group, cum_blocks_b, block_group_b, zero, h, y_perm, y_shared, xq, xs, hq, hs, total;
 };
 
 // Decode batches route, permute and plan in one launch after the router scores (on the decode
@@ -182,14 +182,17 @@ Ws ws_layout(const moe_shape& s) {
   w.pair_slot = take(P * 4);
   w.rank = take(P * 4);
   w.hist = take((size_t)permute_blocks((int)P) * s.E * 4);
-  // the fused route-permute launch: per workgroup of 16 tokens an expert histogram, and its count
-  w.fhist = take(use_fused_route(s) ? (size_t)((s.T + 15) / 16) * s.E * 4 : 0);
+  // the fused route-permute launch: per workgroup of 8 or 16 tokens an expert histogram, and its count
+  w.fhist = take(use_fused_route(s) ? (size_t)((s.T + 7) / 8) * s.E * 4 : 0);
   w.done = take(4);
   w.group_range = take(((size_t)s.E + 1) * 8);
   w.cum_blocks = take(((size_t)s.E + 2) * 4);
   // one entry per row block: at most one partial block per group plus the full ones (64-row
   // blocks at decode, 128 at prefill)
   w.block_group = take(((size_t)s.E + 2 + (R + ROW_BLOCK - 1) / ROW_BLOCK) * 4);
+  // the down product's table when gate/up runs thick blocks (64-row blocks only)
+  w.cum_blocks_b = take(((size_t)s.E + 2) * 4);
+  w.block_group_b = take(((size_t)s.E + 2 + (R + ROW_BLOCK - 1) / ROW_BLOCK) * 4);
   w.h = take(R * s.I * ab);
   w.y_perm = take(P * s.H * ab);
   w.y_shared = take(S * s.T * s.H * ab);
@@ -311,6 +314,19 @@ bool use_prefill(const moe_shape& s) {
   return (long long)s.T * s.k >= 64LL * s.E;
 }
 
+// Decode batches cut the groups of more than 64 rows into blocks of up to 256 for the gate/up product:
+// each wave of such an item runs 64 rows over the whole reduction, so the four waves stream each
+// weight tile together (one HBM read, the other three from cache) instead of once per 64-row block.
+// Its kernel must run 4 row tiles per wave: f32, bf16 or Int8 weights, the same format for the routed
+// and shared experts (one launch). The down product, whose reduction is short, keeps 64-row blocks
+// (a plan table of its own).
+int decode_thick_rows(const moe_shape& s) {
+  if (use_prefill(s)) return 0;
+  if (s.I_shared && s.w_shared != s.w_routed) return 0;
+  if (s.w_routed != MOE_F32 && s.w_routed != MOE_BF16 && s.w_routed != MOE_INT8_W8A8) return 0;
+  return 4 * ROW_BLOCK;
+}
+
 // with_plan: also write the grouped-GEMM plan into the workspace (returns whether it did)
 moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int32_t* st_, int32_t* ps, void* ws,
                       const Ws& L, hipStream_t st, bool with_plan = false, bool* planned = nullptr) {
@@ -318,9 +334,10 @@ moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int3
   if (s.T == 0) return hip_status(launch_fill_i32(off, 0, s.E + 1, st), "permute (empty)");
   hipError_t e;
   if (permute_small_ok(s.T * s.k, s.E)) {
-    e = launch_permute_small(idx, s.T, s.k, s.E, s.I_shared ? 1 : 0, ROW_BLOCK, off, st_, ps,
+    e = launch_permute_small(idx, s.T, s.k, s.E, s.I_shared ? 1 : 0, ROW_BLOCK, decode_thick_rows(s), off, st_, ps,
                              with_plan ? at<int32_t>(ws, L.group_range) : nullptr, at<int32_t>(ws, L.cum_blocks),
-                             at<int32_t>(ws, L.block_group), st);
+                             at<int32_t>(ws, L.block_group), at<int32_t>(ws, L.cum_blocks_b),
+                             at<int32_t>(ws, L.block_group_b), st);
     if (planned) *planned = with_plan;
   } else {
     e = launch_permute(idx, s.T, s.k, s.E, off, st_, ps, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.hist), st);
@@ -353,8 +370,9 @@ moe_status do_route_permute(const moe_shape& s, const void* x, const void* Wr, c
   const hipError_t e = launch_topk_permute(
       at<float>(ws, L.logits), ldl, router_plan(s).ksplit, bias, s.T, s.E, s.k, hash ? hash->ids : nullptr,
       hash ? hash->table : nullptr, hash ? hash->vocab : 0, idx, w, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.fhist),
-      done, s.I_shared ? 1 : 0, ROW_BLOCK, off, slot_token, pair_slot, at<int32_t>(ws, L.group_range),
-      at<int32_t>(ws, L.cum_blocks), at<int32_t>(ws, L.block_group), st);
+      done, s.I_shared ? 1 : 0, ROW_BLOCK, decode_thick_rows(s), off, slot_token, pair_slot, at<int32_t>(ws, L.group_range),
+      at<int32_t>(ws, L.cum_blocks), at<int32_t>(ws, L.block_group), at<int32_t>(ws, L.cum_blocks_b),
+      at<int32_t>(ws, L.block_group_b), st);
   if ((rs = hip_status(e, hash ? "hash routing and permutation" : "router top-k and permutation")) != MOE_OK) return rs;
   *planned = true;
   return MOE_OK;
@@ -483,7 +501,11 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   uint32_t* zero = prefill ? at<uint32_t>(ws, L.zero) : nullptr;
   const int zero_words = (int)((size_t)std::max(s.H, s.I) * act_bytes(s.act) / 4);
   int32_t* bg = at<int32_t>(ws, L.block_group);
-  if (!plan_ready || prefill) e = launch_plan(off, s.E, P, s.T, S, rb, gr, cb, bg, zero, zero_words, st);
+  const int thick = decode_thick_rows(s);
+  int32_t* cb2 = at<int32_t>(ws, L.cum_blocks_b);
+  int32_t* bg2 = at<int32_t>(ws, L.block_group_b);
+  if (!plan_ready || prefill)
+    e = launch_plan(off, s.E, P, s.T, S, rb, thick, gr, cb, bg, cb2, bg2, zero, zero_words, st);
   if (e != hipSuccess) return hip_status(e, "plan");
   moe_status rs;
   if (ev && (rs = record(ev[0], st)) != MOE_OK) return rs;
@@ -493,6 +515,7 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
 
   GroupedArgs a{};
   a.zero_row = zero;
+  a.thick_rows = thick;
   a.group_range = gr;
   a.cum_blocks = cb;
   a.block_group = bg;
@@ -529,7 +552,12 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   e = f.quantise_h(a8, i8);
   if (e != hipSuccess) return hip_status(e, "quantisation of h");
 
-  // down: y = h Wd, the routed rows to y_perm and the shared ones to y_shared
+  // down: y = h Wd, the routed rows to y_perm and the shared ones to y_shared (64-row blocks)
+  if (thick) {
+    a.cum_blocks = cb2;
+    a.block_group = bg2;
+    a.thick_rows = 0;
+  }
   a.gather = nullptr;
   a.act = at<void>(ws, L.h);
   a.lda = s.I;

@@ -193,8 +193,9 @@ struct Stage {
 };
 
 // Issue the loads of packets kt .. kt+U-1 (indices past kt1-1 re-read packet kt1-1 and are
-// not used, so every address stays inside the stream).
-template <int C, int ACT, int NMAT, int NF, int MT, int U>
+// not used, so every address stays inside the stream). NTL: weights as non-temporal loads (read
+// by this wave only); otherwise plain loads, which the other row groups of the item hit in cache.
+template <int C, int ACT, int NMAT, int NF, int MT, int U, bool NTL>
 __device__ __forceinline__ void load_stage(Stage<C, NMAT, NF, MT, U>& st, const uint8_t* __restrict__ w0,
                                            const uint8_t* __restrict__ w1, const uint8_t* __restrict__ s0,
                                            const uint8_t* __restrict__ s1, const uint8_t* const (&xrow)[MT],
@@ -212,8 +213,13 @@ __device__ __forceinline__ void load_stage(Stage<C, NMAT, NF, MT, U>& st, const 
       for (int p = 0; p < Cd::WPK; ++p) {
         // WPK consecutive 1 KiB packets per step (the fp8 pair of a 128-deep MXFP8 step)
         const size_t off = (((size_t)(nt0 + f) * KT + k) * Cd::WPK + p) * PACKET_BYTES + (size_t)lane * 16;
-        st.w[u][0][f][p] = ld_nt((const u32x4*)(w0 + off));
-        if (NMAT == 2) st.w[u][NMAT - 1][f][p] = ld_nt((const u32x4*)(w1 + off));
+        if constexpr (NTL) {
+          st.w[u][0][f][p] = ld_nt((const u32x4*)(w0 + off));
+          if (NMAT == 2) st.w[u][NMAT - 1][f][p] = ld_nt((const u32x4*)(w1 + off));
+        } else {
+          st.w[u][0][f][p] = *(const u32x4*)(w0 + off);
+          if (NMAT == 2) st.w[u][NMAT - 1][f][p] = *(const u32x4*)(w1 + off);
+        }
       }
       st.s[u][0][f] = packet_scale<C>(s0, N, KT, nt0 + f, k, lane);
       if (NMAT == 2) st.s[u][NMAT - 1][f] = packet_scale<C>(s1, N, KT, nt0 + f, k, lane);
@@ -286,7 +292,7 @@ constexpr int stage_depth() {
 // One wave: MT row tiles of 16 rows x (16*NF) features of NMAT matrices over packets
 // [kt0, kt1), with the loads of the next stage in flight while the current stage feeds the
 // MFMAs. Every weight packet the wave loads feeds all MT row tiles.
-template <int C, int ACT, int NMAT, int NF, int MT>
+template <int C, int ACT, int NMAT, int NF, int MT, bool NTL>
 __device__ __forceinline__ void wave_mma(const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
                                          const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,
                                          const uint8_t* const (&xrow)[MT], const uint8_t* const (&xsrow)[MT], int N,
@@ -294,18 +300,18 @@ __device__ __forceinline__ void wave_mma(const uint8_t* __restrict__ w0, const u
   constexpr int U = stage_depth<C, NMAT, NF, MT>();
   if (kt0 >= kt1) return;
   Stage<C, NMAT, NF, MT, U> A, B;
-  load_stage<C, ACT, NMAT, NF, MT, U>(A, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt0, kt1, lane);
+  load_stage<C, ACT, NMAT, NF, MT, U, NTL>(A, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt0, kt1, lane);
   int kt = kt0;
   // steady state: both stages entirely inside the range, so every load and MFMA is
   // unconditional and the wait counts stay exact (the next stage's loads remain in flight)
   for (; kt + 2 * U < kt1; kt += 2 * U) {
-    load_stage<C, ACT, NMAT, NF, MT, U>(B, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + U, kt1, lane);
+    load_stage<C, ACT, NMAT, NF, MT, U, NTL>(B, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + U, kt1, lane);
     mma_stage(A, acc);
-    load_stage<C, ACT, NMAT, NF, MT, U>(A, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + 2 * U, kt1, lane);
+    load_stage<C, ACT, NMAT, NF, MT, U, NTL>(A, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + 2 * U, kt1, lane);
     mma_stage(B, acc);
   }
   // remainder (1 .. 2U packets), branch-free: packets past the range are masked to zero
-  load_stage<C, ACT, NMAT, NF, MT, U>(B, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + U, kt1, lane);
+  load_stage<C, ACT, NMAT, NF, MT, U, NTL>(B, w0, w1, s0, s1, xrow, xsrow, N, KT, nt0, kt + U, kt1, lane);
   mma_stage_masked(A, kt, kt1, acc);
   mma_stage_masked(B, kt + U, kt1, acc);
 }
@@ -376,7 +382,8 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[r][m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (wnr > 0) wave_mma<C, ACT, NMAT, NF, MT>(w0, w1, s0, s1, xrow, xsrow, a.N, KT, nt0, kt0, kt1, lane, acc);
+  if (wnr > 0)
+    wave_mma<C, ACT, NMAT, NF, MT, MTP == 1>(w0, w1, s0, s1, xrow, xsrow, a.N, KT, nt0, kt0, kt1, lane, acc);
 
   if constexpr (Codec<C>::I8) {
     // int32 sums -> fp32 times the row's activation scale and the feature's weight scale (features
@@ -469,8 +476,8 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
   }
 }
 
-// Row layout of an item by its row count: 1, 2 or 4 row tiles, split into MTP row groups of MT
-// tiles. Formats with one 16-byte activation chunk per packet (f32, bf16) give each wave as
+// Row layout of an item of up to 64 rows by its row count: 1, 2 or 4 row tiles, split into MTP row
+// groups of MT tiles. Formats with one 16-byte activation chunk per packet (f32, bf16, int8) give each wave as
 // many row tiles as 64 accumulator registers allow, so a packet is loaded once per row group
 // and feeds MT MFMAs. The converted formats, whose activation chunks per packet are 2x-4x
 // larger, split the rows over the waves (each row group loads the packets of its part of K).
@@ -478,11 +485,15 @@ __device__ __forceinline__ void run_item(const GroupedArgs& a, int g, bool is_sh
 // the one-row-tile path. LEAN (the shared expert's path in a kernel whose routed experts use
 // another format) always splits rows, so the rarely used path does not set the register count.
 template <int C, int ACT, int EPI, int NF, bool LEAN>
-__device__ __forceinline__ void run_rows(const GroupedArgs& a, int g, bool is_shared, int row0, int nr, int ntw,
-                                         float* red) {
+constexpr int max_row_tiles() {
   constexpr int ACC = EpiTraits<EPI>::NMAT * NF * 4;  // accumulator registers per row tile
-  constexpr int MTMAX =
-      (LEAN || Codec<C>::ACT16 != 1) ? 1 : (4 * ACC <= 64 ? 4 : (2 * ACC <= 64 ? 2 : 1));
+  return (LEAN || Codec<C>::ACT16 != 1) ? 1 : (4 * ACC <= 64 ? 4 : (2 * ACC <= 64 ? 2 : 1));
+}
+
+template <int C, int ACT, int EPI, int NF, bool LEAN>
+__device__ __forceinline__ void run_rows64(const GroupedArgs& a, int g, bool is_shared, int row0, int nr, int ntw,
+                                           float* red) {
+  constexpr int MTMAX = max_row_tiles<C, ACT, EPI, NF, LEAN>();
   if (nr <= 16) {
     run_item<C, ACT, EPI, NF, 1, 1>(a, g, is_shared, row0, nr, ntw, red);
   } else if (nr <= 32) {
@@ -495,11 +506,30 @@ __device__ __forceinline__ void run_rows(const GroupedArgs& a, int g, bool is_sh
   }
 }
 
+// An item of nr rows: up to 64 (one block), or a thick block of a group of more than 64 rows (up to
+// 4 x 64 rows), where wave w runs rows 64 w .. 64 w + 63 over the whole reduction: the four waves read
+// each weight packet at about the same time, so HBM delivers it once per item instead of once per
+// 64 rows. Thick blocks exist only in the SwiGLU kernels with 4 row tiles per wave and one format for
+// routed and shared experts (the launcher refuses thick_rows for any other).
+template <int C, int ACT, int EPI, int NF, bool LEAN>
+__device__ __forceinline__ void run_rows(const GroupedArgs& a, int g, bool is_shared, int row0, int nr, int ntw,
+                                         float* red) {
+  if constexpr (EPI == EPI_SWIGLU && max_row_tiles<C, ACT, EPI, NF, LEAN>() >= 4) {
+    if (nr <= RB) run_rows64<C, ACT, EPI, NF, LEAN>(a, g, is_shared, row0, nr, ntw, red);
+    else run_item<C, ACT, EPI, NF, 4, 4>(a, g, is_shared, row0, nr, ntw, red);
+  } else {
+    run_rows64<C, ACT, EPI, NF, LEAN>(a, g, is_shared, row0, nr, ntw, red);
+  }
+}
+
 template <int CR, int CS, int ACT, int EPI, int NF>
 __global__ void __launch_bounds__(256) grouped_decode_kernel(GroupedArgs a) {
   constexpr int NMAT = EpiTraits<EPI>::NMAT;
   __shared__ float red[3 * NMAT * NF * 4 * 64];
-  if (a.clear_word && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.clear_word = 0u;
+  // (the router-score instantiation only: a store the compiler cannot place apart from the plan
+  // arrays would turn the other kernels' uniform plan loads into vector loads)
+  if constexpr (EPI == EPI_F32)
+    if (a.clear_word && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.clear_word = 0u;
   int rbi = blockIdx.x / a.NTW;
   const int ntw = blockIdx.x % a.NTW;
   if (a.cum_blocks && a.g_end > a.g_begin) {
@@ -529,8 +559,10 @@ __global__ void __launch_bounds__(256) grouped_decode_kernel(GroupedArgs a) {
   }
   const int rbeg = a.group_range ? a.group_range[2 * g] : 0;
   const int rend = a.group_range ? a.group_range[2 * g + 1] : a.M;
-  const int row0 = rbeg + RB * blk;
-  const int nr = min(RB, rend - row0);
+  // rows per block: 64, or thick_rows for a group of more than 64 rows when the plan cut it so
+  const int rbg = (a.thick_rows > RB && rend - rbeg > RB) ? min(a.thick_rows, 4 * RB) : RB;
+  const int row0 = rbeg + rbg * blk;
+  const int nr = min(rbg, rend - row0);
   if (nr <= 0) return;
   const bool is_shared = g == a.shared_group;
   if (CR == CS || !is_shared)
@@ -545,6 +577,10 @@ __global__ void __launch_bounds__(256) grouped_decode_kernel(GroupedArgs a) {
 
 template <int CR, int CS, int ACT, int EPI, int NF>
 static hipError_t launch_t(const GroupedArgs& a, int max_row_blocks, hipStream_t st) {
+  // thick blocks: the SwiGLU kernels with 4 row tiles per wave in every path
+  if (a.thick_rows && (EPI != EPI_SWIGLU || a.thick_rows > 4 * RB || max_row_tiles<CR, ACT, EPI, NF, false>() < 4 ||
+                       (CR != CS && a.shared_group >= 0)))
+    return hipErrorInvalidValue;
   GroupedArgs b = a;
   b.NTW = (a.N / 16) / NF;
   dim3 grid((unsigned)(max_row_blocks * b.NTW), (unsigned)(a.ksplit > 1 ? a.ksplit : 1)), block(256);

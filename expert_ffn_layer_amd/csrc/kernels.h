@@ -49,7 +49,8 @@ struct GroupedArgs {
   const void* act_scale; // W4A8: e8m0 exponents of the MXFP8 activations, [row][K/32], gathered as act;
                          // Int8 W8A8: fp32 scale per activation row
   void* out_scale;       // EPI_SWIGLU_Q8: e8m0 exponents of the output, [row][N/64] (N = 2 I)
-  uint32_t* clear_word;  // decode kernel: a word set to 0 by the launch (the next kernel's completion count)
+  uint32_t* clear_word;  // decode kernel, fp32 epilogue: a word set to 0 by the launch (the next kernel's completion count)
+  int thick_rows;        // decode kernel, SwiGLU epilogue: rows per block of the groups of more than 64 rows (0: 64)
 };
 
 // Output features (in units of 16) per decode work item, chosen from the instantiated set so an
@@ -84,9 +85,12 @@ int prefill_row_tile();
 bool prefill_supported(int act, int cr, int cs, int K, int N_gateup, int N_down);
 bool prefill_scores_supported(int act, int K, int N);
 hipError_t launch_prefill_scores(const GroupedArgs& a, hipStream_t st);
-hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb,
-                       int32_t* group_range, int32_t* cum_blocks, int32_t* block_group, uint32_t* zero, int zero_words,
-                       hipStream_t st);
+// The grouped GEMMs' plan (row range per group, rb-row blocks; with thick > 0, groups of more
+// than rb rows in thick-row blocks, listed first, and a second table of rb-row blocks only in
+// cum_blocks_b / block_group_b) and the prefill kernel's zero row.
+hipError_t launch_plan(const int32_t* expert_offsets, int E, int P, int T, int shared, int rb, int thick,
+                       int32_t* group_range, int32_t* cum_blocks, int32_t* block_group, int32_t* cum_blocks_b,
+                       int32_t* block_group_b, uint32_t* zero, int zero_words, hipStream_t st);
 hipError_t launch_topk(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
                        const int32_t* hash_ids, const int32_t* hash_table, int vocab, int32_t* idx, float* w,
                        hipStream_t st);
@@ -95,18 +99,19 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
                           int32_t* ws_hist, hipStream_t st);
 int permute_blocks(int P);
 bool permute_small_ok(int P, int E);
-hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int shared, int rb, int32_t* offsets,
+hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int shared, int rb, int thick, int32_t* offsets,
                                 int32_t* slot_token, int32_t* pair_slot, int32_t* group_range, int32_t* cum_blocks,
-                                int32_t* block_group, hipStream_t st);
+                                int32_t* block_group, int32_t* cum_blocks_b, int32_t* block_group_b, hipStream_t st);
 // Decode batches: selection (or hash routing), permutation and plan in one launch. `done` is a
 // word of the workspace that must read 0 when the kernel starts (the router-score launch before it
-// clears it); ws_hist holds ceil(T / 16) x E ints.
+// clears it); ws_packed holds T*k ints, ws_hist ceil(T / 8) x E ints.
 bool topk_permute_ok(int T, int k, int E);
 hipError_t launch_topk_permute(const float* logits, int ldl, int nparts, const float* bias, int T, int E, int k,
                                const int32_t* hash_ids, const int32_t* hash_table, int vocab, int32_t* idx, float* w,
-                               int32_t* ws_rank, int32_t* ws_hist, uint32_t* done, int shared, int rb,
+                               int32_t* ws_packed, int32_t* ws_hist, uint32_t* done, int shared, int rb, int thick,
                                int32_t* offsets, int32_t* slot_token, int32_t* pair_slot, int32_t* group_range,
-                               int32_t* cum_blocks, int32_t* block_group, hipStream_t st);
+                               int32_t* cum_blocks, int32_t* block_group, int32_t* cum_blocks_b, int32_t* block_group_b,
+                               hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t st);
 // W4A8: bf16 rows [rows][K] -> MXFP8 codes uint8[rows][K] + e8m0 exponents uint8[rows][K/32].
 hipError_t launch_quant_mxfp8(const void* src, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t st);

@@ -21,8 +21,9 @@ constexpr int TOPK_MAX = 16;
 constexpr int PER_LANE_MAX = 16;  // E <= 1024
 
 // The selection of token t by one wave (t wave-uniform): writes idx[t][0..k) and wout[t][0..k),
-// and, when kept is given, the same experts to kept[0..k) (a copy in LDS for the caller).
-template <int PL, bool HASH>
+// and, when kept is given, the same experts to kept[0..k) (a copy in LDS for the caller). PB:
+// split-K parts whose loads are in flight together (PB x PL registers).
+template <int PL, bool HASH, int PB = 8>
 __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int ldl, long long part_stride,
                                           int nparts, const float* __restrict__ bias, int t, int E, int k,
                                           const int32_t* __restrict__ token_ids, const int32_t* __restrict__ table,
@@ -32,7 +33,6 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
   const float NEG = -__builtin_huge_valf();
   // split-K partial scores, summed in ascending part order; the loads of PB parts of every
   // score are issued together, so the sum costs nparts / PB memory round trips, not nparts
-  constexpr int PB = 8;
   float v[PL];
 #pragma unroll
   for (int j = 0; j < PL; ++j) v[j] = 0.0f;

@@ -212,8 +212,8 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx,
  * ('DeepSeek-V4-Pro on NVIDIA H200' §9.2: launch and synchronisation cost eats the gain of small
  * kernels; 'CANN DeepSeek-V4推理优化', fused-kernel section: a fused gating top-k). Decode
  * batches (T*k <= 8192, E <= 512, fewer than 2048 tokens) run as the router-score kernel and one
- * more launch: its workgroups select 16 tokens each and rank their own pairs by expert, and the
- * last workgroup to finish (a completion count in ws, cleared by the score kernel) forms the
+ * more launch: its workgroups select 8 or 16 tokens each and rank their own pairs by expert, and
+ * the last workgroup to finish (a completion count in ws, cleared by the score kernel) forms the
  * offsets and places every pair. Other shapes run moe_route's and moe_permute's kernels.
  *   topk_idx, topk_w               out, as moe_route
  *   expert_offsets, slot_token, pair_slot   out, as moe_permute

@@ -465,6 +465,11 @@ MID = [
                              calib_tokens=512, seed=81)),
     ("mid-int8", L.LayerSpec("m2", T=200, H=7168, E=6, k=2, I=2048, shared=True, w_routed="int8", w_shared="int8",
                              router="zipf", zipf_alpha=1.0, calib_tokens=512, seed=82)),
+    # groups of several 256-row blocks (the decode kernel's largest items) with a ragged last one
+    ("thick-bf16", L.LayerSpec("m3", T=700, H=1024, E=3, k=1, I=1024, shared=True, router="zipf", zipf_alpha=1.0,
+                               calib_tokens=512, seed=83)),
+    ("thick-f32", L.LayerSpec("m4", T=300, H=512, E=2, k=1, I=256, shared=True, act="f32", w_routed="f32",
+                              w_shared="f32", seed=84)),
 ]
 
 
