@@ -44,9 +44,6 @@ def lib():
         _lib.gen_fill_mxfp4.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_fill_mxfp8.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
         _lib.gen_fill_int8.argtypes = [p, p, u32, u32, u32, i32, i32, i32, f32, p, p, p]
-        _lib.gen_copy.argtypes = [p, p, i64, p]
-        _lib.gen_stream_read.argtypes = [p, i64, p, p]
-        _lib.gen_mfma_burst.argtypes = [i32, i32, i32, p, p]
     return _lib
 
 
@@ -67,27 +64,6 @@ def _stream():
 def _chk(rc, what):
     if rc != 0:
         raise RuntimeError("inputgen %s failed (%d)" % (what, rc))
-
-
-def copy(src, dst):
-    """dst <- src with one plain copy kernel (the known-size reference for byte counters)."""
-    n = src.numel() * src.element_size()
-    assert dst.numel() * dst.element_size() >= n
-    _chk(lib().gen_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, _stream()), "copy")
-
-
-def mfma_burst(kind: int, iters: int, blocks: int, sink) -> float:
-    """One MFMA burst (kind 0: bf16 16x16x32, kind 1: fp4 x fp8, kind 2: fp8 x fp8 16x16x128, kind 3:
-    int8 16x16x64); returns its FLOPs (OPs)."""
-    _chk(lib().gen_mfma_burst(kind, iters, blocks, ctypes.c_void_p(sink.data_ptr()), _stream()), "mfma_burst")
-    return float(blocks) * 8 * iters * 16 * {0: 16384, 1: 65536, 2: 65536, 3: 32768}[kind]
-
-
-def stream_read(src, sink):
-    """One plain streaming read of all of src (the achievable HBM read rate)."""
-    n = src.numel() * src.element_size()
-    _chk(lib().gen_stream_read(ctypes.c_void_p(src.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()), _stream()),
-         "stream_read")
 
 
 def fill_dense(out, fmt: str, seed: int, tid: int, stream0: int, count: int, n: int, start: int = 0,
