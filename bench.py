@@ -36,17 +36,12 @@ WORKLOADS = ("c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8
 # the kernel sources it was measured on are unchanged (hash of their code).
 TRAFFIC = {
     # gate/up decode kernel
-    "c2": {"sha": "24c0fd2cc318dc45", "bytes": 3176791832},
-    "c3": {"sha": "24c0fd2cc318dc45", "bytes": 14695798301},
-    "c4": {"sha": "24c0fd2cc318dc45", "bytes": 3676200475},
+    "c1": {"sha": "4ebfc015e8bd9d86", "bytes": 2390368},
+    "c2": {"sha": "4ebfc015e8bd9d86", "bytes": 3176844236},
+    "c3": {"sha": "4ebfc015e8bd9d86", "bytes": 14212862838},
+    "c4": {"sha": "4ebfc015e8bd9d86", "bytes": 3662134510},
     # gate/up prefill kernel
-    "c5": {"sha": "e0463fd1be82c895", "bytes": 16306116370},
-    # the W4A8 gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared bf16 GEMM
-    "v4p-w4a8": {"sha": "176a8dd7ef59aeac", "bytes": 10131416530},
-    # the hybrid gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared W8A8 MXFP8 GEMM
-    "v4p-mx": {"sha": "176a8dd7ef59aeac", "bytes": 9795198467},
-    # the int8 gate/up stage: x to int8 + Int8 W8A8 GEMM
-    "v3-int8": {"sha": "176a8dd7ef59aeac", "bytes": 17225696545},
+    "c5": {"sha": "a4d75bc69100650b", "bytes": 16302908956},
 }
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
