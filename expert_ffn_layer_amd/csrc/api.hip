@@ -157,7 +157,8 @@ RouterPlan router_plan(const moe_shape& s) {
 
 struct Ws {
   size_t logits, idx, w, offsets, slot_token, pair_slot, rank, hist, fhist, done, group_range, cum_blocks,
-      block_group, cum_blocks_b, block_group_b, zero, h, y_perm, y_shared, xq, xs, hq, hs, total;
+      block_group, cum_blocks_b, block_group_b, sh_range, sh_cum, sh_group, sh_cum_b, sh_group_b, zero, h, y_perm,
+      y_shared, xq, xs, hq, hs, total;
 };
 
 // Decode batches route, permute and plan in one launch after the router scores (on the decode
@@ -193,6 +194,13 @@ Ws ws_layout(const moe_shape& s) {
   // the down product's table when gate/up runs thick blocks (64-row blocks only)
   w.cum_blocks_b = take(((size_t)s.E + 2) * 4);
   w.block_group_b = take(((size_t)s.E + 2 + (R + ROW_BLOCK - 1) / ROW_BLOCK) * 4);
+  // the plan of the shared expert alone, when it runs beside the routed experts (one group)
+  const size_t shb = S ? 3 + ((size_t)s.T + ROW_BLOCK - 1) / ROW_BLOCK : 0;
+  w.sh_range = take(S * 8);
+  w.sh_cum = take(S * 8);
+  w.sh_group = take(shb * 4);
+  w.sh_cum_b = take(S * 8);
+  w.sh_group_b = take(shb * 4);
   w.h = take(R * s.I * ab);
   w.y_perm = take(P * s.H * ab);
   w.y_shared = take(S * s.T * s.H * ab);
@@ -329,12 +337,14 @@ int decode_thick_rows(const moe_shape& s) {
 
 // with_plan: also write the grouped-GEMM plan into the workspace (returns whether it did)
 moe_status do_permute(const moe_shape& s, const int32_t* idx, int32_t* off, int32_t* st_, int32_t* ps, void* ws,
-                      const Ws& L, hipStream_t st, bool with_plan = false, bool* planned = nullptr) {
+                      const Ws& L, hipStream_t st, bool with_plan = false, bool* planned = nullptr,
+                      bool shared_in_plan = true) {
   if (planned) *planned = false;
   if (s.T == 0) return hip_status(launch_fill_i32(off, 0, s.E + 1, st), "permute (empty)");
   hipError_t e;
   if (permute_small_ok(s.T * s.k, s.E)) {
-    e = launch_permute_small(idx, s.T, s.k, s.E, s.I_shared ? 1 : 0, ROW_BLOCK, decode_thick_rows(s), off, st_, ps,
+    e = launch_permute_small(idx, s.T, s.k, s.E, s.I_shared && shared_in_plan ? 1 : 0, ROW_BLOCK, decode_thick_rows(s),
+                             off, st_, ps,
                              with_plan ? at<int32_t>(ws, L.group_range) : nullptr, at<int32_t>(ws, L.cum_blocks),
                              at<int32_t>(ws, L.block_group), at<int32_t>(ws, L.cum_blocks_b),
                              at<int32_t>(ws, L.block_group_b), st);
@@ -354,14 +364,15 @@ moe_status record(hipEvent_t ev, hipStream_t st) {
 // moe_permute do. ev (optional): ev[1] is recorded after the scores (fused) or the routing.
 moe_status do_route_permute(const moe_shape& s, const void* x, const void* Wr, const float* bias, int32_t* idx,
                             float* w, int32_t* off, int32_t* slot_token, int32_t* pair_slot, void* ws, const Ws& L,
-                            hipStream_t st, hipEvent_t const* ev, const HashRoute* hash, bool* planned) {
+                            hipStream_t st, hipEvent_t const* ev, const HashRoute* hash, bool* planned,
+                            bool shared_in_plan = true) {
   moe_status rs;
   *planned = false;
   if (s.T == 0) return do_permute(s, idx, off, slot_token, pair_slot, ws, L, st);
   if (!use_fused_route(s)) {
     if ((rs = do_route(s, x, Wr, bias, idx, w, ws, L, st, hash)) != MOE_OK) return rs;
     if (ev && (rs = record(ev[1], st)) != MOE_OK) return rs;
-    return do_permute(s, idx, off, slot_token, pair_slot, ws, L, st, true, planned);
+    return do_permute(s, idx, off, slot_token, pair_slot, ws, L, st, true, planned, shared_in_plan);
   }
   int ldl;
   uint32_t* done = at<uint32_t>(ws, L.done);
@@ -370,7 +381,8 @@ moe_status do_route_permute(const moe_shape& s, const void* x, const void* Wr, c
   const hipError_t e = launch_topk_permute(
       at<float>(ws, L.logits), ldl, router_plan(s).ksplit, bias, s.T, s.E, s.k, hash ? hash->ids : nullptr,
       hash ? hash->table : nullptr, hash ? hash->vocab : 0, idx, w, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.fhist),
-      done, s.I_shared ? 1 : 0, ROW_BLOCK, decode_thick_rows(s), off, slot_token, pair_slot, at<int32_t>(ws, L.group_range),
+      done, s.I_shared && shared_in_plan ? 1 : 0, ROW_BLOCK, decode_thick_rows(s), off, slot_token, pair_slot,
+      at<int32_t>(ws, L.group_range),
       at<int32_t>(ws, L.cum_blocks), at<int32_t>(ws, L.block_group), at<int32_t>(ws, L.cum_blocks_b),
       at<int32_t>(ws, L.block_group_b), st);
   if ((rs = hip_status(e, hash ? "hash routing and permutation" : "router top-k and permutation")) != MOE_OK) return rs;
@@ -388,13 +400,14 @@ struct FfnPass {
   hipStream_t st;
   bool prefill;
   int P, S;
+  int cr;      // the format of the launch's routed groups (the shared one for the shared expert alone)
   int cs;      // the shared expert's format (the routed one when there is none)
   int max_rb;  // row blocks the launch grid covers
 
   // bf16 activations: one launch over the routed and shared groups
   hipError_t plain(int epi, const GroupedArgs& a) const {
-    return prefill ? launch_grouped_prefill(s.act, epi, s.w_routed, cs, a, max_rb, st)
-                   : launch_grouped_decode(s.act, epi, s.w_routed, cs, a, max_rb, st);
+    return prefill ? launch_grouped_prefill(s.act, epi, cr, cs, a, max_rb, st)
+                   : launch_grouped_decode(s.act, epi, cr, cs, a, max_rb, st);
   }
 
   // Int8 W8A8: int8 codes and per-row scales of the activations (rows and gather as in a), one
@@ -483,35 +496,47 @@ void set_weights(GroupedArgs& a, const moe_weights& r, const moe_weights* sh, bo
   a.scale_bytes = (long long)scale_bytes;
 }
 
+// Which groups one do_ffn call runs: all of them, the routed experts alone, or the shared expert
+// alone (its own plan: one group of rows P .. P + T - 1, x read in token order).
+enum FfnPart { FFN_ALL, FFN_ROUTED, FFN_SHARED };
+
 moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const int32_t* slot_token,
                   const moe_weights& r, const moe_weights* sh, void* y_perm, void* y_shared, void* ws, const Ws& L,
-                  hipStream_t st, hipEvent_t const* ev = nullptr, bool plan_ready = false) {
+                  hipStream_t st, hipEvent_t const* ev = nullptr, bool plan_ready = false, FfnPart part = FFN_ALL) {
   if (s.T == 0) return MOE_OK;
-  const int P = s.T * s.k, S = s.I_shared ? 1 : 0, G = s.E + S;
+  const bool only_sh = part == FFN_SHARED;
+  if (only_sh && (!s.I_shared || !sh)) return fail(MOE_ERR_INVALID_ARG, "no shared expert");
+  const int P = s.T * s.k, S = s.I_shared && part != FFN_ROUTED ? 1 : 0, E = only_sh ? 0 : s.E, G = E + S;
   size_t mb1, sb1, mb2, sb2;
   moe_status ps = packed_sizes(s.w_routed, 1, s.H, s.I, &mb1, &sb1);
   if (ps != MOE_OK) return ps;
   ps = packed_sizes(s.w_routed, 1, s.I, s.H, &mb2, &sb2);
   if (ps != MOE_OK) return ps;
-  int32_t* gr = at<int32_t>(ws, L.group_range);
-  int32_t* cb = at<int32_t>(ws, L.cum_blocks);
+  int32_t* gr = at<int32_t>(ws, only_sh ? L.sh_range : L.group_range);
+  int32_t* cb = at<int32_t>(ws, only_sh ? L.sh_cum : L.cum_blocks);
   const bool prefill = use_prefill(s);
   const int rb = prefill ? prefill_row_tile() : ROW_BLOCK;
   hipError_t e = hipSuccess;
   uint32_t* zero = prefill ? at<uint32_t>(ws, L.zero) : nullptr;
   const int zero_words = (int)((size_t)std::max(s.H, s.I) * act_bytes(s.act) / 4);
-  int32_t* bg = at<int32_t>(ws, L.block_group);
+  int32_t* bg = at<int32_t>(ws, only_sh ? L.sh_group : L.block_group);
   const int thick = decode_thick_rows(s);
-  int32_t* cb2 = at<int32_t>(ws, L.cum_blocks_b);
-  int32_t* bg2 = at<int32_t>(ws, L.block_group_b);
+  int32_t* cb2 = at<int32_t>(ws, only_sh ? L.sh_cum_b : L.cum_blocks_b);
+  int32_t* bg2 = at<int32_t>(ws, only_sh ? L.sh_group_b : L.block_group_b);
   if (!plan_ready || prefill)
-    e = launch_plan(off, s.E, P, s.T, S, rb, thick, gr, cb, bg, cb2, bg2, zero, zero_words, st);
+    e = launch_plan(off, E, P, s.T, S, rb, thick, gr, cb, bg, cb2, bg2, zero, zero_words, st);
   if (e != hipSuccess) return hip_status(e, "plan");
   moe_status rs;
   if (ev && (rs = record(ev[0], st)) != MOE_OK) return rs;
-  const int max_rb = std::min(s.E, P) + (P + rb - 1) / rb + S * ((s.T + rb - 1) / rb);
+  const int max_rb = std::min(E, P) + (only_sh ? 0 : (P + rb - 1) / rb) + S * ((s.T + rb - 1) / rb);
   const bool a8 = s.w_routed == MOE_MXFP4_B32_A8, i8 = s.w_routed == MOE_INT8_W8A8;
-  const FfnPass f{s, ws, L, st, prefill, P, S, S ? (int)s.w_shared : (int)s.w_routed, max_rb};
+  if (only_sh && (a8 || i8)) return fail(MOE_ERR_UNSUPPORTED, "the shared expert alone: quantised activations");
+  const int cs = s.I_shared ? (int)s.w_shared : (int)s.w_routed;
+  // the shared expert alone runs the kernel instantiation that the single-stream launch gives its
+  // group: on the decode kernel the (routed, shared) pair of codecs, whose work split the routed
+  // format sets; the prefill kernel already runs a shared expert of another format on its own
+  const FfnPass f{s, ws, L, st, prefill, P, S, only_sh && prefill ? cs : (int)s.w_routed, S ? cs : (int)s.w_routed,
+                  max_rb};
 
   GroupedArgs a{};
   a.zero_row = zero;
@@ -520,7 +545,7 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.cum_blocks = cb;
   a.block_group = bg;
   a.G = G;
-  a.shared_group = S ? s.E : -1;
+  a.shared_group = S ? E : -1;
   a.P = P;
   a.M = P + S * s.T;
   // gate/up with the SwiGLU epilogue: h = SiLU(x Wg) * (x Wu), x gathered per slot
@@ -534,6 +559,7 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.out = at<void>(ws, L.h);
   a.ldo = s.I;
   a.out_s = nullptr;
+  if (only_sh) set_weights(a, *sh, sh, true, mb1, sb1);  // group 0 is the shared expert
   if (a8) {
     // x to MXFP8 once per token; the codes are gathered like x
     e = launch_quant_mxfp8(x, s.T, s.H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), st);
@@ -562,7 +588,7 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   a.act = at<void>(ws, L.h);
   a.lda = s.I;
   a.act_rows = P + S * s.T;
-  set_weights(a, r, S ? sh : nullptr, false, mb2, sb2);
+  set_weights(a, only_sh ? *sh : r, S ? sh : nullptr, false, mb2, sb2);
   a.K = s.I;
   a.N = s.H;
   a.out = y_perm;
@@ -576,10 +602,66 @@ moe_status do_ffn(const moe_shape& s, const void* x, const int32_t* off, const i
   return ev ? record(ev[2], st) : MOE_OK;
 }
 
+// The shared expert beside the routed ones ('CANN DeepSeek-V4推理优化', multi-stream parallelism:
+// the shared expert needs no routing, so it runs on a second stream while the router, the
+// permutation and the routed experts run on the caller's). Its FFN is the same grouped launch
+// restricted to its one group, so every row gets the same arithmetic as in the single-stream
+// order. Decode batches only: there the routing is a chain of short latency-bound kernels that
+// leaves HBM idle for the shared expert's weights (the V4-Pro decode layer: 0.857 -> 0.836 ms);
+// a prefill batch's kernels fill the GPU already, and the overlap measured no gain. Formats with
+// quantised activations keep the single-stream order.
+bool side_shared(const moe_shape& s) {
+  if (!s.I_shared || s.T == 0 || use_prefill(s)) return false;
+  const auto plain = [](int f) {
+    return f == MOE_F32 || f == MOE_BF16 || f == MOE_FP8_E4M3_B128 || f == MOE_MXFP4_B32;
+  };
+  return plain(s.w_routed) && plain(s.w_shared);
+}
+
+// One second stream and its two events per calling thread and device, made on first use (default
+// priority, non-blocking) and kept for the life of the thread. Thread-local, so a thread's fork
+// and join events are never recorded by another thread between its record and its wait.
+constexpr int MAX_SIDE_DEVICES = 64;
+struct SideStream {
+  bool made = false;
+  hipError_t err = hipSuccess;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+thread_local SideStream t_side[MAX_SIDE_DEVICES];
+
+SideStream* side_of_current_device(moe_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_status(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= MAX_SIDE_DEVICES) {
+    *st = fail(MOE_ERR_UNSUPPORTED, "device %d: the second stream covers devices 0..%d", dev, MAX_SIDE_DEVICES - 1);
+    return nullptr;
+  }
+  SideStream& ss = t_side[dev];
+  if (!ss.made) {
+    ss.made = true;
+    ss.err = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    if (ss.err == hipSuccess) ss.err = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (ss.err == hipSuccess) ss.err = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+  }
+  if (ss.err != hipSuccess) {
+    *st = hip_status(ss.err, "second stream");
+    return nullptr;
+  }
+  *st = MOE_OK;
+  return &ss;
+}
+
+// overlap: run a shared expert on the second stream (see side_shared); the timed form and the
+// no-allocation entry point keep one stream.
 moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
                     const moe_weights* routed, const moe_weights* shared, void* y, int32_t* topk_idx_out,
                     float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t const* ev,
-                    const HashRoute* hash = nullptr) {
+                    const HashRoute* hash = nullptr, bool overlap = false) {
   moe_status s = check_shape(shape);
   if (s != MOE_OK) return s;
   if ((s = check_weights(routed, shape->w_routed, "routed")) != MOE_OK) return s;
@@ -599,14 +681,29 @@ moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed
   void* y_perm = at<void>(ws, L.y_perm);
   void* y_sh = shape->I_shared ? at<void>(ws, L.y_shared) : nullptr;
   if (ev && (s = record(ev[0], st)) != MOE_OK) return s;
+  const bool side = overlap && !ev && side_shared(*shape);
+  SideStream* ss = nullptr;
+  if (side) {
+    // fork: the second stream starts after what the caller's stream holds so far, runs the shared
+    // expert's plan, gate/up and down, and records the join event
+    if (!(ss = side_of_current_device(&s))) return s;
+    if ((s = hip_status(hipEventRecord(ss->fork, st), "fork event")) != MOE_OK) return s;
+    if ((s = hip_status(hipStreamWaitEvent(ss->s, ss->fork, 0), "fork wait")) != MOE_OK) return s;
+    if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, ss->s, nullptr, false,
+                    FFN_SHARED)) != MOE_OK)
+      return s;
+    if ((s = hip_status(hipEventRecord(ss->join, ss->s), "join event")) != MOE_OK) return s;
+  }
   bool planned = false;
   if ((s = do_route_permute(*shape, x, Wr_packed, bias, idx, w, off, slot_token, pair_slot, ws, L, st, ev, hash,
-                            &planned)) != MOE_OK)
+                            &planned, !side)) != MOE_OK)
     return s;
   if (ev && (s = record(ev[2], st)) != MOE_OK) return s;
   if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, st, ev ? ev + 3 : nullptr,
-                  planned)) != MOE_OK)
+                  planned, side ? FFN_ROUTED : FFN_ALL)) != MOE_OK)
     return s;
+  // join: combine adds the shared expert's rows
+  if (side && (s = hip_status(hipStreamWaitEvent(st, ss->join, 0), "join wait")) != MOE_OK) return s;
   s = hip_status(launch_combine(shape->act, y_perm, pair_slot, w, y_sh, y, shape->T, shape->H, shape->k, st),
                  "combine");
   if (s == MOE_OK && ev) s = record(ev[6], st);
@@ -794,7 +891,7 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              const moe_weights* routed, const moe_weights* shared, void* y, int32_t* topk_idx_out,
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, ws_bytes,
-                  (hipStream_t)stream, nullptr);
+                  (hipStream_t)stream, nullptr, nullptr, true);
 }
 
 moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,
@@ -823,7 +920,7 @@ moe_status moe_layer_forward_hash(const moe_shape* shape, const void* x, const v
   if (shape && shape->T && (!token_ids || !hash_table)) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
   const HashRoute h{token_ids, hash_table, vocab};
   return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, ws_bytes,
-                  (hipStream_t)stream, nullptr, &h);
+                  (hipStream_t)stream, nullptr, &h, true);
 }
 
 moe_status moe_layer_forward_timed(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,

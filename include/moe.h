@@ -260,6 +260,12 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
  *   topk_idx_out   int32[T][k] or NULL; topk_w_out float[T][k] or NULL (copies of the routing)
  * Routing and permutation run as moe_route_permute; for decode batches its second launch also
  * writes the grouped GEMMs' plan.
+ * Decode batches with a shared expert in a bf16-activation format run that expert ('CANN
+ * DeepSeek-V4推理优化', multi-stream parallelism) on a second stream the library owns, one per
+ * calling thread and device, made on the thread's first such call: it waits for an event recorded
+ * on `stream` at entry, and `stream` waits for its end before the combine. The call still only
+ * enqueues, results are bit-identical to the single-stream order (moe_layer_forward_timed), and
+ * capturing `stream` in a HIP graph captures both streams' work.
  */
 moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* Wr_packed,
                              const float* bias, const moe_weights* routed,
@@ -274,7 +280,7 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
  * one copy per GPU, held until the process ends; its address is looked up on the first call on
  * each device (with that device current).
  *   Arguments, ownership, results and errors as moe_layer_forward (bit-identical outputs), with
- *   `stream` belonging to the current device. A shape whose moe_workspace_size exceeds 64 MiB
+ *   `stream` belonging to the current device; every launch goes to `stream` (no second stream). A shape whose moe_workspace_size exceeds 64 MiB
  *   (e.g. prefill batches) is refused with MOE_ERR_WORKSPACE_TOO_SMALL before any launch.
  *   Every call on a GPU uses that GPU's one scratch array: calls that overlap in time on one GPU
  *   (other streams, other threads) race and give undefined results; calls in one stream are
@@ -303,7 +309,9 @@ moe_status moe_layer_forward_hash(const moe_shape* shape, const void* x, const v
  *   [4] after the gate/up grouped GEMM   [5] after the down grouped GEMM   [6] after combine
  * Decode batches (T*k <= 8192, E <= 512, fewer than 2048 tokens) run the top-k selection, the
  * permutation and the plan as one kernel after the router scores: there [1] follows the scores
- * and [2] that kernel. Same results as moe_layer_forward. With T == 0 nothing is recorded.
+ * and [2] that kernel. Every launch goes to `stream`, a shared expert in the grouped launches of
+ * the routed ones, so the intervals are those of one stream. Same results as moe_layer_forward.
+ * With T == 0 nothing is recorded.
  */
 #define MOE_TIMED_EVENTS 7
 moe_status moe_layer_forward_timed(const moe_shape* shape, const void* x, const void* Wr_packed,

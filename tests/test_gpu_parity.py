@@ -729,6 +729,53 @@ def test_hash_routing_matches_oracle(name, spec, vocab):
     assert err <= tol_of(spec)
 
 
+# ------------------------------------------------------------------ shared expert on a second stream
+
+SIDE_SPECS = [
+    # decode, one format, hot groups of more than 64 rows (thick gate/up blocks)
+    ("decode-bf16-thick", L.LayerSpec("s1", T=300, H=512, E=6, k=2, I=256, shared=True, router="zipf",
+                                      zipf_alpha=1.0, calib_tokens=512, seed=91), "decode"),
+    # decode, MXFP4 routed and bf16 shared experts (two codecs in the one-stream launch)
+    ("decode-mxfp4+bf16", L.LayerSpec("s2", T=40, H=512, E=16, k=4, I=256, shared=True, w_routed="mxfp4",
+                                      w_shared="bf16", seed=92), "decode"),
+    ("decode-fp8+mxfp4", L.LayerSpec("s3", T=33, H=512, E=8, k=2, I=256, shared=True, w_routed="fp8",
+                                     w_shared="mxfp4", seed=93), "decode"),
+    ("decode-f32", L.LayerSpec("s4", T=21, H=256, E=8, k=2, I=128, act="f32", w_routed="f32", w_shared="f32",
+                               shared=True, seed=94), "decode"),
+    ("decode-bf16+fp8", L.LayerSpec("s5", T=64, H=1024, E=32, k=4, I=512, shared=True, w_routed="bf16",
+                                    w_shared="fp8", seed=95), "decode"),
+    # a prefill batch keeps one stream: the two entry points run the same launches
+    ("prefill-fp8", L.LayerSpec("s6", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="fp8",
+                                w_shared="fp8", seed=96), "prefill"),
+]
+
+
+@pytest.mark.parametrize("name,spec,path", SIDE_SPECS, ids=[g[0] for g in SIDE_SPECS])
+def test_shared_expert_on_second_stream_matches_one_stream(name, spec, path):
+    """At decode, moe_layer_forward runs a shared expert (bf16-activation formats) on a second
+    stream beside the routing and the routed experts; moe_layer_forward_timed keeps one stream and
+    one grouped launch over all groups. The shared expert's launch restricted to its own group gives
+    every row the same arithmetic, so the two must agree bit for bit, on two calls in a row."""
+    say("side", name, spec, path)
+    lay, pl = build(spec, DEV, path=path)
+    x = lay["x"] if spec.act == "f32" else lay["x"].view(torch.bfloat16)
+    for call in range(2):
+        y2, idx2, w2 = run(spec, lay, pl)
+        y1 = torch.full_like(y2, float("nan"))
+        idx1 = torch.full_like(idx2, -7)
+        w1 = torch.full_like(w2, float("nan"))
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(N.TIMED_EVENTS)]
+        for e in evs:
+            e.record()  # creates the underlying HIP events
+        N.moe_layer_forward_timed(pl.shape, x, pl.Wr, lay["bias"], pl.routed, pl.shared, y1, evs, idx1, w1, pl.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx2), call
+        assert torch.equal(w1, w2), call
+        assert torch.equal(y1, y2), (call, (y1.float() - y2.float()).abs().max().item())
+        # the second call on another batch: x scaled by two (exact in every activation format)
+        x.mul_(2.0)
+
+
 # ------------------------------------------------------------------ graph capture
 
 GRAPH_SPECS = [
