@@ -42,6 +42,12 @@ TRAFFIC = {
     "c4": {"sha": "4ebfc015e8bd9d86", "bytes": 3662134510},
     # gate/up prefill kernel
     "c5": {"sha": "a4d75bc69100650b", "bytes": 16302908956},
+    # the W4A8 gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared bf16 GEMM
+    "v4p-w4a8": {"sha": "b631906a8dfde38d", "bytes": 10146152314},
+    # the hybrid gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared W8A8 MXFP8 GEMM
+    "v4p-mx": {"sha": "b631906a8dfde38d", "bytes": 9802442640},
+    # the int8 gate/up stage: x to int8 + Int8 W8A8 GEMM
+    "v3-int8": {"sha": "b631906a8dfde38d", "bytes": 17093371508},
 }
 CSRC = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
 KERNEL_SOURCES = {"decode": ("gemm_decode.hip", "common.h", "kernels.h"),
