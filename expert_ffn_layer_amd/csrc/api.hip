@@ -12,6 +12,10 @@
 
 using namespace moe;
 
+extern "C" __attribute__((visibility("hidden"))) hipError_t moe_launch_pack(int fmt, int count, int K, int N, const void* w,
+                                                                         const void* scale, void* packed,
+                                                                         void* packed_scale, hipStream_t stream);
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -710,6 +714,78 @@ moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed
   return s;
 }
 
+// The workspace of moe_layer_forward_logical: the layer's own workspace, then the packed router,
+// routed and shared matrices (moe_pack's layout), each at an ALIGN boundary.
+struct PackedSet {
+  size_t gate, gate_s, up, up_s, down, down_s;
+};
+struct LogicalWs {
+  size_t wr;
+  PackedSet r, sh;
+  size_t total;
+};
+
+moe_status logical_layout(const moe_shape& s, LogicalWs* out) {
+  size_t o = ws_layout(s).total;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += up(bytes ? bytes : 1);
+    return at;
+  };
+  size_t b, sb;
+  moe_status st;
+  if ((st = packed_sizes(s.act, 1, s.H, s.E, &b, &sb)) != MOE_OK) return st;
+  out->wr = take(b);
+  auto set = [&](moe_dtype fmt, int count, PackedSet& p) -> moe_status {
+    size_t b1, s1, b2, s2;
+    moe_status r;
+    if ((r = packed_sizes(fmt, count, s.H, s.I, &b1, &s1)) != MOE_OK) return r;
+    if ((r = packed_sizes(fmt, count, s.I, s.H, &b2, &s2)) != MOE_OK) return r;
+    p.gate = take(b1);
+    p.gate_s = take(s1);
+    p.up = take(b1);
+    p.up_s = take(s1);
+    p.down = take(b2);
+    p.down_s = take(s2);
+    return MOE_OK;
+  };
+  if ((st = set(s.w_routed, s.E, out->r)) != MOE_OK) return st;
+  out->sh = PackedSet{};
+  if (s.I_shared && (st = set(s.w_shared, 1, out->sh)) != MOE_OK) return st;
+  out->total = o;
+  return MOE_OK;
+}
+
+// Pack one expert set's logical matrices (gate and up [count][H][I], down [count][I][H]) into p.
+moe_status pack_set(const moe_shape& s, moe_dtype fmt, int count, const moe_weights& w, void* ws, const PackedSet& p,
+                    moe_weights* packed, hipStream_t st) {
+  const moe_dtype f = stored_fmt(fmt);
+  const bool scaled = fmt != MOE_F32 && fmt != MOE_BF16;
+  const int wal = fmt == MOE_F32 ? 4 : fmt == MOE_BF16 ? 2 : 1;
+  if ((uintptr_t)w.gate % wal || (uintptr_t)w.up % wal || (uintptr_t)w.down % wal) return misaligned("logical weights", wal);
+  if ((fmt == MOE_FP8_E4M3_B128 || fmt == MOE_INT8_W8A8) && (!al4(w.gate_scale) || !al4(w.up_scale) || !al4(w.down_scale)))
+    return misaligned("logical scales", 4);
+  struct Job {
+    const void *src, *src_s;
+    size_t dst, dst_s;
+    int K, N;
+  } jobs[3] = {{w.gate, w.gate_scale, p.gate, p.gate_s, s.H, s.I},
+               {w.up, w.up_scale, p.up, p.up_s, s.H, s.I},
+               {w.down, w.down_scale, p.down, p.down_s, s.I, s.H}};
+  for (const Job& j : jobs) {
+    const hipError_t e = moe_launch_pack(f, count, j.K, j.N, j.src, scaled ? j.src_s : nullptr, at<void>(ws, j.dst),
+                                         scaled ? at<void>(ws, j.dst_s) : nullptr, st);
+    if (e != hipSuccess) return hip_status(e, "pack");
+  }
+  packed->gate = at<void>(ws, p.gate);
+  packed->up = at<void>(ws, p.up);
+  packed->down = at<void>(ws, p.down);
+  packed->gate_scale = scaled ? at<void>(ws, p.gate_s) : nullptr;
+  packed->up_scale = scaled ? at<void>(ws, p.up_s) : nullptr;
+  packed->down_scale = scaled ? at<void>(ws, p.down_s) : nullptr;
+  return MOE_OK;
+}
+
 // ------------------------------------------------------------------------------------------
 // The library's own scratch memory, for callers that cannot allocate: moe_layer_forward_noalloc
 // runs the layer with this array as its workspace. Each GPU holds its own copy for the life of the
@@ -892,6 +968,43 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   return do_layer(shape, x, Wr_packed, bias, routed, shared, y, topk_idx_out, topk_w_out, ws, ws_bytes,
                   (hipStream_t)stream, nullptr, nullptr, true);
+}
+
+moe_status moe_logical_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  LogicalWs L;
+  if ((s = logical_layout(*shape, &L)) != MOE_OK) return s;
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_logical(const moe_shape* shape, const void* x, const void* Wr, const float* bias,
+                                     const moe_weights* routed, const moe_weights* shared, void* y,
+                                     int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                                     moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(routed, shape->w_routed, "routed")) != MOE_OK) return s;
+  if (shape->I_shared && (s = check_weights(shared, shape->w_shared, "shared")) != MOE_OK) return s;
+  if (!Wr) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if ((uintptr_t)Wr % (shape->act == MOE_F32 ? 4 : 2)) return misaligned("Wr", shape->act == MOE_F32 ? 4 : 2);
+  LogicalWs L;
+  if ((s = logical_layout(*shape, &L)) != MOE_OK) return s;
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  if ((uintptr_t)ws % ALIGN) return fail(MOE_ERR_INVALID_ARG, "workspace must be %zu-byte aligned", ALIGN);
+  const hipStream_t st = (hipStream_t)stream;
+  // the router, the routed experts and the shared one into moe_pack's layout, then the layer
+  hipError_t e = moe_launch_pack(shape->act, 1, shape->H, shape->E, Wr, nullptr, at<void>(ws, L.wr), nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "pack");
+  moe_weights pr{}, ps{};
+  if ((s = pack_set(*shape, shape->w_routed, shape->E, *routed, ws, L.r, &pr, st)) != MOE_OK) return s;
+  if (shape->I_shared && (s = pack_set(*shape, shape->w_shared, 1, *shared, ws, L.sh, &ps, st)) != MOE_OK) return s;
+  return do_layer(shape, x, at<void>(ws, L.wr), bias, &pr, shape->I_shared ? &ps : nullptr, y, topk_idx_out,
+                  topk_w_out, ws, ws_layout(*shape).total, st, nullptr, nullptr, true);
 }
 
 moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* Wr_packed, const float* bias,

@@ -20,7 +20,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_pack_size", "moe_pack", "moe_workspace_size",
            "moe_route", "moe_route_hash", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_combine",
            "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_hash", "moe_layer_forward_timed",
-           "moe_quantize_mxfp8", "moe_quantize_int8")
+           "moe_quantize_mxfp8", "moe_quantize_int8", "moe_logical_workspace_size", "moe_layer_forward_logical")
 # the library's own scratch, the workspace of moe_layer_forward_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
 TIMED_EVENTS = 7
@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
                                                 ctypes.POINTER(ctypes.c_void_p)]
         lib.moe_quantize_mxfp8.argtypes = [P, I32, I32, P, P, P]
         lib.moe_quantize_int8.argtypes = [P, I32, I32, P, P, P]
+        lib.moe_logical_workspace_size.argtypes = [PS, ctypes.POINTER(SZ)]
+        lib.moe_layer_forward_logical.argtypes = [PS, P, P, P, PW, PW, P, P, P, P, SZ, P]
         for name in EXPORTS[2:]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -129,6 +131,22 @@ def moe_workspace_size(shape: MoeShape) -> int:
     b = ctypes.c_size_t()
     _check(load().moe_workspace_size(ctypes.byref(shape), ctypes.byref(b)))
     return b.value
+
+
+def moe_logical_workspace_size(shape: MoeShape) -> int:
+    b = ctypes.c_size_t()
+    _check(load().moe_logical_workspace_size(ctypes.byref(shape), ctypes.byref(b)))
+    return b.value
+
+
+def moe_layer_forward_logical(shape, x, Wr, bias, routed: dict, shared: dict | None, y, topk_idx=None,
+                              topk_w=None, ws=None, stream=None):
+    """Weights in the logical row-major layout (moe_pack's source layout), packed into ws each call."""
+    r, s = weights(routed), weights(shared)
+    _check(load().moe_layer_forward_logical(ctypes.byref(shape), _p(x), _p(Wr), _p(bias), ctypes.byref(r),
+                                            None if s is None else ctypes.byref(s), _p(y), _p(topk_idx),
+                                            _p(topk_w), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                            _stream(stream)))
 
 
 def moe_route(shape, x, Wr_packed, bias, topk_idx, topk_w, ws, stream=None):

@@ -273,6 +273,30 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              float* topk_w_out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
+ * moe_layer_forward_logical — moe_layer_forward on weights in the layout in which the pages write
+ * them ('第 6 章 超節點' §6.2.2: x·W_g and x·W_u with W_g, W_u [H][I], then ·W_d with W_d [I][H],
+ * row-major; the router's W_r [H][E]) instead of moe_pack's layout. Each call first packs the
+ * router, the routed experts and the shared one into the workspace (moe_pack's kernels, on
+ * `stream`), then runs moe_layer_forward on the packed copies, with the same results. This reads
+ * and writes every weight once more per call, so a layer that runs more than once is faster packed
+ * once with moe_pack and run with moe_layer_forward.
+ *   Wr        act [H][E] row-major (bf16 bits or float)
+ *   routed    gate, up: [E][H][I]; down: [E][I][H]; scales: moe_pack's source scale layout of
+ *             each matrix, back to back per expert (NULL for F32 / BF16)
+ *   shared    the same for one expert, or NULL when I_shared == 0
+ *   ws        moe_logical_workspace_size(shape) bytes (the layer's workspace followed by the
+ *             packed matrices), 256-byte aligned
+ *   Other arguments, ownership, results and errors as moe_layer_forward; pointers are caller-owned
+ *   device memory, read only.
+ */
+moe_status moe_logical_workspace_size(const moe_shape* shape, size_t* bytes);
+moe_status moe_layer_forward_logical(const moe_shape* shape, const void* x, const void* Wr,
+                                     const float* bias, const moe_weights* routed,
+                                     const moe_weights* shared, void* y, int32_t* topk_idx_out,
+                                     float* topk_w_out, void* ws, size_t ws_bytes,
+                                     moe_stream_t stream);
+
+/*
  * moe_layer_forward_noalloc — moe_layer_forward with the library's own scratch memory as the
  * workspace, for callers that cannot allocate device memory (code under HIP graph capture that
  * owns no workspace, tight serving loops, harnesses that forbid hipMalloc). It allocates nothing

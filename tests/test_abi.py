@@ -132,6 +132,24 @@ def test_pack_sizes():
             N.moe_pack_size(fmt, 1, K, Nn)
 
 
+def test_logical_workspace_adds_the_packed_matrices():
+    """moe_layer_forward_logical's workspace: the layer's, then the packed router and experts, each
+    rounded up to the 256-byte alignment."""
+    def up(n):
+        return (n + 255) // 256 * 256
+    for kw in (dict(), dict(I_shared=128), dict(w_routed="fp8", w_shared="fp8", I_shared=128, H=256, I=128)):
+        s = _shape(**kw)
+        fmt = kw.get("w_routed", "bf16")
+        H, I, E = s.H, s.I, s.E
+        extra = up(N.moe_pack_size("bf16", 1, H, E)[0])
+        mats = [(fmt, E)] + ([(kw.get("w_shared", "bf16"), 1)] if s.I_shared else [])
+        for f, count in mats:
+            g, gs = N.moe_pack_size(f, count, H, I)
+            d, ds = N.moe_pack_size(f, count, I, H)
+            extra += 2 * (up(g) + up(max(gs, 1))) + up(d) + up(max(ds, 1))
+        assert N.moe_logical_workspace_size(s) == N.moe_workspace_size(s) + extra
+
+
 def test_entry_points_reject_null_and_small_workspace_before_launch():
     lib = N.load()
     s = _shape()
@@ -159,6 +177,12 @@ def test_entry_points_reject_null_and_small_workspace_before_launch():
                                       None, None, fake, 1 << 30, None) == 1
     # misaligned workspace
     assert lib.moe_permute(ctypes.byref(s), fake, fake, fake, fake, P(0x1001), 1 << 30, None) == 1
+    # logical weights: NULL router, the packed copies not fitting the workspace
+    assert lib.moe_layer_forward_logical(ctypes.byref(sh), fake, None, None, ctypes.byref(wf), ctypes.byref(wf), fake,
+                                         None, None, fake, 1 << 40, None) == 1
+    need = N.moe_logical_workspace_size(sh)
+    assert lib.moe_layer_forward_logical(ctypes.byref(sh), fake, fake, None, ctypes.byref(wf), ctypes.byref(wf), fake,
+                                         None, None, fake, need - 1, None) == 3
 
 
 def test_quantisers_validate_before_launch():

@@ -729,6 +729,46 @@ def test_hash_routing_matches_oracle(name, spec, vocab):
     assert err <= tol_of(spec)
 
 
+# ------------------------------------------------------------------ weights in the logical layout
+
+LOGICAL_SPECS = [
+    ("f32", L.LayerSpec("l1", T=16, H=256, E=8, k=2, I=128, act="f32", w_routed="f32", w_shared="f32", seed=71)),
+    ("bf16-shared-zipf", L.LayerSpec("l2", T=90, H=512, E=12, k=3, I=256, shared=True, router="zipf",
+                                     zipf_alpha=1.0, calib_tokens=512, seed=72)),
+    ("fp8-prefill", L.LayerSpec("l3", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="fp8", w_shared="fp8",
+                                seed=73)),
+    ("mxfp4+bf16", L.LayerSpec("l4", T=40, H=512, E=16, k=4, I=256, shared=True, w_routed="mxfp4",
+                               w_shared="bf16", seed=74)),
+    ("w4a8+mxfp8", L.LayerSpec("l5", T=200, H=512, E=8, k=2, I=256, shared=True, w_routed="mxfp4a8",
+                               w_shared="mxfp8a8", seed=75)),
+    ("int8", L.LayerSpec("l6", T=300, H=512, E=8, k=2, I=256, shared=True, w_routed="int8", w_shared="int8",
+                         seed=76)),
+]
+
+
+@pytest.mark.parametrize("name,spec", LOGICAL_SPECS, ids=[g[0] for g in LOGICAL_SPECS])
+def test_logical_weights_forward_matches_packed(name, spec):
+    """moe_layer_forward_logical takes the router and the experts in the pages' row-major layout
+    and packs them into its workspace each call; its results equal moe_layer_forward on the same
+    weights packed once with moe_pack, bit for bit, on two calls in a row."""
+    say("logical", name, spec)
+    lay, pl = build(spec, DEV)
+    x = lay["x"] if spec.act == "f32" else lay["x"].view(torch.bfloat16)
+    Wr = lay["Wr"] if spec.act == "f32" else lay["Wr"].view(torch.bfloat16)
+    ws = torch.empty(N.moe_logical_workspace_size(pl.shape), dtype=torch.uint8, device=DEV)
+    for call in range(2):
+        y2, idx2, w2 = run(spec, lay, pl)
+        y1 = torch.full_like(y2, float("nan"))
+        idx1 = torch.full_like(idx2, -7)
+        w1 = torch.full_like(w2, float("nan"))
+        N.moe_layer_forward_logical(pl.shape, x, Wr, lay["bias"], lay["routed"], lay["shared"], y1, idx1, w1, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx2), call
+        assert torch.equal(w1, w2), call
+        assert torch.equal(y1, y2), (call, (y1.float() - y2.float()).abs().max().item())
+        x.mul_(2.0)  # the second call on another batch
+
+
 # ------------------------------------------------------------------ shared expert on a second stream
 
 SIDE_SPECS = [
