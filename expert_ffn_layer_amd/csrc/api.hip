@@ -634,12 +634,26 @@ struct SideStream {
 };
 thread_local SideStream t_side[MAX_SIDE_DEVICES];
 
-SideStream* side_of_current_device(moe_status* st) {
+// The current device's second stream for work on `stream`, or null when `stream` belongs to another
+// device (the caller's launches then all stay on `stream`: *st is MOE_OK) or on an error (*st set).
+SideStream* side_of_current_device(hipStream_t stream, moe_status* st) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
     *st = hip_status(e, "hipGetDevice");
     return nullptr;
+  }
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) {
+      *st = hip_status(e, "hipStreamGetDevice");
+      return nullptr;
+    }
+    if (sdev != dev) {
+      *st = MOE_OK;
+      return nullptr;
+    }
   }
   if (dev < 0 || dev >= MAX_SIDE_DEVICES) {
     *st = fail(MOE_ERR_UNSUPPORTED, "device %d: the second stream covers devices 0..%d", dev, MAX_SIDE_DEVICES - 1);
@@ -685,12 +699,12 @@ moe_status do_layer(const moe_shape* shape, const void* x, const void* Wr_packed
   void* y_perm = at<void>(ws, L.y_perm);
   void* y_sh = shape->I_shared ? at<void>(ws, L.y_shared) : nullptr;
   if (ev && (s = record(ev[0], st)) != MOE_OK) return s;
-  const bool side = overlap && !ev && side_shared(*shape);
   SideStream* ss = nullptr;
+  if (overlap && !ev && side_shared(*shape) && !(ss = side_of_current_device(st, &s)) && s != MOE_OK) return s;
+  const bool side = ss != nullptr;
   if (side) {
     // fork: the second stream starts after what the caller's stream holds so far, runs the shared
     // expert's plan, gate/up and down, and records the join event
-    if (!(ss = side_of_current_device(&s))) return s;
     if ((s = hip_status(hipEventRecord(ss->fork, st), "fork event")) != MOE_OK) return s;
     if ((s = hip_status(hipStreamWaitEvent(ss->s, ss->fork, 0), "fork wait")) != MOE_OK) return s;
     if ((s = do_ffn(*shape, x, off, slot_token, *routed, shared, y_perm, y_sh, ws, L, ss->s, nullptr, false,

@@ -262,8 +262,9 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
  * writes the grouped GEMMs' plan.
  * Decode batches with a shared expert in a bf16-activation format run that expert ('CANN
  * DeepSeek-V4推理优化', multi-stream parallelism) on a second stream the library owns, one per
- * calling thread and device, made on the thread's first such call: it waits for an event recorded
- * on `stream` at entry, and `stream` waits for its end before the combine. The call still only
+ * calling thread and device, made on the thread's first such call (when `stream` belongs to the
+ * current device; otherwise everything stays on `stream`): it waits for an event recorded on
+ * `stream` at entry, and `stream` waits for its end before the combine. The call still only
  * enqueues, results are bit-identical to the single-stream order (moe_layer_forward_timed), and
  * capturing `stream` in a HIP graph captures both streams' work.
  */
