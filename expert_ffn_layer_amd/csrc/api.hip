@@ -1010,6 +1010,7 @@ moe_status moe_layer_forward_logical(const moe_shape* shape, const void* x, cons
   if (ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if ((uintptr_t)ws % ALIGN) return fail(MOE_ERR_INVALID_ARG, "workspace must be %zu-byte aligned", ALIGN);
+  if (shape->T == 0) return MOE_OK;
   const hipStream_t st = (hipStream_t)stream;
   // the router, the routed experts and the shared one into moe_pack's layout, then the layer
   hipError_t e = moe_launch_pack(shape->act, 1, shape->H, shape->E, Wr, nullptr, at<void>(ws, L.wr), nullptr, st);
