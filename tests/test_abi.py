@@ -236,3 +236,50 @@ def test_misaligned_pointers_are_refused_before_launch():
     assert lib.moe_pack(N.DTYPE["bf16"], 1, 256, 128, a, None, m8, None, None) == 1     # packed
     assert lib.moe_pack(N.DTYPE["f32"], 1, 256, 128, m2, None, a, None, None) == 1      # f32 source
     assert lib.moe_pack(N.DTYPE["fp8"], 1, 256, 256, a, m2, a, a, None) == 1            # fp32 scales
+
+
+C_PROGRAM = r"""
+#include "moe.h"
+#include <stdio.h>
+#include <string.h>
+
+int main(void) {
+  moe_shape s;
+  size_t bytes = 0, logical = 0, pb = 0, ps = 0;
+  moe_status st;
+  memset(&s, 0, sizeof s);
+  s.T = 64; s.H = 4096; s.E = 128; s.k = 8; s.I = 1536; s.I_shared = 0;
+  s.act = MOE_BF16; s.w_routed = MOE_BF16; s.w_shared = MOE_BF16; s.path = MOE_PATH_AUTO;
+  st = moe_workspace_size(&s, &bytes);
+  printf("workspace %d %lu\n", (int)st, (unsigned long)bytes);
+  st = moe_logical_workspace_size(&s, &logical);
+  printf("logical %d %lu\n", (int)st, (unsigned long)logical);
+  st = moe_pack_size(MOE_FP8_E4M3_B128, 2, 7168, 2048, &pb, &ps);
+  printf("pack %d %lu %lu\n", (int)st, (unsigned long)pb, (unsigned long)ps);
+  s.k = 0;
+  st = moe_workspace_size(&s, &bytes);
+  printf("bad %d %s\n", (int)st, moe_status_string(st));
+  return 0;
+}
+"""
+
+
+def test_header_is_c99_and_the_library_links_from_c(tmp_path):
+    """include/moe.h compiles as strict C99 (no C++ in the ABI) and a C program linked against
+    libmoe.so gets the same host-side answers as the binding."""
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(N.LIB_PATH)
+    cc = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                         "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                         N.LIB_PATH, "-Wl,-rpath," + libdir], capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    out = dict((l.split()[0], l.split()[1:]) for l in run.stdout.splitlines())
+    shape = N.make_shape(64, 4096, 128, 8, 1536)
+    assert out["workspace"] == ["0", str(N.moe_workspace_size(shape))]
+    assert out["logical"] == ["0", str(N.moe_logical_workspace_size(shape))]
+    assert out["pack"] == ["0"] + [str(v) for v in N.moe_pack_size("fp8", 2, 7168, 2048)]
+    assert out["bad"] == ["1", N.STATUS[1]]
