@@ -457,9 +457,9 @@ def test_full_size_prefill_rows_group_by_group(cfg):
 
 
 # layers at the V3 decode layer's width (H = 7168, I = 2048) on the decode kernel with a few
-# experts, so every group spans several 64-row blocks with a ragged last one: the gate/up widths
-# of the V3 decode layers (16 features, bf16 and int8), down at 32 (bf16) and 64 (int8) features,
-# four row tiles per block; every token compared
+# experts, so every group spans several 64-row blocks with a ragged last one: the gate/up width of
+# the V3 decode layers (32 features: their groups average 8 rows or more; bf16 and int8), down at
+# 32 (bf16) and 64 (int8) features, four row tiles per block; every token compared
 MID = [
     ("mid-bf16", L.LayerSpec("m1", T=200, H=7168, E=6, k=2, I=2048, shared=True, router="zipf", zipf_alpha=1.0,
                              calib_tokens=512, seed=81)),
@@ -485,6 +485,31 @@ def test_decode_widths_every_token(name, spec):
     counts = np.bincount(ridx.reshape(-1), minlength=spec.E)
     say("  group rows %s" % counts.tolist())
     assert counts.max() > 128  # several 64-row blocks in one group
+    tokens = list(range(spec.T))
+    ref = oracle_tokens(spec, lay, ridx, rw, tokens)
+    err = rel_fro(to_f64(y), ref)
+    worst = max(rel_fro(to_f64(y)[t], ref[t]) for t in tokens)
+    say("  rel. Frobenius error %.3e, worst token %.3e (bound %.0e)" % (err, worst, tol_of(spec)))
+    assert err <= tol_of(spec) and worst <= 2 * tol_of(spec)
+
+
+# the same width with groups of fewer than 8 rows on average: gate/up at 16 features per item
+THIN = [
+    ("thin-bf16", L.LayerSpec("m5", T=24, H=7168, E=12, k=2, I=2048, shared=True, seed=85)),
+    ("thin-int8", L.LayerSpec("m6", T=24, H=7168, E=12, k=2, I=2048, shared=True, w_routed="int8", w_shared="int8",
+                              seed=86)),
+]
+
+
+@pytest.mark.parametrize("name,spec", THIN, ids=[m[0] for m in THIN])
+def test_decode_thin_groups_every_token(name, spec):
+    say("thin", name, spec)
+    lay, pl = build(spec, DEV, "decode")
+    y, idx, w = run(spec, lay, pl)
+    ridx, rw, _ = O.route(lay["x_host"], lay["Wr_host"], lay["bias_host"], spec.k, spec.act)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-5
+    assert (spec.T * spec.k + spec.T) / (spec.E + 1) < 8  # the one-tile width
     tokens = list(range(spec.T))
     ref = oracle_tokens(spec, lay, ridx, rw, tokens)
     err = rel_fro(to_f64(y), ref)
