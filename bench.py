@@ -36,10 +36,10 @@ WORKLOADS = ("c1", "c2", "c3", "c4", "c5", "v4p", "v4p-w4a8", "v4p-mx", "v3-int8
 # the kernel sources it was measured on are unchanged (hash of their code).
 TRAFFIC = {
     # gate/up decode kernel
-    "c1": {"sha": "4ebfc015e8bd9d86", "bytes": 2390368},
-    "c2": {"sha": "4ebfc015e8bd9d86", "bytes": 3176844236},
-    "c3": {"sha": "4ebfc015e8bd9d86", "bytes": 14212862838},
-    "c4": {"sha": "4ebfc015e8bd9d86", "bytes": 3662134510},
+    "c1": {"sha": "10b97aefda9c717d", "bytes": 2390482},
+    "c2": {"sha": "10b97aefda9c717d", "bytes": 3176729742},
+    "c3": {"sha": "10b97aefda9c717d", "bytes": 14043819466},
+    "c4": {"sha": "10b97aefda9c717d", "bytes": 3662068654},
     # gate/up prefill kernel
     "c5": {"sha": "a4d75bc69100650b", "bytes": 16302908956},
     # the W4A8 gate/up stage: x to MXFP8 + routed W4A8 GEMM + shared bf16 GEMM
