@@ -809,6 +809,9 @@ SIDE_SPECS = [
                                shared=True, seed=94), "decode"),
     ("decode-bf16+fp8", L.LayerSpec("s5", T=64, H=1024, E=32, k=4, I=512, shared=True, w_routed="bf16",
                                     w_shared="fp8", seed=95), "decode"),
+    # groups of fewer than 8 rows at H = 4096: the all-groups gate/up launch takes one 16-feature
+    # tile per item, the shared expert's own launch (24 rows in one group) two
+    ("decode-bf16-widths", L.LayerSpec("s7", T=24, H=4096, E=12, k=2, I=1024, shared=True, seed=97), "decode"),
     # a prefill batch keeps one stream: the two entry points run the same launches
     ("prefill-fp8", L.LayerSpec("s6", T=600, H=512, E=6, k=2, I=256, shared=True, w_routed="fp8",
                                 w_shared="fp8", seed=96), "prefill"),
